@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Bench: PN decode-step GEMV weight-GB/s on one MI355X.
+
+Workload (one step): one Qwen3.8-27B-shaped MLP at M = 1 token -- gate and up as pn3t 17408 x 5120,
+down as pn4t 5120 x 17408 -- three pn_gemv calls. Weights: seeded N(0, 0.02) fp32 quantized on the
+GPU by the reference quantizer (pn_quantize_rows); x ~ N(0, 1) fp32. Five distinct device copies of
+the weight set (615.5 MB, above the 256 MB Infinity Cache) are used round-robin, so every step reads
+its weights from HBM. value = weight bytes per step / time per step.
+
+Prints one JSON line (rank 0). See --help for the knobs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "PN GEMV weight GB/s at M=1 (% of MI355X HBM peak), K=5120/17408"
+
+# (name, type, N, K, weight seed, x seed)
+MLP = [("gate", 124, 17408, 5120, 301, 304), ("up", 124, 17408, 5120, 302, 304),
+       ("down", 125, 5120, 17408, 303, 305)]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_weights(pn, torch, dev, copies):
+    """Quantize each MLP matrix on the GPU and replicate it `copies` times in distinct buffers."""
+    import numpy as np
+    import synth
+    mats = []
+    for name, typ, N, K, wseed, xseed in MLP:
+        t0 = time.time()
+        w = torch.from_numpy(synth.gaussian_weights(wseed, N, K, 0.02)).to(dev)
+        rb = pn.row_bytes(typ, K)
+        W0 = torch.empty((N, rb), dtype=torch.uint8, device=dev)
+        st = torch.empty(N, dtype=torch.int32, device=dev)
+        pn.quantize_rows(typ, w, W0, st)
+        ver = torch.empty(N, dtype=torch.int32, device=dev)
+        pn.validate_rows(typ, W0, N, K, ver)
+        torch.cuda.synchronize()
+        if int(st.abs().sum()) != 0 or int(ver.sum()) != N:
+            raise RuntimeError(f"{name}: quantizer status / validation failed")
+        del w
+        Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(np.ascontiguousarray(synth.activations(xseed, 1, K))).to(dev)
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        mats.append(dict(name=name, typ=typ, N=N, K=K, Ws=Ws, x=x, y=y, bytes=N * rb))
+        log(f"[bench] {name}: {N}x{K} type {typ}, {N * rb / 1e6:.2f} MB x {copies} copies "
+            f"({time.time() - t0:.1f} s)")
+    return mats
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle's GEMV timed on the host cores: a bounded sample (1/16 of the rows of each MLP
+    matrix, quantized by the oracle), repeated to ~`seconds` of work."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    samples = []
+    for name, typ, N, K, wseed, xseed in MLP:
+        n = N // 16
+        w = synth.gaussian_weights(wseed, N, K, 0.02)[:n]
+        W, _ = oracle.quantize_rows(typ, w, threads=threads)
+        samples.append((typ, n, K, W, synth.activations(xseed, 1, K), W.nbytes))
+    total_bytes, reps, t0 = 0, 0, time.perf_counter()
+    while True:
+        for typ, n, K, W, x, nbytes in samples:
+            oracle.gemv(typ, W, n, K, x, threads=threads)
+            total_bytes += nbytes
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"rows 0..N/16 of gate, up, down (M=1), {reps} passes, {el:.1f} s, "
+                      f"fp64 accumulation, {threads} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=5, help="rotated weight copies (>= 3 to exceed MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: run with --gpus 1 "
+                          "(the GEMV shards by rows; see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+    import block_quantized_weight_pn3t_amd as pn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mats = build_weights(pn, torch, dev, args.copies)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    step_bytes = sum(m["bytes"] for m in mats)
+
+    def one_step(s, evs=None):
+        c = s % args.copies
+        for j, m in enumerate(mats):
+            if evs is not None:
+                evs[j][0].record(stream)
+            st = pn.gemv_ptr(m["typ"], m["Ws"][c].data_ptr(), m["N"], m["K"], m["x"].data_ptr(),
+                             1, m["y"].data_ptr(), sh)
+            if evs is not None:
+                evs[j][1].record(stream)
+            if st != 0:
+                raise RuntimeError(f"pn_gemv failed: {pn.status_string(st)}")
+
+    for s in range(args.warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+
+    # timed region: K steps back to back on one stream, events only at the two ends
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        one_step(s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel durations, live, on the launch stream: each kernel launched K times back to back
+    # over the rotated copies between two events (avg = elapsed / K, launch gaps included), and
+    # again with an event pair around every launch (marker overhead included).
+    kern = {}
+    for j, m in enumerate(mats):
+        def launch(s, m=m):
+            st = pn.gemv_ptr(m["typ"], m["Ws"][s % args.copies].data_ptr(), m["N"], m["K"],
+                             m["x"].data_ptr(), 1, m["y"].data_ptr(), sh)
+            if st != 0:
+                raise RuntimeError(f"pn_gemv failed: {pn.status_string(st)}")
+        for s in range(args.warmup):
+            launch(s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.steps):
+            launch(s)
+        e1.record(stream)
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for s in range(args.steps):
+            pairs[s][0].record(stream)
+            launch(s)
+            pairs[s][1].record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        us_pair = sum(a.elapsed_time(b) for a, b in pairs) * 1e3 / args.steps
+        kern[m["name"]] = dict(avg_us=round(us, 3), weight_GBs=round(m["bytes"] / us / 1e3, 1),
+                               avg_us_event_pair=round(us_pair, 3), bytes=m["bytes"])
+    # dominant kernel: the largest share of the step's kernel time, per kernel kind
+    kinds = {"pn3t_17408x5120": ["gate", "up"], "pn4t_5120x17408": ["down"]}
+    tot = {k: sum(kern[n]["avg_us"] for n in v) for k, v in kinds.items()}
+    dom = max(tot, key=tot.get)
+    dnames = kinds[dom]
+    d_bytes = kern[dnames[0]]["bytes"]
+    d_us = sum(kern[n]["avg_us"] for n in dnames) / len(dnames)
+    achieved = d_bytes / d_us / 1e3
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3.8-27B-shaped MLP at M=1: gate+up pn3t 17408x5120, "
+                               "down pn4t 5120x17408 (3 pn_gemv launches per step)",
+                   "weight_bytes_per_step": step_bytes, "rotated_copies": args.copies,
+                   "working_set_MB": round(step_bytes * args.copies / 1e6, 1),
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "kernel": f"pn_gemv {dom} (M=1)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(d_us, 3), "algorithmic_bytes_per_launch": d_bytes},
+        "kernels": kern,
+    }
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

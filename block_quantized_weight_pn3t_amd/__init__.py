@@ -1,0 +1,180 @@
+"""Python binding of libpn.so (C ABI in include/pn.h): PN (pn3t / pn4t) and NVFP4 W4A16
+decode-step GEMV, validation, decode and quantizers on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libpn.so. PyTorch supplies device
+memory and the current stream. There is no CPU fallback: if the library is missing, importing
+this package raises ImportError; if a call fails, it raises PNError.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+__all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
+           "dequantize_rows", "dequantize_row", "gemv", "quantize_rows", "nvfp4_validate_rows",
+           "nvfp4_dequantize_rows", "gemv_nvfp4", "nvfp4_global_scale", "nvfp4_quantize_rows",
+           "library_path", "status_string", "lib"]
+
+PN3T = 124
+PN4T = 125
+GROUP = {PN3T: 80, PN4T: 64}
+MAX_TOKENS = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpn.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+
+_lib = C.CDLL(library_path)
+_P, _I64, _I32, _F = C.c_void_p, C.c_int64, C.c_int, C.c_float
+_SIGS = {
+    "pn_row_bytes": (_I64, [_I32, _I64]),
+    "pn_status_string": (C.c_char_p, [_I32]),
+    "pn_validate_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P]),
+    "pn_validate_row": (_I32, [_I32, _P, _I64, _P, _P]),
+    "pn_dequantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P]),
+    "pn_dequantize_row": (_I32, [_I32, _P, _I64, _P, _P]),
+    "pn_gemv": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "pn_quantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
+    "pn_nvfp4_validate_rows": (_I32, [_P, _F, _I64, _I64, _P, _P]),
+    "pn_nvfp4_dequantize_rows": (_I32, [_P, _P, _F, _I64, _I64, _P, _P]),
+    "pn_gemv_nvfp4": (_I32, [_P, _P, _F, _I64, _I64, _P, _I64, _P, _P]),
+    "pn_nvfp4_global_scale": (_I32, [_P, _I64, _P, _P]),
+    "pn_nvfp4_quantize_rows": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def lib() -> C.CDLL:
+    return _lib
+
+
+class PNError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def status_string(status: int) -> str:
+    return _lib.pn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PNError(status, what)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else 0
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def row_bytes(type_: int, K: int) -> int:
+    return int(_lib.pn_row_bytes(type_, K))
+
+
+# ---- PN ---------------------------------------------------------------------------------------
+
+def validate_rows(type_, W, nrows, K, verdict, stream=None):
+    """verdict (int32[nrows], device) <- 1 valid / 0 invalid per row."""
+    import torch
+    _dev(verdict, "verdict", torch.int32)
+    _check(_lib.pn_validate_rows(type_, _ptr(W), nrows, K, _ptr(verdict), _stream(stream)),
+           "pn_validate_rows")
+
+
+def validate_row(type_, row, K, verdict, stream=None):
+    _check(_lib.pn_validate_row(type_, _ptr(row), K, _ptr(verdict), _stream(stream)),
+           "pn_validate_row")
+
+
+def dequantize_rows(type_, W, nrows, K, out, stream=None):
+    import torch
+    _dev(out, "out", torch.float32)
+    _check(_lib.pn_dequantize_rows(type_, _ptr(W), nrows, K, _ptr(out), _stream(stream)),
+           "pn_dequantize_rows")
+
+
+def dequantize_row(type_, row, K, out, stream=None):
+    _check(_lib.pn_dequantize_row(type_, _ptr(row), K, _ptr(out), _stream(stream)),
+           "pn_dequantize_row")
+
+
+def gemv(type_, W, N, K, x, y, M=None, stream=None):
+    """y[M, N] <- W[N, K] . x[M, K]^T for PN weights W (raw bytes on the device)."""
+    import torch
+    _dev(x, "x", torch.float32)
+    _dev(y, "y", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    _check(_lib.pn_gemv(type_, _ptr(W), N, K, _ptr(x), M, _ptr(y), _stream(stream)), "pn_gemv")
+
+
+def gemv_ptr(type_, W_ptr, N, K, x_ptr, M, y_ptr, stream_handle):
+    """Raw-pointer form for timing loops: returns the status instead of raising."""
+    return _lib.pn_gemv(type_, W_ptr, N, K, x_ptr, M, y_ptr, stream_handle)
+
+
+def quantize_rows(type_, w, W, status=None, stream=None):
+    """PN reference quantizer: W (uint8[nrows, row_bytes], device) <- fp32 w[nrows, K]."""
+    import torch
+    _dev(w, "w", torch.float32)
+    nrows, K = w.shape
+    _check(_lib.pn_quantize_rows(type_, _ptr(w), nrows, K, _ptr(W), _ptr(status),
+                                 _stream(stream)), "pn_quantize_rows")
+
+
+# ---- NVFP4 ------------------------------------------------------------------------------------
+
+def nvfp4_validate_rows(scales, g, N, K, verdict, stream=None):
+    _check(_lib.pn_nvfp4_validate_rows(_ptr(scales), g, N, K, _ptr(verdict), _stream(stream)),
+           "pn_nvfp4_validate_rows")
+
+
+def nvfp4_dequantize_rows(codes, scales, g, N, K, out, stream=None):
+    _check(_lib.pn_nvfp4_dequantize_rows(_ptr(codes), _ptr(scales), g, N, K, _ptr(out),
+                                         _stream(stream)), "pn_nvfp4_dequantize_rows")
+
+
+def gemv_nvfp4(codes, scales, g, N, K, x_bf16, y, M=None, stream=None):
+    """y[M, N] <- NVFP4 W . x; x_bf16 holds raw bf16 words (int16/uint16/bfloat16 tensor)."""
+    if M is None:
+        M = 1 if x_bf16.dim() == 1 else x_bf16.shape[0]
+    _check(_lib.pn_gemv_nvfp4(_ptr(codes), _ptr(scales), g, N, K, _ptr(x_bf16), M, _ptr(y),
+                              _stream(stream)), "pn_gemv_nvfp4")
+
+
+def gemv_nvfp4_ptr(codes_ptr, scales_ptr, g, N, K, x_ptr, M, y_ptr, stream_handle):
+    return _lib.pn_gemv_nvfp4(codes_ptr, scales_ptr, g, N, K, x_ptr, M, y_ptr, stream_handle)
+
+
+def nvfp4_global_scale(w, g_out, stream=None):
+    _check(_lib.pn_nvfp4_global_scale(_ptr(w), w.numel(), _ptr(g_out), _stream(stream)),
+           "pn_nvfp4_global_scale")
+
+
+def nvfp4_quantize_rows(w, g_dev, codes, scales, stream=None):
+    N, K = w.shape
+    _check(_lib.pn_nvfp4_quantize_rows(_ptr(w), N, K, _ptr(g_dev), _ptr(codes), _ptr(scales),
+                                       _stream(stream)), "pn_nvfp4_quantize_rows")

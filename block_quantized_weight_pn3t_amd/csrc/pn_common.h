@@ -1,0 +1,102 @@
+// pn_common.h -- shared pieces of the gfx950 kernels and the host entry points of libpn.so.
+//
+// Formats: "PN weight format" (PNX-FORMAT-v0), sections "Types", "Block layout", "Value";
+// NVFP4 per "Quantisation and profiles", section "NVFP4", and NInfer "tensor formats" 3.3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pn.h"
+
+namespace pn {
+
+// Per-type constants ("Types"): code width, weights per block, codes per u32 word, zero point.
+// LDS_STRIDE is the number of floats a staged block of x occupies in LDS: the G scaled values,
+// the block's plain sum of x at offset G, and padding so that consecutive lanes reading 16-byte
+// pieces of consecutive blocks hit disjoint LDS banks (stride = 4 mod 32 words for pn4t,
+// 20 mod 32 for pn3t: both give 8 (and 16) distinct 16-byte bank groups).
+template <int TYPE> struct Fmt;
+template <> struct Fmt<PN_TYPE_PN3T> {
+    static constexpr int BITS = 3, G = 80, CPW = 10, Z = 4, LDS_STRIDE = 84;
+};
+template <> struct Fmt<PN_TYPE_PN4T> {
+    static constexpr int BITS = 4, G = 64, CPW = 8, Z = 8, LDS_STRIDE = 68;
+};
+
+constexpr int kBlockBytes = 34;
+
+// One PN block brought into registers without assuming 4-byte alignment of its words.
+// A block at byte address p (2-byte aligned) is read as 32 bytes from the 4-byte aligned address
+// q4 plus one 16-bit piece at q2:
+//   p = 0 mod 4: q4 = p (d and words 0..6 straddle dwords), q2 = p + 32 (upper half of word 7);
+//   p = 2 mod 4: q4 = p + 2 (the eight words, aligned), q2 = p (d).
+// Exactly the block's 34 bytes are read, never a byte past it.
+struct RawBlock {
+    uint32_t dw[8];
+    uint32_t piece;  // the 16-bit piece, zero-extended
+    uint32_t shift;  // 16 when p = 0 mod 4, 0 when p = 2 mod 4 (funnel-shift amount)
+};
+
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ void load_block(const uint8_t *p, RawBlock &rb)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const bool odd = (a & 2u) != 0;  // p = 2 mod 4
+    const uint8_t *q4 = odd ? p + 2 : p;
+    const uint8_t *q2 = odd ? p : p + 32;
+    // Ordinary (temporal) loads: the three loads of a block, and neighbouring lanes' blocks, share
+    // cache lines; non-temporal loads measured slower here.
+    const u32x4a4 v0 = *reinterpret_cast<const u32x4a4 *>(q4);
+    const u32x4a4 v1 = *reinterpret_cast<const u32x4a4 *>(q4 + 16);
+    rb.piece = *reinterpret_cast<const uint16_t *>(q2);
+    rb.dw[0] = v0.x; rb.dw[1] = v0.y; rb.dw[2] = v0.z; rb.dw[3] = v0.w;
+    rb.dw[4] = v1.x; rb.dw[5] = v1.y; rb.dw[6] = v1.z; rb.dw[7] = v1.w;
+    rb.shift = odd ? 0u : 16u;
+}
+
+// Word i (0..7) of the block, as the little-endian u32 at byte 2 + 4i of the block.
+__device__ __forceinline__ uint32_t block_word(const RawBlock &rb, int i)
+{
+    const uint32_t hi = (i < 7) ? rb.dw[i + 1] : rb.piece;
+    return __builtin_amdgcn_alignbit(hi, rb.dw[i], rb.shift);
+}
+
+// The fp16 scale d of the block in the low 16 bits (upper bits undefined).
+__device__ __forceinline__ uint32_t block_d_bits(const RawBlock &rb)
+{
+    return rb.shift ? rb.dw[0] : rb.piece;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Host side --------------------------------------------------------------------------------------
+
+// Checks that the current device is gfx950 (cached per device). Returns PN_OK, PN_ERR_HIP or
+// PN_ERR_DEVICE.
+int check_device();
+
+// Maps the launch status of the last kernel to PN_OK / PN_ERR_HIP.
+int launch_status();
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int pn_group(int type)
+{
+    return type == PN_TYPE_PN3T ? 80 : type == PN_TYPE_PN4T ? 64 : 0;
+}
+
+}  // namespace pn

@@ -1,0 +1,192 @@
+// pn_nvfp4_gemv.hip -- W4A16 decode-step GEMV over NVFP4 weights, M = 1..4 bf16 tokens, gfx950.
+//
+// Format: "Quantisation and profiles", section "NVFP4": w = e2m1(code) * weight_scale[n, k/16] *
+// weight_scale_2; NInfer "tensor formats" section 3.3 for the E2M1 / E4M3FN words. Layout: codes
+// [N, K/2] with even k in the low nibble, scales [N, K/16], one fp32 global multiplier g.
+//
+// Design: like the PN GEMV, a workgroup stages x (bf16 pairs) in LDS and each wave streams R rows;
+// lane l takes groups of 16 weights l, l+64, ... (8 code bytes and 1 scale byte, coalesced).
+// v_cvt_scalef32_pk_bf16_fp4 turns one code byte into a pair of bf16 weights (exact: E2M1 values
+// have 2 significant bits) and v_dot2_f32_bf16 multiplies the pair with the matching bf16 x pair
+// into an fp32 sum: one instruction per weight. The group's E4M3 scale multiplies the group sum
+// once; g multiplies the row total once.
+#include "pn_common.h"
+
+namespace pn {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroupLdsWords = 12;  // 8 bf16 pairs of a group + 4 words of bank padding
+
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float v;
+    if (e == 0)
+        v = (float)m * 0x1p-9f;
+    else if (e == 15 && m == 7)
+        v = __builtin_nanf("");
+    else
+        v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
+template <int M>
+__device__ __forceinline__ void stage_x_bf16(uint32_t *lds, const uint16_t *__restrict__ x,
+                                             int64_t K, int pg0, int pg)
+{
+    const int pairs = pg * 8;
+    for (int q = threadIdx.x; q < M * pairs; q += blockDim.x) {
+        const int m = q / pairs, rem = q - m * pairs;
+        const int j = rem >> 3, i = rem & 7;
+        const int64_t k = (int64_t)pg0 * 16 + 2 * rem;
+        const uint32_t v = (uint32_t)x[(int64_t)m * K + k] | ((uint32_t)x[(int64_t)m * K + k + 1] << 16);
+        lds[(m * pg + j) * kGroupLdsWords + i] = v;
+    }
+}
+
+template <int M, int R>
+__global__ void __launch_bounds__(256) nvfp4_gemv_kernel(const uint8_t *__restrict__ codes,
+                                                         const uint8_t *__restrict__ scales,
+                                                         float g, int64_t N, int64_t K,
+                                                         const uint16_t *__restrict__ x,
+                                                         float *__restrict__ y, int phase_groups)
+{
+    extern __shared__ uint32_t xl[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    const int ngroups = (int)(K >> 4);
+
+    float acc[M][R];
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            acc[m][r] = 0.0f;
+
+    for (int pg0 = 0; pg0 < ngroups; pg0 += phase_groups) {
+        const int pg = min(phase_groups, ngroups - pg0);
+        if (pg0)
+            __syncthreads();
+        stage_x_bf16<M>(xl, x, K, pg0, pg);
+        __syncthreads();
+        if (row0 >= N)
+            continue;
+        const uint8_t *cp[R];
+        const uint8_t *sp[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t row = min(row0 + r, N - 1);
+            cp[r] = codes + row * (K >> 1) + (int64_t)pg0 * 8;
+            sp[r] = scales + row * ngroups + pg0;
+        }
+        for (int j = lane; j < pg; j += 64) {
+            uint2 cw[R];
+            uint32_t sw[R];
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                cw[r] = *reinterpret_cast<const uint2 *>(cp[r] + 8 * j);
+                sw[r] = sp[r][j];
+            }
+            float part[M][R];
+#pragma unroll
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int r = 0; r < R; r++)
+                    part[m][r] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const uint32_t *xg = xl + (m * pg + j) * kGroupLdsWords;
+                uint32_t xp[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    xp[i] = xg[i];
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    float s = part[m][r];
+#define PN_FP4_PAIR(word, sel, xi)                                                                 \
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, sel), \
+                                        __builtin_bit_cast(bf16x2_t, xp[xi]), s, false)
+                    PN_FP4_PAIR(cw[r].x, 0, 0);
+                    PN_FP4_PAIR(cw[r].x, 1, 1);
+                    PN_FP4_PAIR(cw[r].x, 2, 2);
+                    PN_FP4_PAIR(cw[r].x, 3, 3);
+                    PN_FP4_PAIR(cw[r].y, 0, 4);
+                    PN_FP4_PAIR(cw[r].y, 1, 5);
+                    PN_FP4_PAIR(cw[r].y, 2, 6);
+                    PN_FP4_PAIR(cw[r].y, 3, 7);
+#undef PN_FP4_PAIR
+                    part[m][r] = s;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const float S = e4m3_value(sw[r]);
+#pragma unroll
+                for (int m = 0; m < M; m++)
+                    acc[m][r] = __builtin_fmaf(S, part[m][r], acc[m][r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const float s = wave_sum(acc[m][r]);
+            if (lane == 0 && row0 + r < N)
+                y[(int64_t)m * N + row0 + r] = s * g;
+        }
+}
+
+constexpr int kNvLdsBudget = 80 * 1024;
+
+template <int M, int R>
+static int launch_nv(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
+                     const uint16_t *x, float *y, hipStream_t s)
+{
+    const int ngroups = (int)(K >> 4);
+    const int per_group = M * kGroupLdsWords * 4;
+    const int phase_groups = min(ngroups, kNvLdsBudget / per_group);
+    auto kern = nvfp4_gemv_kernel<M, R>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kNvLdsBudget) != hipSuccess)
+            return PN_ERR_HIP;
+        attr_set = true;
+    }
+    const int64_t rows_per_wg = 4 * R;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), dim3(256),
+                       (size_t)phase_groups * per_group, s, codes, scales, g, N, K, x, y,
+                       phase_groups);
+    return launch_status();
+}
+
+}  // namespace pn
+
+using namespace pn;
+
+extern "C" int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int64_t N,
+                             int64_t K, const uint16_t *x_bf16, int64_t M, float *y, void *stream)
+{
+    if (N < 0 || K <= 0 || K % 16)
+        return PN_ERR_SHAPE;
+    if (M < 0 || M > PN_MAX_TOKENS)
+        return PN_ERR_TOKENS;
+    if (N == 0 || M == 0)
+        return PN_OK;
+    if (!codes || !scales || !x_bf16 || !y)
+        return PN_ERR_NULL;
+    if (!aligned(codes, 8) || !aligned(x_bf16, 2) || !aligned(y, 4))
+        return PN_ERR_ALIGN;
+    int st = check_device();
+    if (st != PN_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    switch (M) {
+    case 1: return launch_nv<1, 2>(codes, scales, g, N, K, x_bf16, y, s);
+    case 2: return launch_nv<2, 2>(codes, scales, g, N, K, x_bf16, y, s);
+    case 3: return launch_nv<3, 2>(codes, scales, g, N, K, x_bf16, y, s);
+    default: return launch_nv<4, 2>(codes, scales, g, N, K, x_bf16, y, s);
+    }
+}

@@ -1,0 +1,137 @@
+/*
+ * pn.h -- C ABI of libpn.so: decode-step GEMV y = W.x over block-quantized weights decoded in
+ * registers, on AMD Instinct MI355X (gfx950).
+ *
+ * Formats:
+ *   PN (pn3t, pn4t)  "PN weight format" (PNX-FORMAT-v0), sections "Types", "Block layout",
+ *                    "Value", "Reference quantizer", "Validation".
+ *   NVFP4 (W4A16)    "Quantisation and profiles", sections "NVFP4" and "The clip search";
+ *                    NInfer "tensor formats", section 3.3 (E2M1 and E4M3FN words, validity).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument that names a tensor is a DEVICE pointer, owned by the caller. The
+ *     library allocates nothing and keeps no pointer after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously on it;
+ *     the call returns after argument checks and kernel launch, not after completion.
+ *   - The return value is a status (PN_OK = 0, or a negative PN_ERR_*), decided synchronously from
+ *     the arguments and the launch. Per-row verdicts and quantizer statuses are device outputs.
+ *   - Nothing falls back silently: a shape, dtype or device this library does not handle is an
+ *     error, never a slower path on another device.
+ *   - N == 0, nrows == 0 or M == 0 is a no-op that returns PN_OK. K must be a positive whole
+ *     number of blocks (80 for pn3t, 64 for pn4t, 16 for NVFP4); otherwise PN_ERR_SHAPE.
+ *
+ * PN tensor layout: W is N rows of K weights; row n starts at byte n * pn_row_bytes(type, K); a
+ * row is K/80 (pn3t) or K/64 (pn4t) consecutive 34-byte blocks. Block b of a row starts at byte
+ * 34*b: bytes 0..1 hold d (fp16, little-endian, signed), bytes 2..33 hold eight little-endian u32
+ * words. W needs only 2-byte alignment; nothing assumes a word is 4-byte aligned.
+ */
+#ifndef PN_H
+#define PN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ggml type ids of the two PN types ("PN weight format", "Types"). */
+enum { PN_TYPE_PN3T = 124, PN_TYPE_PN4T = 125 };
+
+/* Status codes. */
+enum {
+    PN_OK = 0,
+    PN_ERR_TYPE = -1,   /* type is neither PN_TYPE_PN3T nor PN_TYPE_PN4T */
+    PN_ERR_SHAPE = -2,  /* K is not a positive whole number of blocks, or a size is negative */
+    PN_ERR_TOKENS = -3, /* M (tokens) outside 0..4 */
+    PN_ERR_NULL = -4,   /* a required pointer is NULL */
+    PN_ERR_ALIGN = -5,  /* W not 2-byte aligned, x / y / w not 4-byte aligned, bf16 x not 2-byte */
+    PN_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
+    PN_ERR_DEVICE = -7  /* the current device is not gfx950 */
+};
+
+/* Maximum tokens per GEMV call. */
+#define PN_MAX_TOKENS 4
+
+/* Bytes of one PN row of K weights: 34*K/80 (pn3t) or 34*K/64 (pn4t); 0 if K is not a positive
+ * multiple of the block size or type is unknown. Host-only, no device work. */
+int64_t pn_row_bytes(int type, int64_t K);
+
+/* Human-readable name of a status code (static storage). */
+const char *pn_status_string(int status);
+
+/* ---- PN validation ("PN weight format", "Validation") --------------------------------------
+ * verdict[r] = 1 if row r is valid, 0 if it is invalid: some block's d is an fp16 NaN or infinity,
+ * or (pn3t) bit 15 or bit 31 of some word is set. verdict is int32[nrows] on the device. */
+int pn_validate_rows(int type, const void *W, int64_t nrows, int64_t K, int32_t *verdict,
+                     void *stream);
+/* One row (nrows = 1). */
+int pn_validate_row(int type, const void *row, int64_t K, int32_t *verdict, void *stream);
+
+/* ---- PN decode ("PN weight format", "Value") -----------------------------------------------
+ * out[r*K + k] = fp32(d) * (n - z) for every weight, bit-exact: the product is exact in fp32, IEEE
+ * signs apply (code z with a negative d gives -0.0; d = +0 with n < z gives -0.0), fp16 subnormal
+ * d are kept. Reserved bits are ignored by the decode (they only make the row invalid). A
+ * non-finite d decodes as the IEEE product (NaN or +-inf). out is fp32[nrows, K]. */
+int pn_dequantize_rows(int type, const void *W, int64_t nrows, int64_t K, float *out,
+                       void *stream);
+int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *stream);
+
+/* ---- PN GEMV -------------------------------------------------------------------------------
+ * y[m*N + n] = sum_k w[n, k] * x[m*K + k] for m < M (1 <= M <= 4 tokens), with w the decode above,
+ * accumulated in fp32. x is fp32[M, K] row-major, y fp32[M, N] row-major (overwritten). Accuracy:
+ * |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100. Rows are not validated
+ * here (validate at load); an invalid row gives an unspecified value but no out-of-bounds access.
+ * Deterministic: the same inputs give the same bits on every call. */
+int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
+            void *stream);
+
+/* ---- PN reference quantizer ("PN weight format", "Reference quantizer") ---------------------
+ * Quantizes fp32 w[nrows, K] (row-major) into PN rows W (nrows * pn_row_bytes bytes), one group of
+ * 80 or 64 weights per block: 36 candidate scales s = fp16(sigma * m * amax / z),
+ * m = 0.50, 0.52, ..., 1.20, codes clamp(rint(w/s) + z, 0, 2z-1), double-precision squared error,
+ * ties to the larger m; an all-zero group, or one whose candidates all round to zero, is the
+ * canonical zero group (d = +0, codes z). Bit-identical to the library's CPU oracle.
+ * status (int32[nrows], optional, may be NULL) receives per row the OR of: 1 = a group held a NaN
+ * or infinity, 2 = every candidate scale overflowed fp16 (such groups are written as the canonical
+ * zero group). */
+int pn_quantize_rows(int type, const float *w, int64_t nrows, int64_t K, void *W, int32_t *status,
+                     void *stream);
+
+/* ---- NVFP4 W4A16 ---------------------------------------------------------------------------
+ * Layout: codes uint8[N, K/2], element k of a row in byte k/2, even k in the low nibble (E2M1
+ * words); scales uint8[N, K/16], one E4M3FN word per group of 16 consecutive k; one fp32 global
+ * multiplier g (weight_scale_2). A weight is fp32(fp32(e2m1(code) * e4m3(scale)) * g). */
+
+/* verdict[n] = 1 iff every scale word of row n has sign bit 0 and is not NaN (0x7F), and g is
+ * finite and > 0. */
+int pn_nvfp4_validate_rows(const uint8_t *scales, float g, int64_t N, int64_t K, int32_t *verdict,
+                           void *stream);
+
+/* out fp32[N, K], bit-exact decode as above. */
+int pn_nvfp4_dequantize_rows(const uint8_t *codes, const uint8_t *scales, float g, int64_t N,
+                             int64_t K, float *out, void *stream);
+
+/* y[m*N + n] = sum_k w[n, k] * x[m, k], x bf16[M, K] (raw 16-bit words, row-major), 1 <= M <= 4,
+ * fp32 accumulation; same accuracy contract as pn_gemv. */
+int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
+                  const uint16_t *x_bf16, int64_t M, float *y, void *stream);
+
+/* g_out (one device float) = fp32(amax(|w|) / (6 * 448)) over count fp32 values, 1.0 for an
+ * all-zero tensor, NaN if w holds a NaN or infinity. */
+int pn_nvfp4_global_scale(const float *w, int64_t count, float *g_out, void *stream);
+
+/* Clip-search quantizer ("The clip search", uniform channel weights): per group of 16, multipliers
+ * 1.00, 0.95, 0.90, 0.85, 0.80 on the scale e4m3(c * amax_group / (6 g)) (nearest, ties to even,
+ * saturating at 448), codes the nearest E2M1 word of w / (S g) (ties to even, saturating at 6, sign
+ * kept), squared error of the decoded weights in double, ties keep the earlier multiplier.
+ * g is read from device memory (g_dev, e.g. written by pn_nvfp4_global_scale). Bit-identical to the
+ * library's CPU oracle. */
+int pn_nvfp4_quantize_rows(const float *w, int64_t N, int64_t K, const float *g_dev,
+                           uint8_t *codes, uint8_t *scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PN_H */

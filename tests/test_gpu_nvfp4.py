@@ -1,0 +1,142 @@
+"""GPU parity of the NVFP4 W4A16 path through the C ABI against the CPU oracle: bit-exact global
+scale, quantizer, validation and decode; GEMV within 1e-5 * sum |w x|."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_cases import nvfp4_quantized
+from test_gpu_pn import assert_bits_equal, assert_within
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_weight_pn3t_amd as pn
+    return pn, torch, torch.device("cuda:0")
+
+
+def up(torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gpu_quantize(pn, torch, dev, w):
+    N, K = w.shape
+    wd = up(torch, dev, w)
+    g = torch.zeros(1, dtype=torch.float32, device=dev)
+    pn.nvfp4_global_scale(wd, g)
+    codes = torch.zeros((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((N, K // 16), dtype=torch.uint8, device=dev)
+    pn.nvfp4_quantize_rows(wd, g, codes, scales)
+    torch.cuda.synchronize()
+    return float(g.item()), codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def gemv(pn, torch, dev, codes, scales, g, N, K, xb):
+    yd = torch.full((xb.shape[0], N), float("nan"), dtype=torch.float32, device=dev)
+    pn.gemv_nvfp4(up(torch, dev, codes), up(torch, dev, scales), g, N, K,
+                  up(torch, dev, xb.view(np.int16)), yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+def test_global_scale_and_quantizer_bit_exact(env):
+    pn, torch, dev = env
+    N, K = 64, 512
+    w = synth.gaussian_weights(501, N, K)
+    w[0, :16] = 0.0                               # an all-zero group
+    w[1, :16] = np.linspace(-1e-6, 1e-6, 16)      # scales that round to E4M3 zero/subnormal
+    w[2, 16:32] = 0.25 * np.arange(16) - 2.0      # E2M1 ties
+    w[3, 5] = 0.4                                 # the tensor's amax
+    g_ref = oracle.nvfp4_global_scale(w)
+    c_ref, s_ref = oracle.nvfp4_quantize_rows(w, g_ref)
+    g, c, s = gpu_quantize(pn, torch, dev, w)
+    assert np.float32(g).view(np.uint32) == np.float32(g_ref).view(np.uint32)
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(c, c_ref)
+
+
+def test_global_scale_special_tensors(env):
+    pn, torch, dev = env
+    for w in (np.zeros((2, 16), np.float32), np.array([[1.0] * 15 + [np.nan]], np.float32),
+              np.array([[-2688.0] + [0.0] * 15], np.float32)):
+        wd = up(torch, dev, w)
+        g = torch.zeros(1, dtype=torch.float32, device=dev)
+        pn.nvfp4_global_scale(wd, g)
+        torch.cuda.synchronize()
+        ref = oracle.nvfp4_global_scale(w)
+        got = float(g.item())
+        assert (np.isnan(got) and np.isnan(ref)) or got == ref
+
+
+def test_validate_and_dequantize_bit_exact(env):
+    pn, torch, dev = env
+    N, K = 24, 256
+    _, g, codes, scales = nvfp4_quantized(N, K, 511)
+    scales = scales.copy()
+    scales[1, 3] = 0x80
+    scales[2, 0] = 0xB8
+    scales[3, 7] = 0x7F
+    scales[4, 15] = 0xFF
+    scales[5, 2] = 0x00
+    codes = codes.copy()
+    codes[6, :] = np.arange(K // 2) % 256  # every code word
+    ver = torch.full((N,), -1, dtype=torch.int32, device=dev)
+    for gg in (g, 0.0, -1.0, float("inf"), float("nan")):
+        pn.nvfp4_validate_rows(up(torch, dev, scales), gg, N, K, ver)
+        torch.cuda.synchronize()
+        assert np.array_equal(ver.cpu().numpy(), oracle.nvfp4_validate_rows(scales, gg, N, K))
+    for gg in (g, 1.0, 1e-30, 3.0e36):
+        out = torch.empty((N, K), dtype=torch.float32, device=dev)
+        pn.nvfp4_dequantize_rows(up(torch, dev, codes), up(torch, dev, scales), gg, N, K, out)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), oracle.nvfp4_dequantize_rows(codes, scales, gg, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K", [(64, 512), (37, 16 * 67), (5, 16)])
+def test_gemv_small(env, M, N, K):
+    pn, torch, dev = env
+    _, g, codes, scales = nvfp4_quantized(N, K, 520 + K)
+    xb = synth.activations_bf16(521, M, K)
+    y = gemv(pn, torch, dev, codes, scales, g, N, K, xb)
+    y_ref, bound = oracle.nvfp4_gemv(codes, scales, g, N, K, xb)
+    assert_within(y, y_ref, bound)
+
+
+def test_gemv_one_hot_exact(env):
+    pn, torch, dev = env
+    N, K = 40, 256
+    _, g, codes, scales = nvfp4_quantized(N, K, 530)
+    deq = oracle.nvfp4_dequantize_rows(codes, scales, g, N, K)
+    ks = [0, 1, 16, 255]
+    xb = np.zeros((4, K), np.uint16)
+    for m, k in enumerate(ks):
+        xb[m, k] = 0x3F80
+    y = gemv(pn, torch, dev, codes, scales, g, N, K, xb)
+    for m, k in enumerate(ks):
+        # one product e2m1 * S, then * g: the same two roundings as the decode
+        assert np.array_equal(y[m], deq[:, k])
+
+
+@pytest.mark.slow
+def test_config5_full_size(env):
+    pn, torch, dev = env
+    N, K = 17408, 5120
+    w, g, codes, scales = nvfp4_quantized(N, K, 501)
+    g2, c2, s2 = gpu_quantize(pn, torch, dev, w)
+    assert g2 == g and np.array_equal(s2, scales) and np.array_equal(c2, codes)
+    out = torch.empty((N, K), dtype=torch.float32, device=dev)
+    pn.nvfp4_dequantize_rows(up(torch, dev, codes), up(torch, dev, scales), g, N, K, out)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), oracle.nvfp4_dequantize_rows(codes, scales, g, N, K))
+    del out
+    xb = synth.activations_bf16(502, 4, K)
+    y_ref4, bound4 = oracle.nvfp4_gemv(codes, scales, g, N, K, xb)
+    for M in (1, 2, 3, 4):
+        y = gemv(pn, torch, dev, codes, scales, g, N, K, xb[:M])
+        assert_within(y, y_ref4[:M], bound4[:M])
