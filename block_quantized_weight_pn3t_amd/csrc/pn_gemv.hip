@@ -4,41 +4,50 @@
 // BITS*(t>>1) + 16*(t&1), no code crosses a 16-bit half), "Value" (w = d * (n - z)).
 //
 // Design (HBM-bound; no MFMA: this is a matrix-vector product, not a dense contraction):
-//  * Persistent: one workgroup per CU. Rows are split into contiguous, balanced ranges, one per
-//    wave. A wave streams its rows through a ring of register buffers so several rows of loads
-//    are in flight while one is decoded. Loads are never inside a branch (indices are clamped),
-//    which keeps the hardware wait counts exact. Weight loads are 2 x 16 bytes from
-//    a 4-byte aligned address plus 2 bytes, exactly the block's 34 bytes at either alignment
-//    parity, re-aligned with v_alignbit.
-//  * Decode uses the pairing of the layout: one AND with a mask like 0x00070007 leaves two codes,
-//    one per 16-bit half, at bit position p of the half. As fp16 words those halves are the exact
-//    subnormals n * 2^(p-24), i.e. a ready-made fp16 pair for v_dot2_f32_f16 (full rate on gfx950;
-//    the mixed-precision FMA v_fma_mix_f32 and v_cvt_f32_f16 issue at half rate). x is staged per
-//    block as fp16 pairs: x' = x * 2^(24-p) * 2^-s (s puts the block's largest |x'| in
-//    [2^14, 2^15)), split into hi = fp16(x') and lo = fp16(x' - hi), so each pair of weights costs
-//    two dot2 (hi, lo) and x keeps ~22 significant bits:
-//      pn3t word: 1 shift + 5 AND + 10 DOT2 for 10 weights; pn4t: 1 shift + 4 AND + 8 DOT2 for 8.
+//  * Persistent: one workgroup of 4 or 8 waves per CU (a multiple of the CU's 4 SIMDs). Rows are
+//    split into contiguous, balanced ranges, one per wave. A wave streams its rows through a ring
+//    of register buffers so several rows of loads are in flight while one is decoded. Loads are
+//    never inside a branch (indices are clamped), which keeps the hardware wait counts exact.
+//    A block is read as 2 x 16 bytes from a 4-byte aligned address plus 2 bytes -- exactly its 34
+//    bytes at either alignment parity -- and re-aligned with v_alignbit.
+//  * Code extraction uses the pairing of the layout: one AND with a mask like 0x00070007 (pn3t) or
+//    0x0F0F0F0F (pn4t) isolates several codes at once; the decode then uses only full-rate
+//    instructions where it can (on gfx950 v_fma_mix_f32 and v_cvt_f32_f16 issue at half rate):
+//    - pn4t: the masked bytes 0..15 read as E4M3 are exactly n * 2^-9, so v_cvt_pk_f32_fp8 turns
+//      two codes into two fp32 values; x is staged as fp32 * 2^9 in the matching byte order.
+//      Per word: 3 bit ops + 4 conversions + 8 FMA for 8 weights.
+//    - pn3t, rows of <= 64 blocks (K <= 5120): a masked 16-bit half holding n << p reads as the
+//      exact fp16 subnormal n * 2^(p-24), so the two codes one mask leaves form an fp16 pair for
+//      v_dot2_f32_f16. x is staged as fp16 pairs x' = x * 2^(24-p-s) (s per block puts the largest
+//      |x'| near 2^15), split into hi and lo halves (lo = the exact remainder), ~20 significant
+//      bits. Per word: 1 shift + 5 AND + 10 DOT2 for 10 weights.
+//    - pn3t, longer rows or 3-4 tokens: fp32 x staged as x * 2^(24-p) and v_fma_mix_f32 on the
+//      same fp16 subnormal codes (half rate, but the staging stays a plain copy).
 //  * The zero point is folded per block: sum_k (n_k - z) x_k = sum_k n_k x_k - z * sum_k x_k, with
-//    the block's plain sum of x staged next to the pairs; d * 2^s multiplies once per block.
-//  * fp32 accumulation; the R rows x M tokens of partial sums are reduced together by a
-//    transposed permlane/DPP reduction. Each output is produced by one wave in a fixed order:
-//    results are deterministic (no atomics).
+//    the block's plain sum of x staged next to x; d (times the block's 2^s) multiplies once.
+//  * fp32 accumulation; R rows x M tokens of partial sums are reduced together by a transposed
+//    permlane/DPP reduction. Each output is produced by one wave in a fixed order: results are
+//    deterministic (no atomics).
 //  * Rows of at most 64 blocks keep the staged x of their block in registers (lane l owns block l);
 //    longer rows stage x in LDS once per workgroup (in K-phases when it does not fit).
 #include <stdlib.h>
+
+#include <algorithm>
 
 #include "pn_common.h"
 
 namespace pn {
 
 typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Bit position p, inside its 16-bit half after the masking below, of code t of a word: pn3t t = 0,1
-// and 6,7 sit at p = 0; t = 2,3 and 8,9 at p = 3; t = 4,5 at p = 6 (t = 6..9 after a >> 9).
-// pn4t: t = 0,1 and 4,5 at p = 0; t = 2,3 and 6,7 at p = 4 (t = 4..7 after a >> 8).
-template <int TYPE> __device__ __forceinline__ int code_pos(int t);
-template <> __device__ __forceinline__ int code_pos<PN_TYPE_PN3T>(int t) { return 3 * ((t >> 1) % 3); }
-template <> __device__ __forceinline__ int code_pos<PN_TYPE_PN4T>(int t) { return 4 * ((t >> 1) & 1); }
+// Bit position p, inside its 16-bit half after the masking used below, of code t of a word: pn3t
+// t = 0,1 and 6,7 sit at p = 0; t = 2,3 and 8,9 at p = 3; t = 4,5 at p = 6 (t = 6..9 after >> 9).
+__device__ __forceinline__ int pn3t_code_pos(int t) { return 3 * ((t >> 1) % 3); }
+
+// pn4t staging slot of code t inside its word: the conversion order (t0,t4), (t1,t5), (t2,t6),
+// (t3,t7) of the bytes of w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F.
+__device__ __forceinline__ int pn4t_slot(int t) { return (t < 4) ? 2 * t : 2 * (t - 4) + 1; }
 
 __device__ __forceinline__ float dot2(uint32_t codes, uint32_t xpair, float acc)
 {
@@ -46,14 +55,38 @@ __device__ __forceinline__ float dot2(uint32_t codes, uint32_t xpair, float acc)
                                   __builtin_bit_cast(h16x2_t, xpair), acc, false);
 }
 
-// ah += sum over the word's codes of n_t * x'hi_t, al the same with the lo parts. xp holds the
-// word's CPW/2 pairs as (hi, lo) dwords: xp[2j] = hi pair j, xp[2j+1] = lo pair j.
-template <int TYPE>
-__device__ __forceinline__ void word_dot(uint32_t w, const uint32_t *xp, float &ah, float &al);
+__device__ __forceinline__ float h_lo(uint32_t a) { return (float)__builtin_bit_cast(_Float16, (uint16_t)a); }
+__device__ __forceinline__ float h_hi(uint32_t a) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(a >> 16)); }
 
-template <>
-__device__ __forceinline__ void word_dot<PN_TYPE_PN3T>(uint32_t w, const uint32_t *xp, float &ah,
-                                                       float &al)
+// ---- per-word decode + multiply-accumulate ----------------------------------------------------
+
+// pn4t, fp32 x staged * 2^9 in slot order: acc0/acc1 += sum_t n_t * x_t.
+__device__ __forceinline__ void word_fp8(uint32_t w, const float *xs, float &acc0, float &acc1)
+{
+    const uint32_t a = w & 0x0F0F0F0Fu;         // bytes: t0 t4 t1 t5
+    const uint32_t b = (w >> 4) & 0x0F0F0F0Fu;  // bytes: t2 t6 t3 t7
+    const f32x2_t c0 = __builtin_amdgcn_cvt_pk_f32_fp8(a, false);
+    const f32x2_t c1 = __builtin_amdgcn_cvt_pk_f32_fp8(a, true);
+    const f32x2_t c2 = __builtin_amdgcn_cvt_pk_f32_fp8(b, false);
+    const f32x2_t c3 = __builtin_amdgcn_cvt_pk_f32_fp8(b, true);
+    acc0 = __builtin_fmaf(c0.x, xs[0], acc0);
+    acc1 = __builtin_fmaf(c0.y, xs[1], acc1);
+    acc0 = __builtin_fmaf(c1.x, xs[2], acc0);
+    acc1 = __builtin_fmaf(c1.y, xs[3], acc1);
+    acc0 = __builtin_fmaf(c2.x, xs[4], acc0);
+    acc1 = __builtin_fmaf(c2.y, xs[5], acc1);
+    acc0 = __builtin_fmaf(c3.x, xs[6], acc0);
+    acc1 = __builtin_fmaf(c3.y, xs[7], acc1);
+}
+
+// pn3t, fp16 x pairs as (hi, lo) dwords (held in float registers): ah/al += sum_t n_t * x'hi_t /
+// x'lo_t.
+__device__ __forceinline__ float dot2f(uint32_t codes, float xpair, float acc)
+{
+    return dot2(codes, __builtin_bit_cast(uint32_t, xpair), acc);
+}
+
+__device__ __forceinline__ void word_dot2(uint32_t w, const float *xp, float &ah, float &al)
 {
     const uint32_t a0 = w & 0x00070007u;  // t = 0 | t = 1   (p = 0)
     const uint32_t a1 = w & 0x00380038u;  // t = 2 | t = 3   (p = 3)
@@ -61,72 +94,77 @@ __device__ __forceinline__ void word_dot<PN_TYPE_PN3T>(uint32_t w, const uint32_
     const uint32_t ws = w >> 9;
     const uint32_t a3 = ws & 0x00070007u; // t = 6 | t = 7   (p = 0)
     const uint32_t a4 = ws & 0x00380038u; // t = 8 | t = 9   (p = 3)
-    ah = dot2(a0, xp[0], ah);
-    al = dot2(a0, xp[1], al);
-    ah = dot2(a1, xp[2], ah);
-    al = dot2(a1, xp[3], al);
-    ah = dot2(a2, xp[4], ah);
-    al = dot2(a2, xp[5], al);
-    ah = dot2(a3, xp[6], ah);
-    al = dot2(a3, xp[7], al);
-    ah = dot2(a4, xp[8], ah);
-    al = dot2(a4, xp[9], al);
+    ah = dot2f(a0, xp[0], ah);
+    al = dot2f(a0, xp[1], al);
+    ah = dot2f(a1, xp[2], ah);
+    al = dot2f(a1, xp[3], al);
+    ah = dot2f(a2, xp[4], ah);
+    al = dot2f(a2, xp[5], al);
+    ah = dot2f(a3, xp[6], ah);
+    al = dot2f(a3, xp[7], al);
+    ah = dot2f(a4, xp[8], ah);
+    al = dot2f(a4, xp[9], al);
 }
 
-template <>
-__device__ __forceinline__ void word_dot<PN_TYPE_PN4T>(uint32_t w, const uint32_t *xp, float &ah,
-                                                       float &al)
+// pn3t, fp32 x staged * 2^(24-p): acc0/acc1 += sum_t n_t * x_t (mixed-precision FMA).
+__device__ __forceinline__ void word_mix(uint32_t w, const float *xs, float &acc0, float &acc1)
 {
-    const uint32_t a0 = w & 0x000F000Fu;  // t = 0 | t = 1   (p = 0)
-    const uint32_t a1 = w & 0x00F000F0u;  // t = 2 | t = 3   (p = 4)
-    const uint32_t ws = w >> 8;
-    const uint32_t a2 = ws & 0x000F000Fu; // t = 4 | t = 5   (p = 0)
-    const uint32_t a3 = ws & 0x00F000F0u; // t = 6 | t = 7   (p = 4)
-    ah = dot2(a0, xp[0], ah);
-    al = dot2(a0, xp[1], al);
-    ah = dot2(a1, xp[2], ah);
-    al = dot2(a1, xp[3], al);
-    ah = dot2(a2, xp[4], ah);
-    al = dot2(a2, xp[5], al);
-    ah = dot2(a3, xp[6], ah);
-    al = dot2(a3, xp[7], al);
+    const uint32_t a0 = w & 0x00070007u;
+    const uint32_t a1 = w & 0x00380038u;
+    const uint32_t a2 = w & 0x01C001C0u;
+    const uint32_t ws = w >> 9;
+    const uint32_t a3 = ws & 0x00070007u;
+    const uint32_t a4 = ws & 0x00380038u;
+    acc0 = __builtin_fmaf(h_lo(a0), xs[0], acc0);
+    acc1 = __builtin_fmaf(h_hi(a0), xs[1], acc1);
+    acc0 = __builtin_fmaf(h_lo(a1), xs[2], acc0);
+    acc1 = __builtin_fmaf(h_hi(a1), xs[3], acc1);
+    acc0 = __builtin_fmaf(h_lo(a2), xs[4], acc0);
+    acc1 = __builtin_fmaf(h_hi(a2), xs[5], acc1);
+    acc0 = __builtin_fmaf(h_lo(a3), xs[6], acc0);
+    acc1 = __builtin_fmaf(h_hi(a3), xs[7], acc1);
+    acc0 = __builtin_fmaf(h_lo(a4), xs[8], acc0);
+    acc1 = __builtin_fmaf(h_hi(a4), xs[9], acc1);
 }
 
-// ---- x staging ----------------------------------------------------------------------------------
-// One staged block of x (G consecutive values of one token) is G + 2 dwords: the G/2 pairs as
-// (hi, lo) dwords, then sxs = (sum of the block's x) * 2^-s and scl = 2^s.
+// ---- fp32 x staging in LDS (general kernel) ----------------------------------------------------
+// Token m, block b of a K-phase at float offset (m*pn + b)*LDS_STRIDE: the G staged values (pn4t:
+// x * 2^9 in slot order; pn3t: x * 2^(24-p) in k order), then at offset G the block's plain sum.
 
-// Scale exponent of a block: s such that max_e |x_e| * 2^(24 - p_e - s) lies in [2^14, 2^15).
-__device__ __forceinline__ int block_shift(float amax_scaled)
+template <int TYPE> __device__ __forceinline__ float stage_factor(int t);
+template <> __device__ __forceinline__ float stage_factor<PN_TYPE_PN3T>(int t)
 {
-    if (!(amax_scaled > 0.0f) || !(amax_scaled < __builtin_inff()))
-        return 0;  // all zero, or non-finite input (the result is then non-finite too)
-    return __builtin_amdgcn_frexp_expf(amax_scaled) - 15;
+    return __builtin_bit_cast(float, (uint32_t)(127 + 24 - pn3t_code_pos(t)) << 23);
 }
-
-__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
+template <> __device__ __forceinline__ float stage_factor<PN_TYPE_PN4T>(int)
 {
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return 512.0f;
 }
 
-// hi and lo fp16 pairs of two staged values (x' already scaled)
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo)
+// 2^(p - 24): the exact inverse of the pn3t staging factor.
+__device__ __forceinline__ float pn3t_unstage(int t)
 {
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    hi = pack_h2(ha, hb);
-    lo = pack_h2((_Float16)(a - (float)ha), (_Float16)(b - (float)hb));
+    return __builtin_bit_cast(float, (uint32_t)(127 - 24 + pn3t_code_pos(t)) << 23);
 }
 
-// Pass 1: 16-byte global loads of x, plain fp32 values written to their block slots in LDS.
-// Unrolled so that every thread has its loads in flight together.
+template <int TYPE> __device__ __forceinline__ int stage_slot(int e)
+{
+    if (TYPE == PN_TYPE_PN4T)
+        return (e & ~7) + pn4t_slot(e & 7);
+    return e;
+}
+
+// Pass 1: coalesced 16-byte loads of four consecutive x of one block, scaled and written to their
+// slots. pn4t: the 16 quads of a block are the 16 lanes of one DPP row, which also produce the
+// block's plain sum (quad sums, then a fixed butterfly). pn3t (20 quads per block): see pass 2.
 template <int TYPE, int M>
-__device__ __forceinline__ void stage_x_raw(float *lds, const float *__restrict__ x, int64_t K,
-                                            int pb, int pn, bool vec4)
+__device__ __forceinline__ void stage_x(float *lds, const float *__restrict__ x, int64_t K, int pb,
+                                        int pn, bool vec4)
 {
     using F = Fmt<TYPE>;
     constexpr int U = 8;
     const int per_tok = pn * (F::G / 4);
-    const int total = M * per_tok;
+    const int total = M * per_tok;  // a multiple of 16
     for (int q0 = threadIdx.x; q0 < total; q0 += U * blockDim.x) {
         float4 v[U];
 #pragma unroll
@@ -144,55 +182,50 @@ __device__ __forceinline__ void stage_x_raw(float *lds, const float *__restrict_
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int q = q0 + u * blockDim.x;
-            if (q < total) {
+            if (q < total) {  // whole DPP rows are in or out (total and the row base are multiples of 16)
                 const int m = q / per_tok, c = q - m * per_tok;
                 const int b = (4 * c) / F::G, e = 4 * c - b * F::G;
-                *reinterpret_cast<float4 *>(lds + (m * pn + b) * F::LDS_STRIDE + e) = v[u];
+                float *blk = lds + (m * pn + b) * F::LDS_STRIDE;
+                const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    blk[stage_slot<TYPE>(e + i)] = vv[i] * stage_factor<TYPE>((e + i) % F::CPW);
+                if (TYPE == PN_TYPE_PN4T) {
+                    float s = ((vv[0] + vv[1]) + vv[2]) + vv[3];
+                    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+                    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+                    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
+                    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x140, 0xF, 0xF, false));
+                    if (e == 0)
+                        blk[F::G] = s;
+                }
             }
         }
     }
 }
 
-// Pass 2 (after a barrier), one thread per (token, block): sum and scale exponent, then the pairs
-// rewritten in place (pair q occupies exactly the dwords of values 2q and 2q+1).
+// Pass 2 (pn3t only, after a barrier): thread per (token, block) sums the block's x in k order,
+// recovering each value exactly from its power-of-two-scaled copy.
 template <int TYPE, int M>
-__device__ __forceinline__ void stage_x_pairs(float *lds, int pn)
+__device__ __forceinline__ void stage_block_sums(float *lds, int pn)
 {
     using F = Fmt<TYPE>;
     for (int q = threadIdx.x; q < M * pn; q += blockDim.x) {
-        float *blk = lds + q * F::LDS_STRIDE;
-        const float4 *src = reinterpret_cast<const float4 *>(blk);
-        float sum = 0.0f, amax = 0.0f;
+        const float4 *src = reinterpret_cast<const float4 *>(lds + q * F::LDS_STRIDE);
+        float s = 0.0f;
 #pragma unroll
         for (int c = 0; c < F::G / 4; c++) {
             const float4 v = src[c];
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                sum += vv[i];
-                amax = fmaxf(amax, __builtin_ldexpf(__builtin_fabsf(vv[i]),
-                                                    24 - code_pos<TYPE>((4 * c + i) % F::CPW)));
-            }
+            s += v.x * pn3t_unstage((4 * c + 0) % F::CPW);
+            s += v.y * pn3t_unstage((4 * c + 1) % F::CPW);
+            s += v.z * pn3t_unstage((4 * c + 2) % F::CPW);
+            s += v.w * pn3t_unstage((4 * c + 3) % F::CPW);
         }
-        const int s = block_shift(amax);
-        uint32_t *bw = reinterpret_cast<uint32_t *>(blk);
-#pragma unroll
-        for (int c = 0; c < F::G / 4; c++) {
-            const float4 v = src[c];
-            const int t0 = (4 * c) % F::CPW, t2 = (4 * c + 2) % F::CPW;
-            uint32_t h0, l0, h1, l1;
-            split_pair(__builtin_ldexpf(v.x, 24 - code_pos<TYPE>(t0) - s),
-                       __builtin_ldexpf(v.y, 24 - code_pos<TYPE>(t0) - s), h0, l0);
-            split_pair(__builtin_ldexpf(v.z, 24 - code_pos<TYPE>(t2) - s),
-                       __builtin_ldexpf(v.w, 24 - code_pos<TYPE>(t2) - s), h1, l1);
-            *reinterpret_cast<uint4 *>(bw + 4 * c) = make_uint4(h0, l0, h1, l1);
-        }
-        blk[F::G] = __builtin_ldexpf(sum, -s);
-        blk[F::G + 1] = __builtin_ldexpf(1.0f, s);
+        lds[q * F::LDS_STRIDE + F::G] = s;
     }
 }
 
-// ---- cross-lane reduction ---------------------------------------------------------------------
+// ---- cross-lane reduction -----------------------------------------------------------------------
 
 #define PN_DPP(v, ctrl)                                                                            \
     __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF,  \
@@ -245,27 +278,37 @@ __device__ __forceinline__ void transpose_reduce(float (&v)[V], float (&out)[V /
     }
 }
 
-// ---- the kernel -------------------------------------------------------------------------------
+// ---- kernels -------------------------------------------------------------------------------------
 
 template <int R>
 struct Item {
     RawBlock blk[R];
 };
 
-// Balanced contiguous row range of wave gw out of T: [begin, begin + count).
-__device__ __forceinline__ void wave_rows(int64_t N, int64_t T, int64_t gw, int64_t &begin, int &count)
+// Row range of a wave. The rows are split into balanced contiguous ranges over the SIMD slots
+// (4 per workgroup: a CU's SIMDs, which take the workgroup's waves round-robin), and each slot's
+// range over the waves that share that SIMD (wave w and w + 4 of an 8-wave group). Every SIMD thus
+// gets the same number of rows, +-1, whichever wave count divides it.
+__device__ __forceinline__ void wave_rows(int64_t N, int wave, int nwaves, int64_t &begin, int &count)
 {
-    begin = gw * N / T;
-    count = (int)((gw + 1) * N / T - begin);
+    const int per_simd = nwaves >> 2;  // 1 or 2
+    const int64_t S = (int64_t)gridDim.x * 4;
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (wave & 3);
+    const int h = wave >> 2;
+    const int64_t s0 = slot * N / S;
+    const int64_t cnt = (slot + 1) * N / S - s0;
+    const int64_t b0 = (h * cnt + per_simd - 1) / per_simd;
+    const int64_t b1 = ((h + 1) * cnt + per_simd - 1) / per_simd;
+    count = (int)(b1 - b0);
+    // an empty range may start at N; its (unused, clamped) prefetch must still address a real row
+    begin = min(s0 + b0, N - 1);
 }
 
-// ---- general kernel: x staged in LDS --------------------------------------------------------
-// Rows are split into T = gridDim.x * waves contiguous, balanced ranges, one per wave. A wave walks
-// its range R rows at a time; for each group, lane l takes blocks l, l+64, ... of the R rows (an
-// "item" is one 64-block slice of R rows). Items go through a ring of D register buffers: the loads
-// of item i + D - 1 are issued before item i is decoded. Each group ends with one transposed
-// reduction and a store. K-phases (x larger than LDS) run as an outer loop; phases after the first
-// add into y.
+// General kernel, fp32 x staged in LDS. A wave walks its rows R at a time; for each group, lane l
+// takes blocks l, l+64, ... of the R rows (an "item" is one 64-block slice of R rows). Items go
+// through a ring of D register buffers: the loads of item i + D - 1 are issued before item i is
+// decoded. Each group ends with one transposed reduction and a store. K-phases (x larger than LDS)
+// run as an outer loop; phases after the first add into y.
 template <int TYPE, int M, int R, int D>
 __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                        int nb, int64_t row_bytes,
@@ -281,7 +324,7 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     int64_t r_begin;
     int nrows;
-    wave_rows(N, (int64_t)gridDim.x * nwaves, (int64_t)blockIdx.x * nwaves + wave, r_begin, nrows);
+    wave_rows(N, wave, nwaves, r_begin, nrows);
     const int ngroups = (nrows + R - 1) / R;
     const uint8_t *wbase = W + r_begin * row_bytes;
 
@@ -310,10 +353,12 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
             load_item(buf[p], p);  // first weights in flight while x is staged
         if (pb)
             __syncthreads();
-        stage_x_raw<TYPE, M>(lds, x, K, pb, pn, x_vec4 != 0);
+        stage_x<TYPE, M>(lds, x, K, pb, pn, x_vec4 != 0);
         __syncthreads();
-        stage_x_pairs<TYPE, M>(lds, pn);
-        __syncthreads();
+        if (TYPE == PN_TYPE_PN3T) {
+            stage_block_sums<TYPE, M>(lds, pn);
+            __syncthreads();
+        }
 
         float acc[M][R];
 #pragma unroll
@@ -326,23 +371,24 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
             const int g = it / iters, i = it - g * iters;
             const int b = lane + 64 * i;
             const bool valid = b < pn;
+            const int live = min(R, nrows - g * R);  // rows of the group that exist (uniform)
             const float *xb = lds + min(b, pn - 1) * F::LDS_STRIDE;
-            float ah[M][R], al[M][R];
+            float a0[M][R], a1[M][R];
 #pragma unroll
             for (int m = 0; m < M; m++)
 #pragma unroll
                 for (int r = 0; r < R; r++)
-                    ah[m][r] = al[m][r] = 0.0f;
+                    a0[m][r] = a1[m][r] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {  // word pairs (2j, 2j+1): 2 * CPW dwords of x pairs
+            for (int j = 0; j < 4; j++) {  // word pairs (2j, 2j+1)
 #pragma unroll
                 for (int m = 0; m < M; m++) {
-                    const uint4 *xq = reinterpret_cast<const uint4 *>(xb + m * pn * F::LDS_STRIDE +
-                                                                      j * 2 * F::CPW);
-                    uint32_t xv[2 * F::CPW];
+                    const float4 *xq = reinterpret_cast<const float4 *>(xb + m * pn * F::LDS_STRIDE +
+                                                                        j * 2 * F::CPW);
+                    float xv[2 * F::CPW];
 #pragma unroll
                     for (int c = 0; c < 2 * F::CPW / 4; c++) {
-                        const uint4 t = xq[c];
+                        const float4 t = xq[c];
                         xv[4 * c + 0] = t.x;
                         xv[4 * c + 1] = t.y;
                         xv[4 * c + 2] = t.z;
@@ -350,20 +396,28 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
                     }
 #pragma unroll
                     for (int r = 0; r < R; r++) {
-                        word_dot<TYPE>(block_word(it_buf.blk[r], 2 * j), xv, ah[m][r], al[m][r]);
-                        word_dot<TYPE>(block_word(it_buf.blk[r], 2 * j + 1), xv + F::CPW, ah[m][r],
-                                       al[m][r]);
+                        if (r < live) {
+                            const uint32_t w0 = block_word(it_buf.blk[r], 2 * j);
+                            const uint32_t w1 = block_word(it_buf.blk[r], 2 * j + 1);
+                            if (TYPE == PN_TYPE_PN4T) {
+                                word_fp8(w0, xv, a0[m][r], a1[m][r]);
+                                word_fp8(w1, xv + F::CPW, a0[m][r], a1[m][r]);
+                            } else {
+                                word_mix(w0, xv, a0[m][r], a1[m][r]);
+                                word_mix(w1, xv + F::CPW, a0[m][r], a1[m][r]);
+                            }
+                        }
                     }
                 }
             }
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                const float2 ss = *reinterpret_cast<const float2 *>(xb + m * pn * F::LDS_STRIDE + F::G);
+                const float sx = xb[m * pn * F::LDS_STRIDE + F::G];
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     const float d = valid ? f16_bits_to_f32(block_d_bits(it_buf.blk[r])) : 0.0f;
-                    const float t = __builtin_fmaf(-(float)F::Z, ss.x, ah[m][r] + al[m][r]);
-                    acc[m][r] = __builtin_fmaf(d * ss.y, t, acc[m][r]);
+                    acc[m][r] = __builtin_fmaf(d, __builtin_fmaf(-(float)F::Z, sx, a0[m][r] + a1[m][r]),
+                                               acc[m][r]);
                 }
             }
             if (i == iters - 1) {  // the group's rows are complete: reduce and store
@@ -416,11 +470,36 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
     }
 }
 
-// ---- short rows: x in registers -----------------------------------------------------------------
-// For rows of at most 64 blocks (K <= 5120 for pn3t, 4096 for pn4t) lane l always owns block l, so
-// its staged x (M x G/2 hi/lo pairs, the block sum and scale) stays in registers: no LDS, no
-// barrier. A wave streams its rows one at a time through a ring of D row buffers (D - 1 rows of
-// loads in flight), and reduces 4 / M rows at once with the transposed reduction.
+// ---- short rows: staged x in registers ----------------------------------------------------------
+
+// fp16 hi/lo pair of two staged values. hi is x' with its fp32 significand cut to fp16 width
+// (exactly an fp16 value in fp16's normal range; below it, 0); lo = x' - hi is exact in fp32 and
+// is converted with truncation. Relative error of hi + lo: below 2^-20 for |x'| >= 2^-14.
+__device__ __forceinline__ void split_pair(float a, float b, float &hi, float &lo)
+{
+    const float ha = (__builtin_fabsf(a) >= 0x1p-14f)
+                         ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u)
+                         : 0.0f;
+    const float hb = (__builtin_fabsf(b) >= 0x1p-14f)
+                         ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) & 0xFFFFE000u)
+                         : 0.0f;
+    hi = __builtin_bit_cast(float, __builtin_amdgcn_cvt_pkrtz(ha, hb));
+    lo = __builtin_bit_cast(float, __builtin_amdgcn_cvt_pkrtz(a - ha, b - hb));
+}
+
+// Scale exponent of a block: s such that max_e |x_e| * 2^(24 - p_e - s) lies in [2^14, 2^15).
+__device__ __forceinline__ int block_shift(float amax_scaled)
+{
+    if (!(amax_scaled > 0.0f) || !(amax_scaled < __builtin_inff()))
+        return 0;  // all zero, or non-finite input (the result is then non-finite too)
+    return __builtin_amdgcn_frexp_expf(amax_scaled) - 15;
+}
+
+// Rows of at most 64 blocks (K <= 5120 for pn3t, 4096 for pn4t): lane l always owns block l, so
+// its staged x stays in registers: no LDS, no barrier. pn3t keeps fp16 hi/lo pairs (dot2 decode);
+// pn4t keeps fp32 * 2^9 in slot order (fp8-conversion decode). A wave streams its rows one at a
+// time through a ring of D row buffers (D - 1 rows of loads in flight) and reduces 4 / M rows at
+// once with the transposed reduction.
 template <int TYPE, int M, int D>
 __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
@@ -431,10 +510,10 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     constexpr int RPR = 4 / M;  // rows per reduction
     static_assert(D % RPR == 0, "ring size must be a multiple of the rows per reduction");
     const int nwaves = blockDim.x >> 6, lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t r_begin;
     int nrows;
-    wave_rows(N, (int64_t)gridDim.x * nwaves, (int64_t)blockIdx.x * nwaves + wave, r_begin, nrows);
+    wave_rows(N, wave, nwaves, r_begin, nrows);
     const bool active = lane < nb;
     const int b = min(lane, nb - 1);
     const uint8_t *wbase = W + r_begin * row_bytes + (int64_t)kBlockBytes * b;
@@ -447,37 +526,86 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     for (int p = 0; p < D - 1; p++)
         load_block(wbase + (int64_t)min(p, last) * row_bytes, buf[p]);
 
-    uint32_t xq[M][F::G];  // (hi, lo) pair dwords of the lane's block
+    // Cooperative staging: 8 lanes per block (one word of x each), the block's amax and sum by a
+    // DPP butterfly over the 8 lanes; the staged words go to LDS, then every lane lifts its own
+    // block into registers.
+    __shared__ float4 stage4[M * 64 * F::LDS_STRIDE / 4];
+    float *stage = reinterpret_cast<float *>(stage4);
+    for (int u = threadIdx.x; u < M * 64 * 8; u += blockDim.x) {  // blockDim is a multiple of 64
+        const int m = u >> 9, bb = (u >> 3) & 63, i = u & 7;
+        const bool have = bb < nb;
+        const float *src = x + (int64_t)m * K + (int64_t)min(bb, nb - 1) * F::G + i * F::CPW;
+        float v[F::CPW];
+#pragma unroll
+        for (int t = 0; t < F::CPW; t += 2) {
+            const float2 p = x_vec4 ? *reinterpret_cast<const float2 *>(src + t)
+                                    : make_float2(src[t], src[t + 1]);
+            v[t] = have ? p.x : 0.0f;
+            v[t + 1] = have ? p.y : 0.0f;
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < F::CPW; t++)
+            sum += v[t];
+        sum += PN_DPP(sum, 0xB1);   // lanes xor 1
+        sum += PN_DPP(sum, 0x4E);   // lanes xor 2
+        sum += PN_DPP(sum, 0x141);  // the mirror half of the 8-lane group
+        float *blk = stage + (m * 64 + bb) * F::LDS_STRIDE;
+        if (TYPE == PN_TYPE_PN3T) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int t = 0; t < F::CPW; t++)
+                amax = fmaxf(amax, __builtin_fabsf(v[t]) * stage_factor<PN_TYPE_PN3T>(t));
+            amax = fmaxf(amax, PN_DPP(amax, 0xB1));
+            amax = fmaxf(amax, PN_DPP(amax, 0x4E));
+            amax = fmaxf(amax, PN_DPP(amax, 0x141));
+            const int sh = block_shift(amax);
+            const float down = __builtin_ldexpf(1.0f, -sh);
+            float4 o[3];
+            float *of = reinterpret_cast<float *>(o);
+#pragma unroll
+            for (int t = 0; t < F::CPW; t += 2) {
+                const float f = stage_factor<PN_TYPE_PN3T>(t) * down;
+                split_pair(v[t] * f, v[t + 1] * f, of[t], of[t + 1]);
+            }
+            float *dst = blk + i * F::CPW;  // 10 dwords at an 8-byte aligned offset
+#pragma unroll
+            for (int t = 0; t < F::CPW; t += 2)
+                *reinterpret_cast<float2 *>(dst + t) = make_float2(of[t], of[t + 1]);
+            if (i == 0)
+                *reinterpret_cast<float2 *>(blk + F::G) =
+                    make_float2(sum * down, __builtin_ldexpf(1.0f, sh));
+        } else {
+            float4 o[2];
+            float *of = reinterpret_cast<float *>(o);
+#pragma unroll
+            for (int t = 0; t < F::CPW; t++)
+                of[pn4t_slot(t)] = v[t] * 512.0f;
+            float4 *dst = reinterpret_cast<float4 *>(blk + i * F::CPW);
+            dst[0] = o[0];
+            dst[1] = o[1];
+            if (i == 0)
+                *reinterpret_cast<float2 *>(blk + F::G) = make_float2(sum, 1.0f);
+        }
+    }
+    __syncthreads();
+
+    float xq[M][F::G];  // pn3t: (hi, lo) fp16 pair dwords; pn4t: fp32 * 2^9 in slot order
     float sxs[M], scl[M];
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float *src = x + (int64_t)m * K + (int64_t)b * F::G;
-        float xv[F::G];
+        const float4 *blk = reinterpret_cast<const float4 *>(stage + (m * 64 + lane) * F::LDS_STRIDE);
 #pragma unroll
         for (int c = 0; c < F::G / 4; c++) {
-            const float4 v = x_vec4 ? reinterpret_cast<const float4 *>(src)[c]
-                                    : make_float4(src[4 * c], src[4 * c + 1], src[4 * c + 2],
-                                                  src[4 * c + 3]);
-            xv[4 * c + 0] = v.x;
-            xv[4 * c + 1] = v.y;
-            xv[4 * c + 2] = v.z;
-            xv[4 * c + 3] = v.w;
+            const float4 t = blk[c];
+            xq[m][4 * c + 0] = t.x;
+            xq[m][4 * c + 1] = t.y;
+            xq[m][4 * c + 2] = t.z;
+            xq[m][4 * c + 3] = t.w;
         }
-        float sum = 0.0f, amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < F::G; e++) {
-            sum += xv[e];
-            amax = fmaxf(amax, __builtin_ldexpf(__builtin_fabsf(xv[e]), 24 - code_pos<TYPE>(e % F::CPW)));
-        }
-        const int s = block_shift(amax);
-#pragma unroll
-        for (int e = 0; e < F::G; e += 2) {
-            const int sh = 24 - code_pos<TYPE>(e % F::CPW) - s;
-            split_pair(__builtin_ldexpf(xv[e], sh), __builtin_ldexpf(xv[e + 1], sh), xq[m][e],
-                       xq[m][e + 1]);
-        }
-        sxs[m] = __builtin_ldexpf(sum, -s);
-        scl[m] = __builtin_ldexpf(1.0f, s);
+        const float2 ss = *reinterpret_cast<const float2 *>(stage + (m * 64 + lane) * F::LDS_STRIDE + F::G);
+        sxs[m] = ss.x;
+        scl[m] = ss.y;
     }
 
     float vals[4];
@@ -495,11 +623,20 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
                 const int slot = s % RPR;
 #pragma unroll
                 for (int m = 0; m < M; m++) {
-                    float ah = 0.0f, al = 0.0f;
+                    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 8; i++)
-                        word_dot<TYPE>(block_word(buf[s], i), &xq[m][i * F::CPW], ah, al);
-                    vals[slot * M + m] = (d * scl[m]) * __builtin_fmaf(-(float)F::Z, sxs[m], ah + al);
+                    for (int i = 0; i < 8; i += 2) {
+                        const uint32_t w0 = block_word(buf[s], i), w1 = block_word(buf[s], i + 1);
+                        if (TYPE == PN_TYPE_PN3T) {
+                            word_dot2(w0, &xq[m][i * F::CPW], a0, a1);
+                            word_dot2(w1, &xq[m][(i + 1) * F::CPW], a2, a3);
+                        } else {
+                            word_fp8(w0, &xq[m][i * F::CPW], a0, a1);
+                            word_fp8(w1, &xq[m][(i + 1) * F::CPW], a2, a3);
+                        }
+                    }
+                    const float t = (a0 + a1) + (a2 + a3);
+                    vals[slot * M + m] = (d * scl[m]) * __builtin_fmaf(-(float)F::Z, sxs[m], t);
                 }
                 if (slot == RPR - 1 || it == nrows - 1) {
                     float tot[1];
@@ -519,6 +656,8 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
         }
     }
 }
+
+// ---- host side ----------------------------------------------------------------------------------
 
 constexpr int kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 
@@ -540,30 +679,18 @@ static int num_cus()
     return cus;
 }
 
-// Waves per workgroup (one workgroup per CU): the count in [4, 8] whose split of the rows over all
-// waves, in groups of R rows, has the smallest largest-range / mean ratio (the largest count wins
-// ties). PN_GEMV_WAVES overrides it.
+// Waves per workgroup (one workgroup per CU): 8 (two per SIMD, so one wave's memory waits overlap
+// the other's arithmetic) unless the rows are too few to give every wave a group of R. Rows are
+// split per SIMD (see wave_rows), so either count keeps the SIMDs balanced. PN_GEMV_WAVES (4 or 8)
+// overrides it.
 static LaunchCfg choose_cfg(int64_t N, int R)
 {
     const int cus = num_cus();
     LaunchCfg c{8, cus};
-    if (const char *e = getenv("PN_GEMV_WAVES")) {
-        c.waves = atoi(e);
-    } else {
-        double best = 1e30;
-        for (int w = 8; w >= 4; w--) {
-            const int64_t T = (int64_t)cus * w;
-            const double mean = (double)N / T;
-            const int64_t most = (N + T - 1) / T;
-            const double worst = (double)(((most + R - 1) / R) * R);
-            const double ratio = worst / (mean > 0 ? mean : 1);
-            if (ratio < best - 1e-9) {
-                best = ratio;
-                c.waves = w;
-            }
-        }
-    }
-    c.waves = c.waves < 1 ? 1 : (c.waves > 8 ? 8 : c.waves);
+    if (const char *e = getenv("PN_GEMV_WAVES"))
+        c.waves = atoi(e) <= 4 ? 4 : 8;
+    else if (N < (int64_t)cus * 8 * R)
+        c.waves = 4;
     return c;
 }
 
@@ -585,8 +712,7 @@ static int launch_lds(const uint8_t *W, int64_t N, int64_t K, const float *x, fl
         attr_set = true;
     }
     const LaunchCfg c = choose_cfg(N, R);
-    const int64_t T = (int64_t)c.grid * c.waves;
-    const int grid = (int)(N < T ? (N + c.waves - 1) / c.waves : c.grid);
+    const int grid = (int)std::min<int64_t>(c.grid, (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * c.waves), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, y, phase_nb, vec4);
@@ -600,12 +726,19 @@ static int launch_xreg(const uint8_t *W, int64_t N, int64_t K, const float *x, f
     using F = Fmt<TYPE>;
     const int nb = (int)(K / F::G);
     const LaunchCfg c = choose_cfg(N, 1);
-    const int64_t T = (int64_t)c.grid * c.waves;
-    const int grid = (int)(N < T ? (N + c.waves - 1) / c.waves : c.grid);
+    const int grid = (int)std::min<int64_t>(c.grid, (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
     hipLaunchKernelGGL((pn_gemv_xreg_kernel<TYPE, M, D>), dim3((unsigned)grid), dim3(64 * c.waves),
                        0, s, W, N, nb, (int64_t)nb * kBlockBytes, x, K, y, vec4);
     return launch_status();
+}
+
+// Rows in flight per wave in the short-row kernel at M = 1 (ring size 4 or 8); PN_GEMV_DEPTH
+// overrides the default.
+static int ring_depth()
+{
+    const char *e = getenv("PN_GEMV_DEPTH");
+    return (e && atoi(e) >= 8) ? 8 : 4;
 }
 
 template <int TYPE>
@@ -615,8 +748,10 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
     const bool short_rows = K / Fmt<TYPE>::G <= 64 && !getenv("PN_GEMV_NO_XREG");
     switch (M) {
     case 1:
-        return short_rows ? launch_xreg<TYPE, 1, 8>(W, N, K, x, y, s)
-                          : launch_lds<TYPE, 1, 2, 4>(W, N, K, x, y, s);
+        if (short_rows)
+            return ring_depth() == 8 ? launch_xreg<TYPE, 1, 8>(W, N, K, x, y, s)
+                                     : launch_xreg<TYPE, 1, 4>(W, N, K, x, y, s);
+        return launch_lds<TYPE, 1, 2, 4>(W, N, K, x, y, s);
     case 2:
         return short_rows ? launch_xreg<TYPE, 2, 2>(W, N, K, x, y, s)
                           : launch_lds<TYPE, 2, 2, 2>(W, N, K, x, y, s);
