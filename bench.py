@@ -2,10 +2,12 @@
 """Bench: PN decode-step GEMV weight-GB/s on one MI355X.
 
 Workload (one step): one Qwen3.8-27B-shaped MLP at M = 1 token -- gate and up as pn3t 17408 x 5120,
-down as pn4t 5120 x 17408 -- three pn_gemv calls. Weights: seeded N(0, 0.02) fp32 quantized on the
-GPU by the reference quantizer (pn_quantize_rows); x ~ N(0, 1) fp32. Five distinct device copies of
-the weight set (615.5 MB, above the 256 MB Infinity Cache) are used round-robin, so every step reads
-its weights from HBM. value = weight bytes per step / time per step.
+down as pn4t 5120 x 17408. Gate and up read the same x, so they are stored stacked by rows as one
+pn3t 34816 x 5120 matrix and run as one pn_gemv call (the usual fused gate/up projection); down is a
+second call: two launches per step. Weights: seeded N(0, 0.02) fp32 quantized on the GPU by the
+reference quantizer (pn_quantize_rows); x ~ N(0, 1) fp32. Five distinct device copies of the weight
+set (615.5 MB, above the 256 MB Infinity Cache) are used round-robin, so every step reads its
+weights from HBM. value = weight bytes per step / time per step.
 
 Prints one JSON line (rank 0). See --help for the knobs.
 """
@@ -24,9 +26,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "PN GEMV weight GB/s at M=1 (% of MI355X HBM peak), K=5120/17408"
 
-# (name, type, N, K, weight seed, x seed)
-MLP = [("gate", 124, 17408, 5120, 301, 304), ("up", 124, 17408, 5120, 302, 304),
-       ("down", 125, 5120, 17408, 303, 305)]
+# (name, type, [(rows, weight seed), ...] stacked by rows, K, x seed)
+MLP = [("gate_up", 124, [(17408, 301), (17408, 302)], 5120, 304),
+       ("down", 125, [(5120, 303)], 17408, 305)]
 
 
 def log(*a):
@@ -38,19 +40,23 @@ def build_weights(pn, torch, dev, copies):
     import numpy as np
     import synth
     mats = []
-    for name, typ, N, K, wseed, xseed in MLP:
+    for name, typ, parts, K, xseed in MLP:
         t0 = time.time()
-        w = torch.from_numpy(synth.gaussian_weights(wseed, N, K, 0.02)).to(dev)
+        N = sum(n for n, _ in parts)
         rb = pn.row_bytes(typ, K)
         W0 = torch.empty((N, rb), dtype=torch.uint8, device=dev)
         st = torch.empty(N, dtype=torch.int32, device=dev)
-        pn.quantize_rows(typ, w, W0, st)
+        r0 = 0
+        for n, wseed in parts:
+            w = torch.from_numpy(synth.gaussian_weights(wseed, n, K, 0.02)).to(dev)
+            pn.quantize_rows(typ, w, W0[r0:r0 + n], st[r0:r0 + n])
+            del w
+            r0 += n
         ver = torch.empty(N, dtype=torch.int32, device=dev)
         pn.validate_rows(typ, W0, N, K, ver)
         torch.cuda.synchronize()
         if int(st.abs().sum()) != 0 or int(ver.sum()) != N:
             raise RuntimeError(f"{name}: quantizer status / validation failed")
-        del w
         Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
         x = torch.from_numpy(np.ascontiguousarray(synth.activations(xseed, 1, K))).to(dev)
         y = torch.empty((1, N), dtype=torch.float32, device=dev)
@@ -68,11 +74,12 @@ def cpu_baseline(seconds: float):
     import synth
     threads = max(1, min(16, os.cpu_count() or 1))
     samples = []
-    for name, typ, N, K, wseed, xseed in MLP:
-        n = N // 16
-        w = synth.gaussian_weights(wseed, N, K, 0.02)[:n]
-        W, _ = oracle.quantize_rows(typ, w, threads=threads)
-        samples.append((typ, n, K, W, synth.activations(xseed, 1, K), W.nbytes))
+    for name, typ, parts, K, xseed in MLP:
+        for N, wseed in parts:
+            n = N // 16
+            w = synth.gaussian_weights(wseed, N, K, 0.02)[:n]
+            W, _ = oracle.quantize_rows(typ, w, threads=threads)
+            samples.append((typ, n, K, W, synth.activations(xseed, 1, K), W.nbytes))
     total_bytes, reps, t0 = 0, 0, time.perf_counter()
     while True:
         for typ, n, K, W, x, nbytes in samples:
@@ -84,7 +91,7 @@ def cpu_baseline(seconds: float):
             break
     return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"rows 0..N/16 of gate, up, down (M=1), {reps} passes, {el:.1f} s, "
+            "sample": f"rows 0..N/16 of each of gate, up, down (M=1), {reps} passes, {el:.1f} s, "
                       f"fp64 accumulation, {threads} host threads"}
 
 
@@ -168,7 +175,7 @@ def main():
         kern[m["name"]] = dict(avg_us=round(us, 3), weight_GBs=round(m["bytes"] / us / 1e3, 1),
                                avg_us_event_pair=round(us_pair, 3), bytes=m["bytes"])
     # dominant kernel: the largest share of the step's kernel time, per kernel kind
-    kinds = {"pn3t_17408x5120": ["gate", "up"], "pn4t_5120x17408": ["down"]}
+    kinds = {"pn3t_34816x5120": ["gate_up"], "pn4t_5120x17408": ["down"]}
     tot = {k: sum(kern[n]["avg_us"] for n in v) for k, v in kinds.items()}
     dom = max(tot, key=tot.get)
     dnames = kinds[dom]
@@ -190,8 +197,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Qwen3.8-27B-shaped MLP at M=1: gate+up pn3t 17408x5120, "
-                               "down pn4t 5120x17408 (3 pn_gemv launches per step)",
+        "config": {"workload": "Qwen3.8-27B-shaped MLP at M=1: gate and up pn3t 17408x5120 each, "
+                               "stacked as one 34816x5120 launch, down pn4t 5120x17408 "
+                               "(2 pn_gemv launches per step)",
                    "weight_bytes_per_step": step_bytes, "rotated_copies": args.copies,
                    "working_set_MB": round(step_bytes * args.copies / 1e6, 1),
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},

@@ -288,20 +288,35 @@ struct Item {
 // Row range of a wave. The rows are split into balanced contiguous ranges over the SIMD slots
 // (4 per workgroup: a CU's SIMDs, which take the workgroup's waves round-robin), and each slot's
 // range over the waves that share that SIMD (wave w and w + 4 of an 8-wave group). Every SIMD thus
-// gets the same number of rows, +-1, whichever wave count divides it.
-__device__ __forceinline__ void wave_rows(int64_t N, int wave, int nwaves, int64_t &begin, int &count)
+// gets the same number of rows, +-1, whichever wave count divides it. The instruction arbiter
+// favours the older wave of a SIMD, so it may be given the larger part (fnum/16). The quotient
+// and remainder of N by the slot count come from the host (rq, rr): no division runs on the
+// device.
+struct RowSplit {
+    int64_t rq;  // N / (gridDim.x * 4)
+    int rr;      // N % (gridDim.x * 4)
+};
+
+__device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int nwaves, int fnum,
+                                          int64_t &begin, int &count)
 {
-    const int per_simd = nwaves >> 2;  // 1 or 2
-    const int64_t S = (int64_t)gridDim.x * 4;
-    const int64_t slot = (int64_t)blockIdx.x * 4 + (wave & 3);
+    const int slot = blockIdx.x * 4 + (wave & 3);
     const int h = wave >> 2;
-    const int64_t s0 = slot * N / S;
-    const int64_t cnt = (slot + 1) * N / S - s0;
-    const int64_t b0 = (h * cnt + per_simd - 1) / per_simd;
-    const int64_t b1 = ((h + 1) * cnt + per_simd - 1) / per_simd;
+    const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
+    const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
+    // two waves per SIMD: the older one (h = 0) takes the first fnum/16 of the slot's rows
+    const int64_t mid = nwaves == 8 ? (cnt * fnum + 8) >> 4 : cnt;
+    const int64_t b0 = h ? mid : 0;
+    const int64_t b1 = h ? cnt : mid;
     count = (int)(b1 - b0);
     // an empty range may start at N; its (unused, clamped) prefetch must still address a real row
     begin = min(s0 + b0, N - 1);
+}
+
+static RowSplit row_split(int64_t N, int grid)
+{
+    const int64_t S = (int64_t)grid * 4;
+    return RowSplit{N / S, (int)(N % S)};
 }
 
 // General kernel, fp32 x staged in LDS. A wave walks its rows R at a time; for each group, lane l
@@ -313,8 +328,8 @@ template <int TYPE, int M, int R, int D>
 __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                        int nb, int64_t row_bytes,
                                                        const float *__restrict__ x, int64_t K,
-                                                       float *__restrict__ y, int phase_nb,
-                                                       int x_vec4)
+                                                       float *__restrict__ y, RowSplit sp,
+                                                       int phase_nb, int x_vec4, int fnum)
 {
     using F = Fmt<TYPE>;
     constexpr int V = ((M * R + 3) / 4) * 4;
@@ -324,7 +339,7 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     int64_t r_begin;
     int nrows;
-    wave_rows(N, wave, nwaves, r_begin, nrows);
+    wave_rows(N, sp, wave, nwaves, fnum, r_begin, nrows);
     const int ngroups = (nrows + R - 1) / R;
     const uint8_t *wbase = W + r_begin * row_bytes;
 
@@ -470,7 +485,7 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
     }
 }
 
-// ---- short rows: staged x in registers ----------------------------------------------------------
+// ---- x as fp16 hi/lo pairs ------------------------------------------------------------------
 
 // fp16 hi/lo pair of two staged values. hi is x' with its fp32 significand cut to fp16 width
 // (exactly an fp16 value in fp16's normal range; below it, 0); lo = x' - hi is exact in fp32 and
@@ -495,6 +510,368 @@ __device__ __forceinline__ int block_shift(float amax_scaled)
     return __builtin_amdgcn_frexp_expf(amax_scaled) - 15;
 }
 
+// ---- long rows: flat partition over (row group, block) ------------------------------------------
+
+// pn4t with x in natural k order (x * 2^9): the conversions yield the codes in the order (t0,t4),
+// (t1,t5), (t2,t6), (t3,t7), and each is paired with its own x.
+__device__ __forceinline__ void word_fp8n(uint32_t w, const float *xn, float &acc0, float &acc1)
+{
+    const uint32_t a = w & 0x0F0F0F0Fu;         // bytes: t0 t4 t1 t5
+    const uint32_t b = (w >> 4) & 0x0F0F0F0Fu;  // bytes: t2 t6 t3 t7
+    const f32x2_t c0 = __builtin_amdgcn_cvt_pk_f32_fp8(a, false);
+    const f32x2_t c1 = __builtin_amdgcn_cvt_pk_f32_fp8(a, true);
+    const f32x2_t c2 = __builtin_amdgcn_cvt_pk_f32_fp8(b, false);
+    const f32x2_t c3 = __builtin_amdgcn_cvt_pk_f32_fp8(b, true);
+    acc0 = __builtin_fmaf(c0.x, xn[0], acc0);
+    acc1 = __builtin_fmaf(c0.y, xn[4], acc1);
+    acc0 = __builtin_fmaf(c1.x, xn[1], acc0);
+    acc1 = __builtin_fmaf(c1.y, xn[5], acc1);
+    acc0 = __builtin_fmaf(c2.x, xn[2], acc0);
+    acc1 = __builtin_fmaf(c2.y, xn[6], acc1);
+    acc0 = __builtin_fmaf(c3.x, xn[3], acc0);
+    acc1 = __builtin_fmaf(c3.y, xn[7], acc1);
+}
+
+constexpr int kFlatWaves = 8;  // waves per workgroup of the flat kernel (two per SIMD)
+
+// Rows of more than 64 blocks, x fully resident in LDS (one K-phase), M = 1..2.
+//
+// Work split: the rows are taken R at a time ("groups"); a workgroup owns a balanced, contiguous
+// range of groups, and the (group, block) pairs of that range, in row-major order, are cut into
+// kFlatWaves contiguous pieces, one per wave. Each SIMD gets a quarter; the instruction arbiter
+// favours the older of the two waves on a SIMD, so that wave takes the larger part (fnum/16; 10/16
+// measured best), the younger one the rest. A wave walks its piece 64 blocks at a time
+// (lane l takes the l-th block of each "item"); since a group has at least 64 blocks an item spans
+// at most two groups, so each lane keeps two accumulator sets, for the item's first group and the
+// next one. When the walk leaves a group, the group's sums are reduced across the wave: a group
+// that lies wholly inside the piece is stored to y; the (at most two) groups at the piece's ends
+// are written to LDS and, after a barrier, summed over the waves that share them, lowest wave
+// first. Every output thus has one fixed summation order (deterministic), and only the last item
+// of a piece is partly idle.
+//
+// Staging: all x loads of the workgroup are issued before the first weight loads, so waiting for
+// x never waits for weights (the memory counter retires loads in order).
+template <int TYPE, int M, int R, int D, int QPT>
+__global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__restrict__ W, int64_t N,
+                                                            int nb, int64_t row_bytes,
+                                                            const float *__restrict__ x, int64_t K,
+                                                            float *__restrict__ y, int64_t gq,
+                                                            int gr, int x_vec4, int fnum)
+{
+    using F = Fmt<TYPE>;
+    constexpr int V = ((M * R + 3) / 4) * 4;
+    constexpr int QB = F::G / 4;  // 16-byte pieces of x per block
+    extern __shared__ float4 lds4[];
+    float *lds = reinterpret_cast<float *>(lds4);  // staged x: [M][nb][LDS_STRIDE]
+    float *part = lds + M * nb * F::LDS_STRIDE;    // partial sums: [kFlatWaves][2][V]
+    int *meta = reinterpret_cast<int *>(part + kFlatWaves * 2 * V);  // [kFlatWaves][4]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // this workgroup's groups [P0, P1) and this wave's piece [F0, F1) of its (group, block) pairs
+    // (gq, gr: quotient and remainder of the group count by the grid, from the host)
+    const int blk = blockIdx.x;
+    const int64_t P0 = (int64_t)blk * gq + min(blk, gr);
+    const int T = (int)(gq + (blk < gr ? 1 : 0)) * nb;  // < 2^30 (checked on the host)
+    // SIMD j = wave & 3 takes the quarter [q0, q1) of the range; its older wave (h = 0) the first
+    // fnum/16 of it, the younger wave (h = 1) the rest.
+    const int sj = wave & 3, sh = wave >> 2;
+    const int q0 = (int)(((int64_t)sj * T) >> 2), q1 = (int)(((int64_t)(sj + 1) * T) >> 2);
+    const int qm = q0 + (int)(((int64_t)(q1 - q0) * fnum) >> 4);
+    const int F0 = sh ? qm : q0;
+    const int F1 = sh ? q1 : qm;
+    const int L = F1 - F0;
+    const int nitems = (L + 63) >> 6;
+    const int pf = (int)((uint32_t)F0 / (uint32_t)nb);  // first group of the piece (relative to P0)
+    const int pl = L > 0 ? (int)((uint32_t)(F1 - 1) / (uint32_t)nb) : pf;  // last group
+    const int be = L > 0 ? (F1 - 1) - pl * nb : 0;  // block of the piece's last pair
+
+    // 1. x loads: nq = ceil(total / 512) per thread (at most QPT), under a uniform branch so that
+    // no load is issued past the last round. The weight loads issued next are unconditional, so
+    // waiting for x never waits for them.
+    const int per_tok = nb * QB;
+    const int total = M * per_tok;
+    const int nq = (total + kFlatWaves * 64 - 1) / (kFlatWaves * 64);
+    // Each workgroup walks x from its own starting block (rotated by the workgroup index) so that
+    // the CUs of an XCD do not all request the same lines of x, i.e. the same L2 channel, at once.
+    const int rot = (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB;
+    auto rotq = [&](int q) { q += rot; return q >= total ? q - total : q; };
+    auto token_of = [](int q, int per) {  // q / per for q < M * per, without a division
+        int m = 0;
+#pragma unroll
+        for (int i = 1; i < M; i++)
+            m += q >= i * per ? 1 : 0;
+        return m;
+    };
+    float4 xv[QPT];
+#pragma unroll
+    for (int u = 0; u < QPT; u++) {
+        if (u < nq) {
+            const int q = rotq(min((int)threadIdx.x + u * kFlatWaves * 64, total - 1));
+            const int m = token_of(q, per_tok);
+            const float *src = x + (int64_t)m * K + 4 * (q - m * per_tok);
+            xv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
+                           : make_float4(src[0], src[1], src[2], src[3]);
+        }
+    }
+
+    // 2. first weight loads. Item positions come from uniform cursors (group, block of the item's
+    // first pair); a lane past the piece's end re-reads the piece's last pair (the result is
+    // unused), and item indices past the last item are clamped, so no load is ever inside a
+    // branch and no load leaves the matrix.
+    auto load_item = [&](Item<R> &buf, int itc, int pu, int bu) {
+        int b = bu + lane, p = pu;
+        if (b >= nb) {
+            b -= nb;
+            p += 1;
+        }
+        if (64 * itc + lane >= L) {
+            p = pl;
+            b = be;
+        }
+        const int64_t row0 = R * (P0 + p);
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t row = min(row0 + r, N - 1);
+            load_block(W + row * row_bytes + (int64_t)kBlockBytes * b, buf.blk[r]);
+        }
+    };
+    int lp = pf, lb = F0 - pf * nb, lit = 0;  // load cursor, at item lit
+    auto load_next = [&](Item<R> &buf, int it) {
+        const int itc = min(it, max(nitems - 1, 0));
+        if (lit < itc) {  // uniform; advances by at most one item per call
+            lb += 64;
+            if (lb >= nb) {
+                lb -= nb;
+                lp += 1;
+            }
+            lit += 1;
+        }
+        load_item(buf, itc, lp, lb);
+    };
+    Item<R> buf[D];
+#pragma unroll
+    for (int p = 0; p < D - 1; p++)
+        load_next(buf[p], p);
+
+    // 3. stage x: pn4t x * 2^9 in k order, the block's plain sum at offset G (a DPP row of 16
+    // lanes holds one block); pn3t x * 2^(24-p), sums in a second pass.
+#pragma unroll
+    for (int u = 0; u < QPT; u++) {
+        const int q0 = (int)threadIdx.x + u * kFlatWaves * 64;
+        if (u < nq && q0 < total) {  // pn4t: whole DPP rows are in or out (total and row bases are multiples of 16)
+            const int q = rotq(q0);  // a whole-block rotation keeps each DPP row on one block
+            const int m = token_of(q, per_tok);
+            const int c = q - m * per_tok;
+            const int b = c / QB, e = 4 * (c - b * QB);
+            float *blk = lds + (m * nb + b) * F::LDS_STRIDE;
+            const float4 v = xv[u];
+            if (TYPE == PN_TYPE_PN4T) {
+                *reinterpret_cast<float4 *>(blk + e) =
+                    make_float4(v.x * 512.0f, v.y * 512.0f, v.z * 512.0f, v.w * 512.0f);
+                float s = ((v.x + v.y) + v.z) + v.w;
+                s += PN_DPP(s, 0xB1);
+                s += PN_DPP(s, 0x4E);
+                s += PN_DPP(s, 0x141);
+                s += PN_DPP(s, 0x140);
+                if (e == 0)
+                    blk[F::G] = s;
+            } else {
+                *reinterpret_cast<float4 *>(blk + e) =
+                    make_float4(v.x * stage_factor<TYPE>((e + 0) % F::CPW),
+                                v.y * stage_factor<TYPE>((e + 1) % F::CPW),
+                                v.z * stage_factor<TYPE>((e + 2) % F::CPW),
+                                v.w * stage_factor<TYPE>((e + 3) % F::CPW));
+            }
+        }
+    }
+    if (lane == 0) {
+        meta[wave * 4 + 0] = F0;
+        meta[wave * 4 + 1] = F1;
+        meta[wave * 4 + 2] = pf;
+        meta[wave * 4 + 3] = pl;
+    }
+    __syncthreads();
+    if (TYPE == PN_TYPE_PN3T) {
+        stage_block_sums<TYPE, M>(lds, nb);
+        __syncthreads();
+    }
+
+    // 4. stream the piece
+    float accA[M][R], accB[M][R];
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            accA[m][r] = accB[m][r] = 0.0f;
+    int pc = pf, bc = F0 - pf * nb;  // compute cursor
+
+    auto flush = [&](int p) {  // group p is done in this wave: reduce accA and store it
+        float v[V], tot[V / 4];
+#pragma unroll
+        for (int o = 0; o < V; o++)
+            v[o] = (o < M * R) ? accA[(o < M * R ? o : 0) / R][o % R] : 0.0f;
+        transpose_reduce<V>(v, tot);
+        const bool complete = F0 <= p * nb && (p + 1) * nb <= F1;
+        if ((lane & 15) == 0) {
+            const int q = lane >> 4;
+#pragma unroll
+            for (int t = 0; t < V / 4; t++) {
+                const int o = t + q * (V / 4);
+                if (o < M * R) {
+                    const int m = o / R, r = o - m * R;
+                    if (complete) {
+                        const int64_t row = R * (P0 + p) + r;
+                        if (row < N)
+                            y[(int64_t)m * N + row] = tot[t];
+                    } else {
+                        part[(wave * 2 + (p == pf ? 0 : 1)) * V + o] = tot[t];
+                    }
+                }
+            }
+        }
+    };
+
+    auto compute_item = [&](const Item<R> &it_buf, int it) {
+        int b = bc + lane;
+        const bool second = b >= nb;
+        if (second)
+            b -= nb;
+        const bool valid = 64 * it + lane < L;
+        const float *xb = lds + (valid ? b : 0) * F::LDS_STRIDE;
+        float a0[M][R], a1[M][R], a2[M][R], a3[M][R];  // four chains per output
+#pragma unroll
+        for (int m = 0; m < M; m++)
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                a0[m][r] = a1[m][r] = a2[m][r] = a3[m][r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {  // word pairs (2j, 2j+1)
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float4 *xq = reinterpret_cast<const float4 *>(xb + m * nb * F::LDS_STRIDE +
+                                                                    j * 2 * F::CPW);
+                float xw[2 * F::CPW];
+#pragma unroll
+                for (int c = 0; c < 2 * F::CPW / 4; c++) {
+                    const float4 t = xq[c];
+                    xw[4 * c + 0] = t.x;
+                    xw[4 * c + 1] = t.y;
+                    xw[4 * c + 2] = t.z;
+                    xw[4 * c + 3] = t.w;
+                }
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const uint32_t w0 = block_word(it_buf.blk[r], 2 * j);
+                    const uint32_t w1 = block_word(it_buf.blk[r], 2 * j + 1);
+                    if (TYPE == PN_TYPE_PN4T) {
+                        word_fp8n(w0, xw, a0[m][r], a1[m][r]);
+                        word_fp8n(w1, xw + F::CPW, a2[m][r], a3[m][r]);
+                    } else {
+                        word_mix(w0, xw, a0[m][r], a1[m][r]);
+                        word_mix(w1, xw + F::CPW, a2[m][r], a3[m][r]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float sx = xb[m * nb * F::LDS_STRIDE + F::G];  // the block's plain sum of x
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                // d is selected, not multiplied by a mask, so a non-finite d stays in its own row
+                const float d = f16_bits_to_f32(block_d_bits(it_buf.blk[r]));
+                const float dA = (valid && !second) ? d : 0.0f;
+                const float dB = (valid && second) ? d : 0.0f;
+                const float t = __builtin_fmaf(-(float)F::Z, sx, (a0[m][r] + a1[m][r]) + (a2[m][r] + a3[m][r]));
+                accA[m][r] = __builtin_fmaf(dA, t, accA[m][r]);
+                accB[m][r] = __builtin_fmaf(dB, t, accB[m][r]);
+            }
+        }
+        bc += 64;  // advance the compute cursor; leaving group pc completes it
+        if (bc >= nb) {
+            bc -= nb;
+            flush(pc);
+#pragma unroll
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    accA[m][r] = accB[m][r];
+                    accB[m][r] = 0.0f;
+                }
+            pc += 1;
+        }
+    };
+
+    if constexpr (D == 2) {
+        for (int it = 0; it < nitems; it += 2) {
+            load_next(buf[1], it + 1);
+            compute_item(buf[0], it);
+            if (it + 1 >= nitems)
+                break;
+            load_next(buf[0], it + 2);
+            compute_item(buf[1], it + 1);
+        }
+    } else {
+        for (int it0 = 0; it0 < nitems; it0 += D) {
+#pragma unroll
+            for (int s = 0; s < D; s++) {
+                const int it = it0 + s;
+                load_next(buf[(s + D - 1) % D], it + D - 1);
+                if (it < nitems)
+                    compute_item(buf[s], it);
+            }
+        }
+    }
+    if (nitems > 0 && pc <= pl)
+        flush(pc);
+    __syncthreads();
+
+    // 5. groups shared by several waves: the lowest wave that touches one sums the partials of
+    // every wave that touches it, in wave order. meta[w] = (F0, F1, first group, last group).
+    if (threadIdx.x < 2 * kFlatWaves) {
+        const int w = threadIdx.x >> 1, s = threadIdx.x & 1;
+        const int4 *m4 = reinterpret_cast<const int4 *>(meta);
+        int4 mm[kFlatWaves];
+#pragma unroll
+        for (int w2 = 0; w2 < kFlatWaves; w2++)
+            mm[w2] = m4[w2];
+        const int4 me = m4[w];
+        const int p = s ? me.w : me.z;
+        auto touches = [&](const int4 &q) { return q.y > q.x && q.z <= p && p <= q.w; };
+        bool own = me.y > me.x && !(s == 1 && me.w == me.z);
+        own = own && !(me.x <= p * nb && (p + 1) * nb <= me.y);  // complete: already stored
+#pragma unroll
+        for (int w2 = 0; w2 < kFlatWaves; w2++)
+            if (w2 < w && touches(mm[w2]))
+                own = false;
+        if (own) {
+            float tot[M * R];
+#pragma unroll
+            for (int o = 0; o < M * R; o++)
+                tot[o] = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < kFlatWaves; w2++) {
+                if (w2 >= w && touches(mm[w2])) {
+                    const float *src = part + (w2 * 2 + (p == mm[w2].z ? 0 : 1)) * V;
+#pragma unroll
+                    for (int o = 0; o < M * R; o++)
+                        tot[o] += src[o];
+                }
+            }
+#pragma unroll
+            for (int o = 0; o < M * R; o++) {
+                const int m = o / R, r = o - m * R;
+                const int64_t row = R * (P0 + p) + r;
+                if (row < N)
+                    y[(int64_t)m * N + row] = tot[o];
+            }
+        }
+    }
+}
+
+// ---- short rows: staged x in registers ----------------------------------------------------------
+
 // Rows of at most 64 blocks (K <= 5120 for pn3t, 4096 for pn4t): lane l always owns block l, so
 // its staged x stays in registers: no LDS, no barrier. pn3t keeps fp16 hi/lo pairs (dot2 decode);
 // pn4t keeps fp32 * 2^9 in slot order (fp8-conversion decode). A wave streams its rows one at a
@@ -504,7 +881,8 @@ template <int TYPE, int M, int D>
 __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
                                                             const float *__restrict__ x, int64_t K,
-                                                            float *__restrict__ y, int x_vec4)
+                                                            float *__restrict__ y, RowSplit sp,
+                                                            int x_vec4, int fnum)
 {
     using F = Fmt<TYPE>;
     constexpr int RPR = 4 / M;  // rows per reduction
@@ -513,10 +891,29 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t r_begin;
     int nrows;
-    wave_rows(N, wave, nwaves, r_begin, nrows);
+    wave_rows(N, sp, wave, nwaves, fnum, r_begin, nrows);
     const bool active = lane < nb;
     const int b = min(lane, nb - 1);
     const uint8_t *wbase = W + r_begin * row_bytes + (int64_t)kBlockBytes * b;
+
+    // Cooperative staging, 512 threads: thread t takes word t & 7 of block t >> 3 of every token.
+    // The x loads are issued before the first weight loads, so waiting for x never waits for
+    // weights (the memory counter retires loads in order).
+    // (blocks taken in an order rotated by the workgroup index, as in the long-row kernel)
+    const int bb = ((threadIdx.x >> 3) + blockIdx.x * 5) & 63, i = threadIdx.x & 7;
+    const bool have = bb < nb;
+    float xv[M][F::CPW];
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float *src = x + (int64_t)m * K + (int64_t)min(bb, nb - 1) * F::G + i * F::CPW;
+#pragma unroll
+        for (int t = 0; t < F::CPW; t += 2) {
+            const float2 p = x_vec4 ? *reinterpret_cast<const float2 *>(src + t)
+                                    : make_float2(src[t], src[t + 1]);
+            xv[m][t] = have ? p.x : 0.0f;
+            xv[m][t + 1] = have ? p.y : 0.0f;
+        }
+    }
 
     // Loads are never inside a branch (row indices are clamped to the wave's last row; a clamped
     // load re-reads a row already requested and is unused): the wait counts then stay exact.
@@ -526,23 +923,13 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     for (int p = 0; p < D - 1; p++)
         load_block(wbase + (int64_t)min(p, last) * row_bytes, buf[p]);
 
-    // Cooperative staging: 8 lanes per block (one word of x each), the block's amax and sum by a
-    // DPP butterfly over the 8 lanes; the staged words go to LDS, then every lane lifts its own
-    // block into registers.
+    // The block's amax and sum by a DPP butterfly over its 8 lanes; the staged words go to LDS,
+    // then every lane lifts its own block into registers.
     __shared__ float4 stage4[M * 64 * F::LDS_STRIDE / 4];
     float *stage = reinterpret_cast<float *>(stage4);
-    for (int u = threadIdx.x; u < M * 64 * 8; u += blockDim.x) {  // blockDim is a multiple of 64
-        const int m = u >> 9, bb = (u >> 3) & 63, i = u & 7;
-        const bool have = bb < nb;
-        const float *src = x + (int64_t)m * K + (int64_t)min(bb, nb - 1) * F::G + i * F::CPW;
-        float v[F::CPW];
 #pragma unroll
-        for (int t = 0; t < F::CPW; t += 2) {
-            const float2 p = x_vec4 ? *reinterpret_cast<const float2 *>(src + t)
-                                    : make_float2(src[t], src[t + 1]);
-            v[t] = have ? p.x : 0.0f;
-            v[t + 1] = have ? p.y : 0.0f;
-        }
+    for (int m = 0; m < M; m++) {
+        const float *v = xv[m];
         float sum = 0.0f;
 #pragma unroll
         for (int t = 0; t < F::CPW; t++)
@@ -666,6 +1053,14 @@ struct LaunchCfg {
     int grid;   // workgroups (one per CU)
 };
 
+// Share of a SIMD's work given to the older of its two waves, in sixteenths (PN_GEMV_SPLIT).
+static int older_share(int dflt)
+{
+    const char *e = getenv("PN_GEMV_SPLIT");
+    const int v = e ? atoi(e) : dflt;
+    return v < 4 ? 4 : v > 12 ? 12 : v;
+}
+
 static int num_cus()
 {
     static int cus = 0;
@@ -715,7 +1110,7 @@ static int launch_lds(const uint8_t *W, int64_t N, int64_t K, const float *x, fl
     const int grid = (int)std::min<int64_t>(c.grid, (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * c.waves), lds, s, W, N, nb,
-                       (int64_t)nb * kBlockBytes, x, K, y, phase_nb, vec4);
+                       (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), phase_nb, vec4, 8);
     return launch_status();
 }
 
@@ -725,12 +1120,58 @@ static int launch_xreg(const uint8_t *W, int64_t N, int64_t K, const float *x, f
 {
     using F = Fmt<TYPE>;
     const int nb = (int)(K / F::G);
-    const LaunchCfg c = choose_cfg(N, 1);
-    const int grid = (int)std::min<int64_t>(c.grid, (N + 3) / 4);
+    const int grid = (int)std::min<int64_t>(num_cus(), (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
-    hipLaunchKernelGGL((pn_gemv_xreg_kernel<TYPE, M, D>), dim3((unsigned)grid), dim3(64 * c.waves),
-                       0, s, W, N, nb, (int64_t)nb * kBlockBytes, x, K, y, vec4);
+    // 512 threads: the cooperative staging gives each thread one word of one block
+    hipLaunchKernelGGL((pn_gemv_xreg_kernel<TYPE, M, D>), dim3((unsigned)grid), dim3(512), 0, s, W,
+                       N, nb, (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), vec4,
+                       older_share(8));
     return launch_status();
+}
+
+constexpr int kNotApplicable = 1;  // internal: the flat kernel does not take this shape
+
+template <int TYPE, int M, int QPT>
+static int launch_flat_q(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, float *y,
+                         int grid, int64_t NP, size_t lds, hipStream_t s)
+{
+    auto kern = pn_gemv_flat_kernel<TYPE, M, 2, 4, QPT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMaxLds) != hipSuccess)
+            return PN_ERR_HIP;
+        attr_set = true;
+    }
+    const int vec4 = aligned(x, 16) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kFlatWaves), lds, s, W, N, nb,
+                       (int64_t)nb * kBlockBytes, x, K, y, NP / grid, (int)(NP % grid), vec4,
+                       older_share(10));
+    return launch_status();
+}
+
+// The flat kernel takes rows of at least 64 blocks whose x (M tokens) fits in LDS at once and
+// whose staging needs at most 32 16-byte loads per thread; otherwise kNotApplicable.
+template <int TYPE, int M>
+static int launch_flat(const uint8_t *W, int64_t N, int64_t K, const float *x, float *y,
+                       hipStream_t s)
+{
+    using F = Fmt<TYPE>;
+    constexpr int R = 2, V = ((M * R + 3) / 4) * 4;
+    const int64_t nb = K / F::G;
+    const int64_t NP = (N + R - 1) / R;
+    const int grid = (int)std::min<int64_t>(num_cus(), NP);
+    const size_t lds = (size_t)M * nb * F::LDS_STRIDE * sizeof(float) +
+                       (size_t)kFlatWaves * 2 * V * sizeof(float) + kFlatWaves * 4 * sizeof(int);
+    const int64_t need = (M * nb * (F::G / 4) + 64 * kFlatWaves - 1) / (64 * kFlatWaves);
+    const int64_t per_wg = (NP + grid - 1) / grid;  // groups per workgroup, at most
+    if (nb < 64 || lds > (size_t)kMaxLds || need > 32 || per_wg * nb >= (int64_t(1) << 30))
+        return kNotApplicable;
+    if (need <= 8)
+        return launch_flat_q<TYPE, M, 8>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
+    if (need <= 16)
+        return launch_flat_q<TYPE, M, 16>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
+    return launch_flat_q<TYPE, M, 32>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
 }
 
 // Rows in flight per wave in the short-row kernel at M = 1 (ring size 4 or 8); PN_GEMV_DEPTH
@@ -746,15 +1187,22 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
                       hipStream_t s)
 {
     const bool short_rows = K / Fmt<TYPE>::G <= 64 && !getenv("PN_GEMV_NO_XREG");
+    const bool flat = !getenv("PN_GEMV_NO_FLAT");
+    int st;
     switch (M) {
     case 1:
         if (short_rows)
             return ring_depth() == 8 ? launch_xreg<TYPE, 1, 8>(W, N, K, x, y, s)
                                      : launch_xreg<TYPE, 1, 4>(W, N, K, x, y, s);
+        if (flat && (st = launch_flat<TYPE, 1>(W, N, K, x, y, s)) != kNotApplicable)
+            return st;
         return launch_lds<TYPE, 1, 2, 4>(W, N, K, x, y, s);
     case 2:
-        return short_rows ? launch_xreg<TYPE, 2, 2>(W, N, K, x, y, s)
-                          : launch_lds<TYPE, 2, 2, 2>(W, N, K, x, y, s);
+        if (short_rows)
+            return launch_xreg<TYPE, 2, 2>(W, N, K, x, y, s);
+        if (flat && (st = launch_flat<TYPE, 2>(W, N, K, x, y, s)) != kNotApplicable)
+            return st;
+        return launch_lds<TYPE, 2, 2, 2>(W, N, K, x, y, s);
     case 3: return launch_lds<TYPE, 3, 1, 2>(W, N, K, x, y, s);
     default: return launch_lds<TYPE, 4, 2, 2>(W, N, K, x, y, s);
     }

@@ -168,6 +168,24 @@ def test_gemv_ragged(env, typ, N, nb, M):
         assert_within(y, y_ref, bound)
 
 
+@pytest.mark.parametrize("typ,N,nb", [
+    (PN4T, 1, 65), (PN4T, 2, 100), (PN4T, 3, 272), (PN3T, 5, 70), (PN4T, 600, 65),
+    (PN3T, 515, 66), (PN4T, 1031, 130), (PN4T, 97, 301)])
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_long_rows(env, typ, N, nb, M):
+    """Rows of more than 64 blocks at 1-2 tokens: pieces of (row pair, block) that start and end
+    inside row pairs, an odd last row, fewer row pairs than workgroups and more."""
+    pn, torch, dev = env
+    G = oracle.PARAMS[typ][1]
+    K = nb * G
+    _, W = quantized(typ, N, K, 7000 + nb)
+    x = synth.activations(7100 + nb, M, K)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    for offset in (0, 2):
+        y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
+        assert_within(y, y_ref, bound)
+
+
 @pytest.mark.parametrize("typ,nb", [(PN3T, 1), (PN3T, 3), (PN4T, 129)])
 def test_decode_validate_ragged(env, typ, nb):
     pn, torch, dev = env
