@@ -24,6 +24,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), scaled by what
+# the same counters read for a plain copy of known size; valid only for the kernel sources they
+# were taken on (their hash is recorded with them).
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pn_gemv_mlp_m1_hbm_counters.txt")
+KERNEL_SOURCES = ["block_quantized_weight_pn3t_amd/csrc/pn_gemv.hip",
+                  "block_quantized_weight_pn3t_amd/csrc/pn_common.h"]
 METRIC = "PN GEMV weight GB/s at M=1 (% of MI355X HBM peak), K=5120/17408"
 
 # (name, type, [(rows, weight seed), ...] stacked by rows, K, x seed)
@@ -66,6 +72,45 @@ def build_weights(pn, torch, dev, copies):
     return mats
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of `kind` from the counter summary, or None when there is none or it
+    was taken on other kernel sources."""
+    try:
+        lines = open(COUNTERS_FILE).read().splitlines()
+    except OSError:
+        return None
+    fields = {}
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) >= 2 and parts[0] in ("source_sha256", "traffic_bytes"):
+            fields[(parts[0], parts[1] if parts[0] == "traffic_bytes" else "")] = parts[-1]
+    if fields.get(("source_sha256", "")) != kernel_source_hash():
+        return None
+    v = fields.get(("traffic_bytes", kind))
+    return int(v) if v is not None else None
+
+
+def copy_calibration(torch, dev, mb: int, reps: int = 4):
+    """Plain device copies of `mb` MiB (three rotated sources), for counter calibration: each copy
+    reads and writes exactly mb MiB."""
+    n = mb * (1 << 20) // 4
+    srcs = [torch.full((n,), float(i + 1), dtype=torch.float32, device=dev) for i in range(3)]
+    dst = torch.empty(n, dtype=torch.float32, device=dev)
+    for i in range(reps):
+        dst.copy_(srcs[i % 3])
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {mb} MiB")
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle's GEMV timed on the host cores: a bounded sample (1/16 of the rows of each MLP
     matrix, quantized by the oracle), repeated to ~`seconds` of work."""
@@ -102,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=5, help="rotated weight copies (>= 3 to exceed MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -205,10 +252,12 @@ def main():
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "kernel": f"pn_gemv {dom} (M=1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom),
                      "avg_launch_us": round(d_us, 3), "algorithmic_bytes_per_launch": d_bytes},
         "kernels": kern,
     }
+    if args.copy_mb > 0:
+        copy_calibration(torch, dev, args.copy_mb)
     if args.cpu_seconds > 0:
         log("[bench] timing the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

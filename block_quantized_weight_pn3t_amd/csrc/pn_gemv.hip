@@ -388,12 +388,17 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
             const bool valid = b < pn;
             const int live = min(R, nrows - g * R);  // rows of the group that exist (uniform)
             const float *xb = lds + min(b, pn - 1) * F::LDS_STRIDE;
-            float a0[M][R], a1[M][R];
+            // accumulator chains per output: NC = 8 (two words each) at M <= 2, 4 at M >= 3 (registers);
+            // the codes are unsigned, so a chain's rounding error scales with sum n|x|
+            constexpr int NC = M <= 2 ? 8 : 4;
+            float a[NC][M][R];
 #pragma unroll
-            for (int m = 0; m < M; m++)
+            for (int c = 0; c < NC; c++)
 #pragma unroll
-                for (int r = 0; r < R; r++)
-                    a0[m][r] = a1[m][r] = 0.0f;
+                for (int m = 0; m < M; m++)
+#pragma unroll
+                    for (int r = 0; r < R; r++)
+                        a[c][m][r] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; j++) {  // word pairs (2j, 2j+1)
 #pragma unroll
@@ -414,12 +419,13 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
                         if (r < live) {
                             const uint32_t w0 = block_word(it_buf.blk[r], 2 * j);
                             const uint32_t w1 = block_word(it_buf.blk[r], 2 * j + 1);
+                            const int c0 = (2 * j) % NC, c1 = (2 * j + 2) % NC;  // chain pairs
                             if (TYPE == PN_TYPE_PN4T) {
-                                word_fp8(w0, xv, a0[m][r], a1[m][r]);
-                                word_fp8(w1, xv + F::CPW, a0[m][r], a1[m][r]);
+                                word_fp8(w0, xv, a[c0][m][r], a[c0 + 1][m][r]);
+                                word_fp8(w1, xv + F::CPW, a[c1][m][r], a[c1 + 1][m][r]);
                             } else {
-                                word_mix(w0, xv, a0[m][r], a1[m][r]);
-                                word_mix(w1, xv + F::CPW, a0[m][r], a1[m][r]);
+                                word_mix(w0, xv, a[c0][m][r], a[c0 + 1][m][r]);
+                                word_mix(w1, xv + F::CPW, a[c1][m][r], a[c1 + 1][m][r]);
                             }
                         }
                     }
@@ -431,8 +437,11 @@ __global__ void __launch_bounds__(512) pn_gemv_kernel(const uint8_t *__restrict_
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     const float d = valid ? f16_bits_to_f32(block_d_bits(it_buf.blk[r])) : 0.0f;
-                    acc[m][r] = __builtin_fmaf(d, __builtin_fmaf(-(float)F::Z, sx, a0[m][r] + a1[m][r]),
-                                               acc[m][r]);
+                    float t = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NC; c += 2)
+                        t += a[c][m][r] + a[c + 1][m][r];
+                    acc[m][r] = __builtin_fmaf(d, __builtin_fmaf(-(float)F::Z, sx, t), acc[m][r]);
                 }
             }
             if (i == iters - 1) {  // the group's rows are complete: reduce and store
@@ -739,12 +748,16 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
             b -= nb;
         const bool valid = 64 * it + lane < L;
         const float *xb = lds + (valid ? b : 0) * F::LDS_STRIDE;
-        float a0[M][R], a1[M][R], a2[M][R], a3[M][R];  // four chains per output
+        // eight accumulator chains per output (two words each): the codes are unsigned, so a
+        // chain's rounding error scales with sum n|x|, not sum |n - z||x|
+        float a[8][M][R];
 #pragma unroll
-        for (int m = 0; m < M; m++)
+        for (int c = 0; c < 8; c++)
 #pragma unroll
-            for (int r = 0; r < R; r++)
-                a0[m][r] = a1[m][r] = a2[m][r] = a3[m][r] = 0.0f;
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int r = 0; r < R; r++)
+                    a[c][m][r] = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; j++) {  // word pairs (2j, 2j+1)
 #pragma unroll
@@ -764,12 +777,13 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
                 for (int r = 0; r < R; r++) {
                     const uint32_t w0 = block_word(it_buf.blk[r], 2 * j);
                     const uint32_t w1 = block_word(it_buf.blk[r], 2 * j + 1);
+                    const int c0 = (4 * j) % 8, c1 = (4 * j + 2) % 8;  // chain pairs of words 2j, 2j+1
                     if (TYPE == PN_TYPE_PN4T) {
-                        word_fp8n(w0, xw, a0[m][r], a1[m][r]);
-                        word_fp8n(w1, xw + F::CPW, a2[m][r], a3[m][r]);
+                        word_fp8n(w0, xw, a[c0][m][r], a[c0 + 1][m][r]);
+                        word_fp8n(w1, xw + F::CPW, a[c1][m][r], a[c1 + 1][m][r]);
                     } else {
-                        word_mix(w0, xw, a0[m][r], a1[m][r]);
-                        word_mix(w1, xw + F::CPW, a2[m][r], a3[m][r]);
+                        word_mix(w0, xw, a[c0][m][r], a[c0 + 1][m][r]);
+                        word_mix(w1, xw + F::CPW, a[c1][m][r], a[c1 + 1][m][r]);
                     }
                 }
             }
@@ -783,7 +797,9 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
                 const float d = f16_bits_to_f32(block_d_bits(it_buf.blk[r]));
                 const float dA = (valid && !second) ? d : 0.0f;
                 const float dB = (valid && second) ? d : 0.0f;
-                const float t = __builtin_fmaf(-(float)F::Z, sx, (a0[m][r] + a1[m][r]) + (a2[m][r] + a3[m][r]));
+                const float sn = ((a[0][m][r] + a[1][m][r]) + (a[2][m][r] + a[3][m][r])) +
+                                 ((a[4][m][r] + a[5][m][r]) + (a[6][m][r] + a[7][m][r]));
+                const float t = __builtin_fmaf(-(float)F::Z, sx, sn);
                 accA[m][r] = __builtin_fmaf(dA, t, accA[m][r]);
                 accB[m][r] = __builtin_fmaf(dB, t, accB[m][r]);
             }
@@ -1010,19 +1026,23 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
                 const int slot = s % RPR;
 #pragma unroll
                 for (int m = 0; m < M; m++) {
-                    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+                    // Eight accumulator chains of two words each: the codes are unsigned (the
+                    // zero point is folded in below), so a chain's rounding error scales with
+                    // sum n|x|, not sum |n - z||x|; short chains keep it well inside the bound.
+                    float a[8];
 #pragma unroll
-                    for (int i = 0; i < 8; i += 2) {
-                        const uint32_t w0 = block_word(buf[s], i), w1 = block_word(buf[s], i + 1);
-                        if (TYPE == PN_TYPE_PN3T) {
-                            word_dot2(w0, &xq[m][i * F::CPW], a0, a1);
-                            word_dot2(w1, &xq[m][(i + 1) * F::CPW], a2, a3);
-                        } else {
-                            word_fp8(w0, &xq[m][i * F::CPW], a0, a1);
-                            word_fp8(w1, &xq[m][(i + 1) * F::CPW], a2, a3);
-                        }
+                    for (int c = 0; c < 8; c++)
+                        a[c] = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const uint32_t w = block_word(buf[s], i);
+                        const int c = 2 * (i & 3);
+                        if (TYPE == PN_TYPE_PN3T)
+                            word_dot2(w, &xq[m][i * F::CPW], a[c], a[c + 1]);
+                        else
+                            word_fp8(w, &xq[m][i * F::CPW], a[c], a[c + 1]);
                     }
-                    const float t = (a0 + a1) + (a2 + a3);
+                    const float t = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
                     vals[slot * M + m] = (d * scl[m]) * __builtin_fmaf(-(float)F::Z, sxs[m], t);
                 }
                 if (slot == RPR - 1 || it == nrows - 1) {

@@ -45,7 +45,8 @@ enum {
     PN_ERR_SHAPE = -2,  /* K is not a positive whole number of blocks, or a size is negative */
     PN_ERR_TOKENS = -3, /* M (tokens) outside 0..4 */
     PN_ERR_NULL = -4,   /* a required pointer is NULL */
-    PN_ERR_ALIGN = -5,  /* W not 2-byte aligned, x / y / w not 4-byte aligned, bf16 x not 2-byte */
+    PN_ERR_ALIGN = -5,  /* W not 2-byte aligned, x / y / w not 4-byte aligned, bf16 x not 2-byte,
+                           NVFP4 codes not 8-byte aligned */
     PN_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
     PN_ERR_DEVICE = -7  /* the current device is not gfx950 */
 };
@@ -79,10 +80,20 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
 
 /* ---- PN GEMV -------------------------------------------------------------------------------
  * y[m*N + n] = sum_k w[n, k] * x[m*K + k] for m < M (1 <= M <= 4 tokens), with w the decode above,
- * accumulated in fp32. x is fp32[M, K] row-major, y fp32[M, N] row-major (overwritten). Accuracy:
- * |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100. Rows are not validated
- * here (validate at load); an invalid row gives an unspecified value but no out-of-bounds access.
- * Deterministic: the same inputs give the same bits on every call. */
+ * accumulated in fp32. x is fp32[M, K] row-major, y fp32[M, N] row-major (overwritten).
+ * Accuracy: |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100, under two
+ * conditions that activations of ordinary dynamic range meet by a wide margin:
+ *  - The zero point is folded per block, d * (sum n x - z * sum x), with the unsigned codes n, in
+ *    fp32 chains of at most 16 terms, so the rounding error scales with a block's sum n|x| rather
+ *    than its sum |n - z||x|. It stays inside the bound unless, in the blocks that dominate a
+ *    row, sum n|x| exceeds about 8 * sum |n - z||x| (a large x meeting a code next to z).
+ *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
+ *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
+ *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
+ *    Every other path uses x exactly (scaled by powers of two). Rows are not
+ * validated here (validate at load); an invalid row gives an unspecified value but no
+ * out-of-bounds access. Deterministic: the same inputs and launch give the same bits on every
+ * call. */
 int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
             void *stream);
 
@@ -91,7 +102,8 @@ int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64
  * 80 or 64 weights per block: 36 candidate scales s = fp16(sigma * m * amax / z),
  * m = 0.50, 0.52, ..., 1.20, codes clamp(rint(w/s) + z, 0, 2z-1), double-precision squared error,
  * ties to the larger m; an all-zero group, or one whose candidates all round to zero, is the
- * canonical zero group (d = +0, codes z). Bit-identical to the library's CPU oracle.
+ * canonical zero group (d = +0, codes z). Every step runs in fp64 in the order stated, so these
+ * rules fix every output bit.
  * status (int32[nrows], optional, may be NULL) receives per row the OR of: 1 = a group held a NaN
  * or infinity, 2 = every candidate scale overflowed fp16 (such groups are written as the canonical
  * zero group). */
@@ -113,7 +125,8 @@ int pn_nvfp4_dequantize_rows(const uint8_t *codes, const uint8_t *scales, float 
                              int64_t K, float *out, void *stream);
 
 /* y[m*N + n] = sum_k w[n, k] * x[m, k], x bf16[M, K] (raw 16-bit words, row-major), 1 <= M <= 4,
- * fp32 accumulation; same accuracy contract as pn_gemv. */
+ * fp32 accumulation; same accuracy contract as pn_gemv. codes must be 8-byte aligned (rows of
+ * K/2 bytes with K a multiple of 16 keep every row 8-byte aligned), else PN_ERR_ALIGN. */
 int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
                   const uint16_t *x_bf16, int64_t M, float *y, void *stream);
 
@@ -125,8 +138,8 @@ int pn_nvfp4_global_scale(const float *w, int64_t count, float *g_out, void *str
  * 1.00, 0.95, 0.90, 0.85, 0.80 on the scale e4m3(c * amax_group / (6 g)) (nearest, ties to even,
  * saturating at 448), codes the nearest E2M1 word of w / (S g) (ties to even, saturating at 6, sign
  * kept), squared error of the decoded weights in double, ties keep the earlier multiplier.
- * g is read from device memory (g_dev, e.g. written by pn_nvfp4_global_scale). Bit-identical to the
- * library's CPU oracle. */
+ * g is read from device memory (g_dev, e.g. written by pn_nvfp4_global_scale). Every step runs in
+ * fp64 in the order stated, so these rules fix every output bit. */
 int pn_nvfp4_quantize_rows(const float *w, int64_t N, int64_t K, const float *g_dev,
                            uint8_t *codes, uint8_t *scales, void *stream);
 

@@ -186,6 +186,48 @@ def test_gemv_long_rows(env, typ, N, nb, M):
         assert_within(y, y_ref, bound)
 
 
+@pytest.mark.parametrize("force", ["PN_GEMV_NO_XREG", "PN_GEMV_NO_FLAT"])
+@pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 19, 40), (PN4T, 45, 130), (PN3T, 9, 70)])
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_general_kernel_forced(env, monkeypatch, force, typ, N, nb, M):
+    """The general LDS kernel at 1-2 tokens, reached by switching off the specialised kernels."""
+    pn, torch, dev = env
+    monkeypatch.setenv(force, "1")
+    G = oracle.PARAMS[typ][1]
+    K = nb * G
+    _, W = quantized(typ, N, K, 8000 + nb)
+    x = synth.activations(8100 + nb, M, K)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    for offset in (0, 2):
+        y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
+        assert_within(y, y_ref, bound)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_x_dynamic_range(env, M):
+    """pn3t rows of <= 64 blocks carry x as fp16 (hi, lo) pairs with one exponent per block: within
+    the documented range (every x within 2^20 of its block's largest |x|) the tolerance holds.
+    Here |x| is in [1, 2) with one element per block at 2^19. That element meets code 0 (weight
+    -4d), so the block's sum of n|x| stays comparable to its sum of |n - z||x|: the condition under
+    which the folded zero point keeps the bound (a dominant x meeting a code next to z is the
+    documented exception)."""
+    pn, torch, dev = env
+    N, K = 300, 5120
+    _, W = quantized(PN3T, N, K, 8200)
+    W = W.copy()
+    # element 37 of each block is code t = 7 of word 3: bits 25..27 of the word, i.e. bits 1..3 of
+    # block byte 2 + 4*3 + 3 = 17 ("PN weight format", "Block layout"); set it to 0
+    blocks = W.reshape(N, K // 80, 34)
+    blocks[:, :, 17] &= np.uint8(0xF1)
+    u = synth.uniform(8201, M * K).reshape(M, K)
+    x = ((1.0 + u) * np.where(synth.uniform(8202, M * K).reshape(M, K) < 0.5, -1.0, 1.0))
+    x[:, 37::80] = 2.0 ** 19
+    x = x.astype(np.float32)
+    y_ref, bound = oracle.gemv(PN3T, W, N, K, x)
+    y = run_gemv(pn, torch, dev, PN3T, dev_bytes(torch, dev, W), N, K, x)
+    assert_within(y, y_ref, bound)
+
+
 @pytest.mark.parametrize("typ,nb", [(PN3T, 1), (PN3T, 3), (PN4T, 129)])
 def test_decode_validate_ragged(env, typ, nb):
     pn, torch, dev = env
