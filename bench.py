@@ -111,6 +111,111 @@ def copy_calibration(torch, dev, mb: int, reps: int = 4):
     log(f"[bench] copy calibration: {reps} copies of {mb} MiB")
 
 
+def time_launches(torch, stream, launch, copies, reps, warmup):
+    """Average µs of `launch(i)` over `reps` back-to-back launches (rotating copies i % copies)
+    between two events on the launch stream."""
+    for i in range(warmup):
+        launch(i % copies)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        launch(i % copies)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def check(st, what):
+    if st != 0:
+        raise RuntimeError(f"{what} failed: status {st}")
+
+
+def quantize_pn(pn, torch, dev, typ, w_np):
+    """Quantize fp32 rows on the GPU and validate them; returns the device bytes."""
+    N, K = w_np.shape
+    w = torch.from_numpy(w_np).to(dev)
+    W = torch.empty((N, pn.row_bytes(typ, K)), dtype=torch.uint8, device=dev)
+    st = torch.empty(N, dtype=torch.int32, device=dev)
+    pn.quantize_rows(typ, w, W, st)
+    ver = torch.empty(N, dtype=torch.int32, device=dev)
+    pn.validate_rows(typ, W, N, K, ver)
+    torch.cuda.synchronize()
+    if int(st.abs().sum()) != 0 or int(ver.sum()) != N:
+        raise RuntimeError("quantizer status / validation failed")
+    return W
+
+
+def extra_workloads(pn, torch, dev, reps, warmup):
+    """The other measured configurations: per launch µs and weight-GB/s, weights rotated over
+    enough copies to exceed the 256 MB Infinity Cache."""
+    import numpy as np
+    import synth
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    out = {}
+
+    def pn_entry(typ, N, K, Ws, M, x, y):
+        us = time_launches(torch, stream, lambda c: check(pn.gemv_ptr(
+            typ, Ws[c].data_ptr(), N, K, x.data_ptr(), M, y.data_ptr(), sh), "pn_gemv"),
+            len(Ws), reps, warmup)
+        return {"us": round(us, 3), "GBs": round(Ws[0].numel() / us / 1e3, 1)}
+
+    # pn4t 5120 x 6144, Laplace(0, 0.015) with 0.1% outliers x8, M = 1, 32 copies
+    N, K = 5120, 6144
+    W0 = quantize_pn(pn, torch, dev, 125, synth.laplace_outlier_weights(201, 202, N, K, 0.015, 0.001, 8.0))
+    Ws = [W0] + [W0.clone() for _ in range(31)]
+    x = torch.from_numpy(np.ascontiguousarray(synth.activations(203, 1, K))).to(dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    out["pn4t_5120x6144_laplace_M1"] = pn_entry(125, N, K, Ws, 1, x, y)
+    del Ws, W0
+    log("[bench] extra: pn4t 5120x6144 done")
+
+    # decoder-layer set at M = 1..4, 4 copies (679.6 MB)
+    layer = [("gate", 124, 17408, 5120, 401), ("up", 124, 17408, 5120, 402), ("q", 124, 6144, 5120, 403),
+             ("o", 124, 5120, 5120, 404), ("k", 125, 1024, 5120, 405), ("v", 125, 1024, 5120, 406),
+             ("p6144", 125, 5120, 6144, 407), ("down", 125, 5120, 17408, 408)]
+    mats = []
+    for name, typ, N, K, seed in layer:
+        W0 = quantize_pn(pn, torch, dev, typ, synth.gaussian_weights(seed, N, K, 0.02))
+        mats.append((name, typ, N, K, [W0] + [W0.clone() for _ in range(3)]))
+    xs = {K: torch.from_numpy(np.ascontiguousarray(synth.activations(409, 4, K))).to(dev)
+          for K in (5120, 6144, 17408)}
+    y = torch.empty((4, 17408), dtype=torch.float32, device=dev)
+    for M in (1, 2, 3, 4):
+        per, tot_b, tot_us = {}, 0, 0.0
+        for name, typ, N, K, Ws in mats:
+            e = pn_entry(typ, N, K, Ws, M, xs[K], y)
+            per[name] = e
+            tot_b += Ws[0].numel()
+            tot_us += e["us"]
+        out[f"layer_set_M{M}"] = {"GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
+                                   "per_matrix_us": {k: v["us"] for k, v in per.items()}}
+    del mats
+    log("[bench] extra: layer set done")
+
+    # NVFP4 17408 x 5120, clip-search quantized on the GPU, x bf16, M = 1..4, 11 copies
+    N, K = 17408, 5120
+    w = torch.from_numpy(synth.gaussian_weights(501, N, K, 0.02)).to(dev)
+    g = torch.zeros(1, dtype=torch.float32, device=dev)
+    pn.nvfp4_global_scale(w, g)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    pn.nvfp4_quantize_rows(w, g, codes, scales)
+    torch.cuda.synchronize()
+    del w
+    gv = float(g.item())
+    C = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(10)]
+    xb = torch.from_numpy(np.ascontiguousarray(synth.activations_bf16(502, 4, K)).view(np.int16)).to(dev)
+    nbytes = codes.numel() + scales.numel() + 4
+    for M in (1, 2, 3, 4):
+        us = time_launches(torch, stream, lambda c: check(pn.gemv_nvfp4_ptr(
+            C[c][0].data_ptr(), C[c][1].data_ptr(), gv, N, K, xb.data_ptr(), M, y.data_ptr(), sh),
+            "pn_gemv_nvfp4"), len(C), reps, warmup)
+        out[f"nvfp4_17408x5120_M{M}"] = {"us": round(us, 3), "GBs": round(nbytes / us / 1e3, 1)}
+    log("[bench] extra: nvfp4 done")
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle's GEMV timed on the host cores: a bounded sample (1/16 of the rows of each MLP
     matrix, quantized by the oracle), repeated to ~`seconds` of work."""
@@ -147,6 +252,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=5, help="rotated weight copies (>= 3 to exceed MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other measured configurations (pn4t 5120x6144, layer set at "
+                         "M=1..4, NVFP4 at M=1..4)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -256,6 +364,8 @@ def main():
                      "avg_launch_us": round(d_us, 3), "algorithmic_bytes_per_launch": d_bytes},
         "kernels": kern,
     }
+    if not args.no_extra:
+        result["extra"] = extra_workloads(pn, torch, dev, args.steps, args.warmup)
     if args.copy_mb > 0:
         copy_calibration(torch, dev, args.copy_mb)
     if args.cpu_seconds > 0:

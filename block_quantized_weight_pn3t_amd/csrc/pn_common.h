@@ -83,6 +83,59 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// ---- cross-lane reduction -----------------------------------------------------------------------
+
+#define PN_DPP(v, ctrl)                                                                            \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF,  \
+                                                       0xF, false))
+
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the row's sum.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += PN_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+    v += PN_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+    v += PN_DPP(v, 0x141);  // row_half_mirror
+    v += PN_DPP(v, 0x140);  // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ void swap32(float &a, float &b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    a = __builtin_bit_cast(float, (unsigned)p[0]);
+    b = __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+__device__ __forceinline__ void swap16(float &a, float &b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    a = __builtin_bit_cast(float, (unsigned)p[0]);
+    b = __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+// Transposed reduction of V per-lane partial sums (V a multiple of 4) over the wave. Afterwards
+// out[i] (i < V/4) holds, in every lane of DPP row q = lane / 16, the wave total of value
+// i + q * V/4. Cost: 3V/4 swaps + 3V/4 adds + V DPP adds, i.e. 2.5 instructions per value.
+template <int V>
+__device__ __forceinline__ void transpose_reduce(float (&v)[V], float (&out)[V / 4])
+{
+    float a[V / 2];
+#pragma unroll
+    for (int i = 0; i < V / 2; i++) {
+        float lo = v[i], hi = v[i + V / 2];
+        swap32(lo, hi);  // lo = [v_i lanes 0-31 | v_(i+V/2) lanes 0-31], hi = the upper halves
+        a[i] = lo + hi;  // lanes 0-31: value i, lanes 32-63: value i + V/2
+    }
+#pragma unroll
+    for (int i = 0; i < V / 4; i++) {
+        float lo = a[i], hi = a[i + V / 4];
+        swap16(lo, hi);
+        out[i] = row16_sum(lo + hi);
+    }
+}
+
 // Host side --------------------------------------------------------------------------------------
 
 // Checks that the current device is gfx950 (cached per device). Returns PN_OK, PN_ERR_HIP or

@@ -10,6 +10,10 @@
 // have 2 significant bits) and v_dot2_f32_bf16 multiplies the pair with the matching bf16 x pair
 // into an fp32 sum: one instruction per weight. The group's E4M3 scale multiplies the group sum
 // once; g multiplies the row total once.
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include "pn_common.h"
 
 namespace pn {
@@ -138,6 +142,157 @@ __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(const uint8_t *__restri
         }
 }
 
+// ---- rows of at most 64*GPL groups, M <= 2: x in registers ---------------------------------------
+//
+// Persistent: one workgroup of 8 waves per CU; rows split into contiguous ranges per SIMD slot
+// (quotient and remainder from the host). Lane l owns groups l, l + 64, ..., l + 64*(GPL-1) of every
+// row: its x (8 bf16 pairs per group and token) is loaded once, straight into registers (bf16
+// pairs are what v_dot2_f32_bf16 takes: no staging arithmetic, no LDS, no barrier). The x loads
+// are issued before the first weight loads, so waiting for x never waits for weights. Each row
+// then costs per lane GPL 8-byte code loads and GPL scale-byte loads, streamed through a ring of D
+// rows; per group: 8 conversions + 8 DOT2 + one E4M3 conversion (v_cvt_f32_fp8 reads the OCP
+// E4M3FN word) + one FMA. Partial sums of 4 / M rows are reduced together (transposed reduction).
+struct NvRowSplit {
+    int64_t rq;  // N / (gridDim.x * 4)
+    int rr;      // N % (gridDim.x * 4)
+};
+
+__device__ __forceinline__ float nv_dot8(uint2 cw, const uint32_t *xp, float s)
+{
+#define PN_FP4_PAIR(word, sel, xi)                                                                 \
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, sel), \
+                                        __builtin_bit_cast(bf16x2_t, xp[xi]), s, false)
+    PN_FP4_PAIR(cw.x, 0, 0);
+    PN_FP4_PAIR(cw.x, 1, 1);
+    PN_FP4_PAIR(cw.x, 2, 2);
+    PN_FP4_PAIR(cw.x, 3, 3);
+    PN_FP4_PAIR(cw.y, 0, 4);
+    PN_FP4_PAIR(cw.y, 1, 5);
+    PN_FP4_PAIR(cw.y, 2, 6);
+    PN_FP4_PAIR(cw.y, 3, 7);
+#undef PN_FP4_PAIR
+    return s;
+}
+
+template <int GPL>
+struct NvRow {
+    uint2 c[GPL];
+    uint32_t s[GPL];
+};
+
+template <int M, int GPL, int D>
+__global__ void __launch_bounds__(512) nvfp4_gemv_xreg_kernel(const uint8_t *__restrict__ codes,
+                                                              const uint8_t *__restrict__ scales,
+                                                              float g, int64_t N, int64_t K,
+                                                              const uint16_t *__restrict__ x,
+                                                              float *__restrict__ y, NvRowSplit sp)
+{
+    constexpr int RPR = 4 / M;  // rows per reduction
+    static_assert(D % RPR == 0, "ring size must be a multiple of the rows per reduction");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ng = (int)(K >> 4);  // groups per row (<= 64 * GPL)
+
+    // rows of this wave: slot = (workgroup, SIMD); the two waves of a SIMD split its range
+    const int slot = blockIdx.x * 4 + (wave & 3);
+    const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
+    const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
+    const int64_t mid = (cnt + 1) >> 1;
+    const int64_t r_begin = min(s0 + ((wave >> 2) ? mid : 0), N - 1);
+    const int nrows = (int)((wave >> 2) ? cnt - mid : mid);
+    const int last = max(nrows - 1, 0);
+
+    // x of this lane's groups, bf16 pairs in registers (clamped for groups past the row's end)
+    uint32_t xr[M][GPL][8];
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int i = 0; i < GPL; i++) {
+            const int j = min(lane + 64 * i, ng - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)m * K + 16 * (int64_t)j);
+            const uint4 a = src[0], b = src[1];
+            xr[m][i][0] = a.x; xr[m][i][1] = a.y; xr[m][i][2] = a.z; xr[m][i][3] = a.w;
+            xr[m][i][4] = b.x; xr[m][i][5] = b.y; xr[m][i][6] = b.z; xr[m][i][7] = b.w;
+        }
+
+    const int64_t cbytes = K >> 1;
+    auto load_row = [&](NvRow<GPL> &rw, int it) {
+        const int64_t row = r_begin + min(it, last);
+        const uint8_t *cp = codes + row * cbytes;
+        const uint8_t *sc = scales + row * ng;
+#pragma unroll
+        for (int i = 0; i < GPL; i++) {
+            const int j = min(lane + 64 * i, ng - 1);
+            rw.c[i] = *reinterpret_cast<const uint2 *>(cp + 8 * (int64_t)j);
+            rw.s[i] = sc[j];
+        }
+    };
+    NvRow<GPL> buf[D];
+#pragma unroll
+    for (int p = 0; p < D - 1; p++)
+        load_row(buf[p], p);
+
+    float vals[4];
+#pragma unroll
+    for (int o = 0; o < 4; o++)
+        vals[o] = 0.0f;
+    for (int it0 = 0; it0 < nrows; it0 += D) {
+#pragma unroll
+        for (int sidx = 0; sidx < D; sidx++) {
+            const int it = it0 + sidx;
+            load_row(buf[(sidx + D - 1) % D], it + D - 1);
+            if (it < nrows) {
+                const int rs = sidx % RPR;
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < GPL; i++) {
+                        // groups past the row's end (clamped loads) get a zero scale
+                        const float S = (lane + 64 * i < ng)
+                                            ? __builtin_amdgcn_cvt_f32_fp8((int)buf[sidx].s[i], 0)
+                                            : 0.0f;
+                        acc = __builtin_fmaf(S, nv_dot8(buf[sidx].c[i], xr[m][i], 0.0f), acc);
+                    }
+                    vals[rs * M + m] = acc;
+                }
+                if (rs == RPR - 1 || it == nrows - 1) {
+                    float tot[1];
+                    transpose_reduce<4>(vals, tot);
+                    if ((lane & 15) == 0) {
+                        const int o = lane >> 4;  // value o = rs * M + m
+                        const int jr = o / M, m = o - jr * M;
+                        if (jr <= rs)
+                            y[(int64_t)m * N + r_begin + (it - rs + jr)] = tot[0] * g;
+                    }
+#pragma unroll
+                    for (int o = 0; o < 4; o++)
+                        vals[o] = 0.0f;
+                }
+            }
+        }
+    }
+}
+
+template <int M, int GPL>
+static int launch_nv_xreg(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
+                          const uint16_t *x, float *y, hipStream_t s)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return PN_ERR_HIP;
+        cus = prop.multiProcessorCount;
+    }
+    const int grid = (int)std::min<int64_t>(cus, (N + 3) / 4);
+    const int64_t S = (int64_t)grid * 4;
+    hipLaunchKernelGGL((nvfp4_gemv_xreg_kernel<M, GPL, 4>), dim3((unsigned)grid), dim3(512), 0, s,
+                       codes, scales, g, N, K, x, y, NvRowSplit{N / S, (int)(N % S)});
+    return launch_status();
+}
+
 constexpr int kNvLdsBudget = 80 * 1024;
 
 template <int M, int R>
@@ -183,6 +338,18 @@ extern "C" int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float 
     if (st != PN_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    // x in registers: M <= 2, at most 64*GPL groups per row, x 16-byte aligned (PN_GEMV_NO_XREG
+    // selects the LDS kernel, for tests)
+    const int64_t ng = K >> 4;
+    if (M <= 2 && ng <= 64 * 6 && aligned(x_bf16, 16) && !getenv("PN_GEMV_NO_XREG")) {
+        if (M == 1)
+            return ng <= 64 * 4   ? launch_nv_xreg<1, 4>(codes, scales, g, N, K, x_bf16, y, s)
+                   : ng <= 64 * 5 ? launch_nv_xreg<1, 5>(codes, scales, g, N, K, x_bf16, y, s)
+                                  : launch_nv_xreg<1, 6>(codes, scales, g, N, K, x_bf16, y, s);
+        return ng <= 64 * 4   ? launch_nv_xreg<2, 4>(codes, scales, g, N, K, x_bf16, y, s)
+               : ng <= 64 * 5 ? launch_nv_xreg<2, 5>(codes, scales, g, N, K, x_bf16, y, s)
+                              : launch_nv_xreg<2, 6>(codes, scales, g, N, K, x_bf16, y, s);
+    }
     switch (M) {
     case 1: return launch_nv<1, 2>(codes, scales, g, N, K, x_bf16, y, s);
     case 2: return launch_nv<2, 2>(codes, scales, g, N, K, x_bf16, y, s);

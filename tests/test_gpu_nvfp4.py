@@ -140,3 +140,53 @@ def test_config5_full_size(env):
     for M in (1, 2, 3, 4):
         y = gemv(pn, torch, dev, codes, scales, g, N, K, xb[:M])
         assert_within(y, y_ref4[:M], bound4[:M])
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N,K", [(1, 16 * 256), (37, 16 * 257), (300, 5120), (5, 16 * 321), (1031, 6144),
+                                 (9, 16 * 385), (70, 16 * 64), (3, 16 * 5)])
+def test_gemv_register_x_shapes(env, M, N, K):
+    """1-2 tokens: the kernel that keeps x in registers (up to 6 groups per lane: K <= 6144), at
+    the 4 / 5 / 6 groups-per-lane boundaries, partly filled lanes, and past it (K = 6160)."""
+    pn, torch, dev = env
+    _, g, codes, scales = nvfp4_quantized(N, K, 540 + K % 97)
+    xb = synth.activations_bf16(541 + K, M, K)
+    y = gemv(pn, torch, dev, codes, scales, g, N, K, xb)
+    y_ref, bound = oracle.nvfp4_gemv(codes, scales, g, N, K, xb)
+    assert_within(y, y_ref, bound)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_one_hot_exact_few_tokens(env, M):
+    pn, torch, dev = env
+    N, K = 40, 5120
+    _, g, codes, scales = nvfp4_quantized(N, K, 531)
+    deq = oracle.nvfp4_dequantize_rows(codes, scales, g, N, K)
+    ks = [17, 5119][:M]
+    xb = np.zeros((M, K), np.uint16)
+    for m, k in enumerate(ks):
+        xb[m, k] = 0x3F80
+    y = gemv(pn, torch, dev, codes, scales, g, N, K, xb)
+    for m, k in enumerate(ks):
+        assert np.array_equal(y[m], deq[:, k])
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_lds_kernel_and_unaligned_x(env, monkeypatch, M):
+    """The LDS kernel at 1-2 tokens: forced, and taken by itself when x is not 16-byte aligned."""
+    pn, torch, dev = env
+    N, K = 45, 5120
+    _, g, codes, scales = nvfp4_quantized(N, K, 550)
+    xb = synth.activations_bf16(551, M, K)
+    y_ref, bound = oracle.nvfp4_gemv(codes, scales, g, N, K, xb)
+    # x at a 2-byte offset inside a larger buffer
+    buf = torch.zeros(M * K + 8, dtype=torch.int16, device=dev)
+    buf[1:1 + M * K] = up(torch, dev, xb.view(np.int16).reshape(-1))
+    xd = buf[1:1 + M * K].view(M, K)
+    yd = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    pn.gemv_nvfp4(up(torch, dev, codes), up(torch, dev, scales), g, N, K, xd, yd)
+    torch.cuda.synchronize()
+    assert_within(yd.cpu().numpy(), y_ref, bound)
+    monkeypatch.setenv("PN_GEMV_NO_XREG", "1")
+    y = gemv(pn, torch, dev, codes, scales, g, N, K, xb)
+    assert_within(y, y_ref, bound)
