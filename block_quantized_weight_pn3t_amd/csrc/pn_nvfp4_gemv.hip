@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(const uint8_t *__restri
         }
 }
 
-// ---- rows of at most 64*GPL groups, M <= 2: x in registers ---------------------------------------
+// ---- rows of at most 64*GPL groups: x in registers ------------------------------------------------
 //
 // Persistent: one workgroup of 8 waves per CU; rows split into contiguous ranges per SIMD slot
 // (quotient and remainder from the host). Lane l owns groups l, l + 64, ..., l + 64*(GPL-1) of every
@@ -288,8 +288,9 @@ static int launch_nv_xreg(const uint8_t *codes, const uint8_t *scales, float g, 
     }
     const int grid = (int)std::min<int64_t>(cus, (N + 3) / 4);
     const int64_t S = (int64_t)grid * 4;
-    hipLaunchKernelGGL((nvfp4_gemv_xreg_kernel<M, GPL, 4>), dim3((unsigned)grid), dim3(512), 0, s,
-                       codes, scales, g, N, K, x, y, NvRowSplit{N / S, (int)(N % S)});
+    // ring of 4 rows at 1-2 tokens, 2 at 3-4 (registers: x takes 8*GPL per token)
+    hipLaunchKernelGGL((nvfp4_gemv_xreg_kernel<M, GPL, M <= 2 ? 4 : 2>), dim3((unsigned)grid),
+                       dim3(512), 0, s, codes, scales, g, N, K, x, y, NvRowSplit{N / S, (int)(N % S)});
     return launch_status();
 }
 
@@ -338,17 +339,26 @@ extern "C" int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float 
     if (st != PN_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    // x in registers: M <= 2, at most 64*GPL groups per row, x 16-byte aligned (PN_GEMV_NO_XREG
-    // selects the LDS kernel, for tests)
+    // x in registers: at most 64*GPL groups per row (GPL = 6 at 1-2 tokens, 5 at 3-4), x 16-byte
+    // aligned (PN_GEMV_NO_XREG selects the LDS kernel, for tests)
     const int64_t ng = K >> 4;
-    if (M <= 2 && ng <= 64 * 6 && aligned(x_bf16, 16) && !getenv("PN_GEMV_NO_XREG")) {
-        if (M == 1)
+    if (ng <= 64 * (M <= 2 ? 6 : 5) && aligned(x_bf16, 16) && !getenv("PN_GEMV_NO_XREG")) {
+        switch (M) {
+        case 1:
             return ng <= 64 * 4   ? launch_nv_xreg<1, 4>(codes, scales, g, N, K, x_bf16, y, s)
                    : ng <= 64 * 5 ? launch_nv_xreg<1, 5>(codes, scales, g, N, K, x_bf16, y, s)
                                   : launch_nv_xreg<1, 6>(codes, scales, g, N, K, x_bf16, y, s);
-        return ng <= 64 * 4   ? launch_nv_xreg<2, 4>(codes, scales, g, N, K, x_bf16, y, s)
-               : ng <= 64 * 5 ? launch_nv_xreg<2, 5>(codes, scales, g, N, K, x_bf16, y, s)
-                              : launch_nv_xreg<2, 6>(codes, scales, g, N, K, x_bf16, y, s);
+        case 2:
+            return ng <= 64 * 4   ? launch_nv_xreg<2, 4>(codes, scales, g, N, K, x_bf16, y, s)
+                   : ng <= 64 * 5 ? launch_nv_xreg<2, 5>(codes, scales, g, N, K, x_bf16, y, s)
+                                  : launch_nv_xreg<2, 6>(codes, scales, g, N, K, x_bf16, y, s);
+        case 3:
+            return ng <= 64 * 4 ? launch_nv_xreg<3, 4>(codes, scales, g, N, K, x_bf16, y, s)
+                                : launch_nv_xreg<3, 5>(codes, scales, g, N, K, x_bf16, y, s);
+        default:
+            return ng <= 64 * 4 ? launch_nv_xreg<4, 4>(codes, scales, g, N, K, x_bf16, y, s)
+                                : launch_nv_xreg<4, 5>(codes, scales, g, N, K, x_bf16, y, s);
+        }
     }
     switch (M) {
     case 1: return launch_nv<1, 2>(codes, scales, g, N, K, x_bf16, y, s);

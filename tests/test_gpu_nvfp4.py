@@ -142,12 +142,13 @@ def test_config5_full_size(env):
         assert_within(y, y_ref4[:M], bound4[:M])
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("N,K", [(1, 16 * 256), (37, 16 * 257), (300, 5120), (5, 16 * 321), (1031, 6144),
                                  (9, 16 * 385), (70, 16 * 64), (3, 16 * 5)])
 def test_gemv_register_x_shapes(env, M, N, K):
-    """1-2 tokens: the kernel that keeps x in registers (up to 6 groups per lane: K <= 6144), at
-    the 4 / 5 / 6 groups-per-lane boundaries, partly filled lanes, and past it (K = 6160)."""
+    """The kernel that keeps x in registers (up to 6 groups per lane at 1-2 tokens: K <= 6144; 5 at
+    3-4 tokens), at the 4 / 5 / 6 groups-per-lane boundaries, partly filled lanes, and past them
+    (the LDS kernel)."""
     pn, torch, dev = env
     _, g, codes, scales = nvfp4_quantized(N, K, 540 + K % 97)
     xb = synth.activations_bf16(541 + K, M, K)
