@@ -1021,11 +1021,12 @@ struct LaunchCfg {
 };
 
 // Share of a SIMD's work given to the older of its two waves, in sixteenths (PN_GEMV_SPLIT).
+// Measured best: 12/16 for the short-row kernel, 10/16 for the long-row kernel.
 static int older_share(int dflt)
 {
     const char *e = getenv("PN_GEMV_SPLIT");
     const int v = e ? atoi(e) : dflt;
-    return v < 4 ? 4 : v > 12 ? 12 : v;
+    return v < 4 ? 4 : v > 15 ? 15 : v;
 }
 
 static int num_cus()
@@ -1092,7 +1093,7 @@ static int launch_xreg(const uint8_t *W, int64_t N, int64_t K, const float *x, f
     // 512 threads: the cooperative staging gives each thread one word of one block
     hipLaunchKernelGGL((pn_gemv_xreg_kernel<TYPE, M, D>), dim3((unsigned)grid), dim3(512), 0, s, W,
                        N, nb, (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), vec4,
-                       older_share(8));
+                       older_share(12));
     return launch_status();
 }
 

@@ -185,7 +185,8 @@ __global__ void __launch_bounds__(512) nvfp4_gemv_xreg_kernel(const uint8_t *__r
                                                               const uint8_t *__restrict__ scales,
                                                               float g, int64_t N, int64_t K,
                                                               const uint16_t *__restrict__ x,
-                                                              float *__restrict__ y, NvRowSplit sp)
+                                                              float *__restrict__ y, NvRowSplit sp,
+                                                              int fnum)
 {
     constexpr int RPR = 4 / M;  // rows per reduction
     static_assert(D % RPR == 0, "ring size must be a multiple of the rows per reduction");
@@ -193,11 +194,12 @@ __global__ void __launch_bounds__(512) nvfp4_gemv_xreg_kernel(const uint8_t *__r
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ng = (int)(K >> 4);  // groups per row (<= 64 * GPL)
 
-    // rows of this wave: slot = (workgroup, SIMD); the two waves of a SIMD split its range
+    // rows of this wave: slot = (workgroup, SIMD); the two waves of a SIMD split its range, the
+    // older one (favoured by the instruction arbiter) taking fnum/16 of it
     const int slot = blockIdx.x * 4 + (wave & 3);
     const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
     const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
-    const int64_t mid = (cnt + 1) >> 1;
+    const int64_t mid = (cnt * fnum + 8) >> 4;
     const int64_t r_begin = min(s0 + ((wave >> 2) ? mid : 0), N - 1);
     const int nrows = (int)((wave >> 2) ? cnt - mid : mid);
     const int last = max(nrows - 1, 0);
@@ -274,6 +276,14 @@ __global__ void __launch_bounds__(512) nvfp4_gemv_xreg_kernel(const uint8_t *__r
     }
 }
 
+// Older-wave share in sixteenths (PN_GEMV_NV_SPLIT overrides; 4..15); 10/16 measured best.
+static int nv_older_share()
+{
+    const char *e = getenv("PN_GEMV_NV_SPLIT");
+    const int v = e ? atoi(e) : 10;
+    return v < 4 ? 4 : v > 15 ? 15 : v;
+}
+
 template <int M, int GPL>
 static int launch_nv_xreg(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
                           const uint16_t *x, float *y, hipStream_t s)
@@ -290,7 +300,8 @@ static int launch_nv_xreg(const uint8_t *codes, const uint8_t *scales, float g, 
     const int64_t S = (int64_t)grid * 4;
     // ring of 4 rows at 1-2 tokens, 2 at 3-4 (registers: x takes 8*GPL per token)
     hipLaunchKernelGGL((nvfp4_gemv_xreg_kernel<M, GPL, M <= 2 ? 4 : 2>), dim3((unsigned)grid),
-                       dim3(512), 0, s, codes, scales, g, N, K, x, y, NvRowSplit{N / S, (int)(N % S)});
+                       dim3(512), 0, s, codes, scales, g, N, K, x, y, NvRowSplit{N / S, (int)(N % S)},
+                       nv_older_share());
     return launch_status();
 }
 

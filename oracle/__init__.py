@@ -1,4 +1,5 @@
-"""CPU oracle for the PN / NVFP4 decode-step GEMV -- TEST INFRASTRUCTURE, NOT THE PRODUCT.
+"""CPU oracle for the PN / NVFP4 / row-scaled E4M3 decode-step GEMV -- TEST INFRASTRUCTURE, NOT
+THE PRODUCT.
 
 Only the tests, the smoke entry and the bench's CPU-baseline leg may import this package. It wraps
 ``oracle/liboracle.so`` (plain C, built with gcc from ``pn_oracle.c``) through ctypes and numpy. It
@@ -65,6 +66,12 @@ def _sigs():
         "or_double_to_f16_n": (None, [P, I64, P]),
         "or_double_to_e4m3_sat_n": (None, [P, I64, P]),
         "or_double_to_e2m1_sat_n": (None, [P, I64, P]),
+        "or_double_to_bf16": (C.c_uint16, [C.c_double]),
+        "or_double_to_bf16_n": (None, [P, I64, P]),
+        "or_fp8row_dequantize_rows": (None, [P, P, I64, I64, P]),
+        "or_fp8row_validate_rows": (None, [P, P, I64, I64, P]),
+        "or_fp8row_quantize_rows": (None, [P, I64, I64, P, P, P]),
+        "or_fp8row_gemv": (None, [P, P, I64, I64, P, I64, P, P]),
     }
 
 
@@ -302,6 +309,74 @@ def nvfp4_gemv(codes, scales, g: float, N: int, K: int, x_bf16: np.ndarray,
         b = np.empty((M, e - s), dtype=np.float64)
         L.or_nvfp4_gemv(_p(codes) + s * (K // 2), _p(scales) + s * (K // 16), g, e - s, K, _p(x), M,
                         _p(y), _p(b))
+        ys[i], bs[i] = y, b
+
+    with ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run, range(len(parts))))
+    return np.concatenate(ys, axis=1), np.concatenate(bs, axis=1)
+
+
+# ---- row-scaled E4M3FN (FP8_E4M3FN_ROW_BF16S) ----------------------------------------------------
+
+def double_to_bf16(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64).ravel()
+    out = np.empty(v.size, dtype=np.uint16)
+    lib().or_double_to_bf16_n(_p(v), v.size, _p(out))
+    return out
+
+
+def fp8row_dequantize_rows(codes: np.ndarray, scales: np.ndarray, N: int, K: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    out = np.empty((N, K), dtype=np.float32)
+    lib().or_fp8row_dequantize_rows(_p(codes), _p(scales), N, K, _p(out))
+    return out
+
+
+def fp8row_validate_rows(codes: np.ndarray, scales: np.ndarray, N: int, K: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    out = np.empty(N, dtype=np.int32)
+    lib().or_fp8row_validate_rows(_p(codes), _p(scales), N, K, _p(out))
+    return out
+
+
+def fp8row_quantize_rows(w: np.ndarray, threads: int | None = None):
+    """Returns (codes uint8[N, K], scales uint16[N], status int32[N])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.empty((N, K), dtype=np.uint8)
+    scales = np.empty(N, dtype=np.uint16)
+    status = np.empty(N, dtype=np.int32)
+    L = lib()
+
+    def run(r):
+        s, e = r
+        L.or_fp8row_quantize_rows(_p(w) + s * K * 4, e - s, K, _p(codes) + s * K,
+                                  _p(scales) + s * 2, _p(status) + s * 4)
+
+    parts = _row_split(N, threads or _threads(N))
+    with ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run, parts))
+    return codes, scales, status
+
+
+def fp8row_gemv(codes, scales, N: int, K: int, x: np.ndarray, threads: int | None = None):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    M = x.shape[0]
+    L = lib()
+    parts = _row_split(N, threads or _threads(N))
+    ys, bs = [None] * len(parts), [None] * len(parts)
+
+    def run(i):
+        s, e = parts[i]
+        y = np.empty((M, e - s), dtype=np.float64)
+        b = np.empty((M, e - s), dtype=np.float64)
+        L.or_fp8row_gemv(_p(codes) + s * K, _p(scales) + s * 2, e - s, K, _p(x), M, _p(y), _p(b))
         ys[i], bs[i] = y, b
 
     with ThreadPoolExecutor(len(parts)) as ex:

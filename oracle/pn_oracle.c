@@ -12,8 +12,11 @@
  *           "Block layout", "Value", "Reference quantizer", "Validation".
  *   [QP]    "Quantisation and profiles" (TandemLLM docs): sections "NVFP4", "The clip search".
  *   [TF]    NInfer "tensor formats" maintainer page: the BF16 word (section 3.1), the NVFP4
- *           representation with its E2M1 / E4M3FN words (section 3.3), and the integral
- *           rounding examples of the canonical encoder (section 7).
+ *           representation with its E2M1 / E4M3FN words (section 3.3), the row-scaled E4M3FN
+ *           format FP8_E4M3FN_ROW_BF16S (section 3.4), and the integral rounding examples of the
+ *           canonical encoder (section 7).
+ *   [QP]    also "The FP8 head": one scale per row, a search over 1.0, 0.95, 0.90 of the row's
+ *           largest weight.
  *
  * Floating point: everything that is not stated as fp32 by the pages is done in double.
  * Build with -ffp-contract=off so that no multiply-add is fused behind our back.
@@ -27,6 +30,9 @@
  *   GEMV        exact rational brute force on small rows; one-hot and block-indicator x.
  *   quantizers  invariants and brute-force re-scans only: parity unpinned against the engines'
  *               own quantizers (no printed vectors exist on the pages).
+ *   row E4M3    decode by the section 3.4 product over all 256 code words at power-of-two and
+ *               other scales; each validity clause of section 3.4 on its own; the bf16 rounding
+ *               against the integer round-half-even of binary32 words.
  */
 #include <math.h>
 #include <stdint.h>
@@ -91,6 +97,35 @@ float or_bf16_to_float(uint16_t b)
     float f;
     memcpy(&f, &u, 4);
     return f;
+}
+
+/* Double -> bfloat16 word, one rounding to nearest with ties to even (8 significant bits,
+ * binary32's exponent range, subnormals down to 2^-133), +-inf past the largest finite value. */
+uint16_t or_double_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80);
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1; /* a in [2^E, 2^(E+1)) */
+    if (E < -126) {
+        double r = rint(ldexp(a, 133)); /* subnormal quantum 2^-133; r = 128 is the smallest normal */
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    double r = rint(ldexp(a, 7 - E)); /* in [128, 256] */
+    if (r == 256.0) {
+        r = 128.0;
+        E += 1;
+    }
+    if (E > 127)
+        return (uint16_t)(sign | 0x7F80);
+    return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(r - 128.0));
 }
 
 /* [TF] section 3.3: E4M3FN. sign bit 7, exponent bits 6:3 (bias 7), fraction bits 2:0.
@@ -554,6 +589,127 @@ void or_nvfp4_gemv(const uint8_t *codes, const uint8_t *scales, float g, int64_t
             y[m * N + n] = acc;
             bound[m * N + n] = abs_acc;
         }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Row-scaled E4M3FN ([TF] section 3.4, FP8_E4M3FN_ROW_BF16S; [QP] "The FP8 head"): codes        */
+/* [N, K] E4M3FN words, row-major; one bfloat16 multiplier word per row.                         */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [TF] section 3.4: w = binary32(e4m3(c) * bf16(s)), the scale a multiplier. */
+void or_fp8row_dequantize_rows(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                               float *out)
+{
+    for (int64_t n = 0; n < N; n++) {
+        float s32 = or_bf16_to_float(scales[n]);
+        for (int64_t k = 0; k < K; k++) {
+            float c32 = (float)or_e4m3_to_double(codes[n * K + k]);
+            out[n * K + k] = c32 * s32;
+        }
+    }
+}
+
+/* [TF] section 3.4 validity, per row: the scale word has sign bit 0 and is finite (positive zero
+ * and positive subnormals included); no code is a NaN word (0x7F, 0xFF); a positive-zero scale
+ * requires every code to be a signed zero (0x00 or 0x80). Returns 1 for a valid row. */
+void or_fp8row_validate_rows(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                             int32_t *verdict)
+{
+    for (int64_t n = 0; n < N; n++) {
+        uint16_t s = scales[n];
+        int ok = !(s & 0x8000) && (s & 0x7F80) != 0x7F80;
+        for (int64_t k = 0; k < K; k++) {
+            uint8_t c = codes[n * K + k];
+            if ((c & 0x7F) == 0x7F)
+                ok = 0;
+            if (s == 0 && (c & 0x7F) != 0)
+                ok = 0;
+        }
+        verdict[n] = ok;
+    }
+}
+
+/* [QP] "The FP8 head", with the scale stored as the [TF] section 3.4 bfloat16 multiplier: for each
+ * row and each multiplier c in 1.0, 0.95, 0.90, the scale word is bf16(c * amax / 448) (skipped when
+ * it is zero or not finite); each code is the E4M3FN word nearest to w / s, ties to the even
+ * fraction, saturating at 448, sign kept (also when the magnitude rounds to zero); the error is the
+ * squared difference between w and the fp32 decode, summed in double in k order; the smallest
+ * error wins, a tie keeping the earlier multiplier. An all-zero row, or one whose candidates are
+ * all skipped, is scale +0 with codes 0x00. status[n] = 1 when the row holds a NaN or infinity
+ * (the row is then written as the zero row). */
+void or_fp8row_quantize_rows(const float *w, int64_t N, int64_t K, uint8_t *codes,
+                             uint16_t *scales, int32_t *status)
+{
+    static const double mult[3] = {1.0, 0.95, 0.90};
+    for (int64_t n = 0; n < N; n++) {
+        const float *wr = w + n * K;
+        uint8_t *cr = codes + n * K;
+        double amax = 0.0;
+        int bad = 0;
+        for (int64_t k = 0; k < K; k++) {
+            double a = fabs((double)wr[k]);
+            if (!isfinite(a))
+                bad = 1;
+            else if (a > amax)
+                amax = a;
+        }
+        status[n] = bad;
+        scales[n] = 0;
+        memset(cr, 0, (size_t)K);
+        if (bad || amax == 0.0)
+            continue;
+        double best = INFINITY;
+        for (int i = 0; i < 3; i++) {
+            uint16_t sw = or_double_to_bf16(mult[i] * amax / 448.0);
+            double sd = (double)or_bf16_to_float(sw);
+            if (sd == 0.0 || !isfinite(sd))
+                continue;
+            float s32 = (float)sd;
+            double err = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double q = (double)wr[k] / sd;
+                uint8_t c = (uint8_t)((signbit(q) ? 0x80 : 0) | or_double_to_e4m3_sat(fabs(q)));
+                float dq = (float)or_e4m3_to_double(c) * s32;
+                double e = (double)wr[k] - (double)dq;
+                err += e * e;
+            }
+            if (err < best) {
+                best = err;
+                scales[n] = sw;
+                for (int64_t k = 0; k < K; k++) {
+                    double q = (double)wr[k] / sd;
+                    cr[k] = (uint8_t)((signbit(q) ? 0x80 : 0) | or_double_to_e4m3_sat(fabs(q)));
+                }
+            }
+        }
+    }
+}
+
+/* GEMV: y[m, n] = sum_k w[n, k] x[m, k] in double with w the fp32 decode above, x fp32;
+ * bound = sum |w x|. */
+void or_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                    const float *x, int64_t M, double *y, double *bound)
+{
+    for (int64_t n = 0; n < N; n++) {
+        float s32 = or_bf16_to_float(scales[n]);
+        for (int64_t m = 0; m < M; m++) {
+            double acc = 0.0, abs_acc = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                float wv = (float)or_e4m3_to_double(codes[n * K + k]) * s32;
+                double pr = (double)wv * (double)x[m * K + k];
+                acc += pr;
+                abs_acc += fabs(pr);
+            }
+            y[m * N + n] = acc;
+            bound[m * N + n] = abs_acc;
+        }
+    }
+}
+
+void or_double_to_bf16_n(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = or_double_to_bf16(v[i]);
 }
 
 /* Vector helpers for the tests (element-wise wrappers of the scalar codecs). */

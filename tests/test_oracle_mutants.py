@@ -46,6 +46,15 @@ MUTANTS = {
     "nvfp4_clip_keeps_last_multiplier_only": ("for (int i = 0; i < 5; i++) {",
                                                "for (int i = 4; i < 5; i++) {",
                                                ["test_oracle_nvfp4.py"]),
+    "fp8row_scale_divides": ("            out[n * K + k] = c32 * s32;",
+                             "            out[n * K + k] = c32 / s32;",
+                             ["test_oracle_fp8row.py"]),
+    "fp8row_zero_scale_clause_dropped": ("            if (s == 0 && (c & 0x7F) != 0)\n                ok = 0;",
+                                         "",
+                                         ["test_oracle_fp8row.py"]),
+    "bf16_rounding_truncates": ("    double r = rint(ldexp(a, 7 - E)); /* in [128, 256] */",
+                                "    double r = floor(ldexp(a, 7 - E)); /* in [128, 256] */",
+                                ["test_oracle_fp8row.py"]),
 }
 
 
