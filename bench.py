@@ -213,6 +213,32 @@ def extra_workloads(pn, torch, dev, reps, warmup):
             "pn_gemv_nvfp4"), len(C), reps, warmup)
         out[f"nvfp4_17408x5120_M{M}"] = {"us": round(us, 3), "GBs": round(nbytes / us / 1e3, 1)}
     log("[bench] extra: nvfp4 done")
+    del C, codes, scales
+
+    # row-scaled E4M3 head, 248,320 x 5,120 (1.27 GB of codes per copy), quantized on the GPU from
+    # seeded N(0, 0.02) weights (every 7th row x20), 2 copies, M = 1..4
+    N, K = 248320, 5120
+    hc = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    hs = torch.empty(N, dtype=torch.int16, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(601)
+    for r0 in range(0, N, 8192):
+        n = min(8192, N - r0)
+        w = torch.randn((n, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        w[::7] *= 20.0
+        pn.fp8row_quantize_rows(w, hc[r0:r0 + n], hs[r0:r0 + n])
+    torch.cuda.synchronize()
+    del w
+    H = [(hc, hs), (hc.clone(), hs.clone())]
+    xh = torch.from_numpy(np.ascontiguousarray(synth.activations(602, 4, K))).to(dev)
+    yh = torch.empty((4, N), dtype=torch.float32, device=dev)
+    hbytes = N * K + 2 * N
+    for M in (1, 2, 3, 4):
+        us = time_launches(torch, stream, lambda c: check(pn.gemv_fp8row_ptr(
+            H[c][0].data_ptr(), H[c][1].data_ptr(), N, K, xh.data_ptr(), M, yh.data_ptr(), sh),
+            "pn_gemv_fp8row"), len(H), max(10, reps // 10), max(2, warmup // 5))
+        out[f"fp8row_head_248320x5120_M{M}"] = {"us": round(us, 2), "GBs": round(hbytes / us / 1e3, 1)}
+    log("[bench] extra: fp8row head done")
     return out
 
 
@@ -254,7 +280,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured configurations (pn4t 5120x6144, layer set at "
-                         "M=1..4, NVFP4 at M=1..4)")
+                         "M=1..4, NVFP4 at M=1..4, row-scaled E4M3 head at M=1..4)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
     args = ap.parse_args()

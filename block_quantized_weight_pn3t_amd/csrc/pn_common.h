@@ -39,6 +39,7 @@ struct RawBlock {
 };
 
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void load_block(const uint8_t *p, RawBlock &rb)
 {
@@ -134,6 +135,79 @@ __device__ __forceinline__ void transpose_reduce(float (&v)[V], float (&out)[V /
         swap16(lo, hi);
         out[i] = row16_sum(lo + hi);
     }
+}
+
+// Row range of a wave. The rows are split into balanced contiguous ranges over the SIMD slots
+// (4 per workgroup: a CU's SIMDs, which take the workgroup's waves round-robin), and each slot's
+// range over the waves that share that SIMD (wave w and w + 4 of an 8-wave group). Every SIMD thus
+// gets the same number of rows, +-1, whichever wave count divides it. The instruction arbiter
+// favours the older wave of a SIMD, so it may be given the larger part (fnum/16). The quotient
+// and remainder of N by the slot count come from the host (rq, rr): no division runs on the
+// device.
+struct RowSplit {
+    int64_t rq;  // N / (gridDim.x * 4)
+    int rr;      // N % (gridDim.x * 4)
+};
+
+__device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int nwaves, int fnum,
+                                          int64_t &begin, int &count)
+{
+    const int slot = blockIdx.x * 4 + (wave & 3);
+    const int h = wave >> 2;
+    const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
+    const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
+    // two waves per SIMD: the older one (h = 0) takes the first fnum/16 of the slot's rows
+    const int64_t mid = nwaves == 8 ? (cnt * fnum + 8) >> 4 : cnt;
+    const int64_t b0 = h ? mid : 0;
+    const int64_t b1 = h ? cnt : mid;
+    count = (int)(b1 - b0);
+    // an empty range may start at N; its (unused, clamped) prefetch must still address a real row
+    begin = min(s0 + b0, N - 1);
+}
+
+inline RowSplit row_split(int64_t N, int grid)
+{
+    const int64_t S = (int64_t)grid * 4;
+    return RowSplit{N / S, (int)(N % S)};
+}
+
+// ---- E4M3FN words (NInfer "tensor formats", section 3.3) in double ----------------------------
+
+__device__ __forceinline__ double e4m3_f64(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    double v;
+    if (e == 0)
+        v = (double)m * 0x1p-9;
+    else if (e == 15 && m == 7)
+        v = __builtin_nan("");
+    else
+        v = __longlong_as_double((int64_t)((uint64_t)(e - 7 + 1023) << 52 | (uint64_t)m << 49));
+    return (c & 0x80u) ? -v : v;
+}
+
+// non-negative double -> E4M3FN word, nearest even, saturating at 448 (0x7E)
+__device__ __forceinline__ uint32_t f64_to_e4m3_sat(double v)
+{
+    if (!(v > 0.0))
+        return 0;
+    if (v >= 448.0)
+        return 0x7E;
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    int e = (int)(u >> 52) - 1023;
+    if (e < -6)
+        return (uint32_t)__builtin_rint(v * 512.0);  // subnormal quantum 2^-9 (8 -> 0x08)
+    const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+    uint64_t q = sig >> 49;
+    const uint64_t rem = sig & ((1ull << 49) - 1), half = 1ull << 48;
+    if (rem > half || (rem == half && (q & 1)))
+        q++;
+    if (q == 16) {
+        q = 8;
+        e++;
+    }
+    const uint32_t code = (uint32_t)((e + 7) << 3) | (uint32_t)(q - 8);
+    return code > 0x7Eu ? 0x7Eu : code;
 }
 
 // Host side --------------------------------------------------------------------------------------

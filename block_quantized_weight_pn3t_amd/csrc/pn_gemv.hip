@@ -39,7 +39,6 @@
 namespace pn {
 
 typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Bit position p, inside its 16-bit half after the masking used below, of code t of a word: pn3t
 // t = 0,1 and 6,7 sit at p = 0; t = 2,3 and 8,9 at p = 3; t = 4,5 at p = 6 (t = 6..9 after >> 9).
@@ -232,39 +231,6 @@ struct Item {
     RawBlock blk[R];
 };
 
-// Row range of a wave. The rows are split into balanced contiguous ranges over the SIMD slots
-// (4 per workgroup: a CU's SIMDs, which take the workgroup's waves round-robin), and each slot's
-// range over the waves that share that SIMD (wave w and w + 4 of an 8-wave group). Every SIMD thus
-// gets the same number of rows, +-1, whichever wave count divides it. The instruction arbiter
-// favours the older wave of a SIMD, so it may be given the larger part (fnum/16). The quotient
-// and remainder of N by the slot count come from the host (rq, rr): no division runs on the
-// device.
-struct RowSplit {
-    int64_t rq;  // N / (gridDim.x * 4)
-    int rr;      // N % (gridDim.x * 4)
-};
-
-__device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int nwaves, int fnum,
-                                          int64_t &begin, int &count)
-{
-    const int slot = blockIdx.x * 4 + (wave & 3);
-    const int h = wave >> 2;
-    const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
-    const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
-    // two waves per SIMD: the older one (h = 0) takes the first fnum/16 of the slot's rows
-    const int64_t mid = nwaves == 8 ? (cnt * fnum + 8) >> 4 : cnt;
-    const int64_t b0 = h ? mid : 0;
-    const int64_t b1 = h ? cnt : mid;
-    count = (int)(b1 - b0);
-    // an empty range may start at N; its (unused, clamped) prefetch must still address a real row
-    begin = min(s0 + b0, N - 1);
-}
-
-static RowSplit row_split(int64_t N, int grid)
-{
-    const int64_t S = (int64_t)grid * 4;
-    return RowSplit{N / S, (int)(N % S)};
-}
 
 // General kernel, fp32 x staged in LDS. A wave walks its rows R at a time; for each group, lane l
 // takes blocks l, l+64, ... of the R rows (an "item" is one 64-block slice of R rows). Items go

@@ -7,6 +7,8 @@
  *                    "Value", "Reference quantizer", "Validation".
  *   NVFP4 (W4A16)    "Quantisation and profiles", sections "NVFP4" and "The clip search";
  *                    NInfer "tensor formats", section 3.3 (E2M1 and E4M3FN words, validity).
+ *   row-scaled E4M3  NInfer "tensor formats", section 3.4 (FP8_E4M3FN_ROW_BF16S);
+ *                    "Quantisation and profiles", "The FP8 head".
  *
  * Conventions for every entry point:
  *   - Every pointer argument that names a tensor is a DEVICE pointer, owned by the caller. The
@@ -142,6 +144,40 @@ int pn_nvfp4_global_scale(const float *w, int64_t count, float *g_out, void *str
  * fp64 in the order stated, so these rules fix every output bit. */
 int pn_nvfp4_quantize_rows(const float *w, int64_t N, int64_t K, const float *g_dev,
                            uint8_t *codes, uint8_t *scales, void *stream);
+
+/* ---- Row-scaled E4M3FN (FP8_E4M3FN_ROW_BF16S) -----------------------------------------------
+ * NInfer "tensor formats", section 3.4: codes uint8[N, K] E4M3FN words (section 3.3), row-major;
+ * one bfloat16 multiplier word per row, scales uint16[N]; w = binary32(e4m3(c) * bf16(s)).
+ * "Quantisation and profiles", "The FP8 head": the output head (248,320 x 5,120) is stored this
+ * way, one scale per vocabulary row. */
+
+/* verdict[n] = 1 iff row n is valid: its multiplier has sign bit 0 and is finite (+0 and positive
+ * subnormals included), no code is a NaN word (0x7F, 0xFF), and a +0 multiplier has only
+ * signed-zero codes (0x00, 0x80). */
+int pn_fp8row_validate_rows(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                            int32_t *verdict, void *stream);
+
+/* out fp32[N, K] = binary32(e4m3(code) * bf16(scale)), bit-exact (NaN words decode to NaN). */
+int pn_fp8row_dequantize_rows(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                              float *out, void *stream);
+
+/* y[m*N + n] = sum_k w[n, k] * x[m*K + k], x fp32[M, K], y fp32[M, N] (overwritten), 1 <= M <= 4,
+ * fp32 accumulation, |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs. K must be a multiple of
+ * 16 (PN_ERR_SHAPE) and codes 16-byte aligned (PN_ERR_ALIGN). Rows are not validated here.
+ * Deterministic. */
+int pn_gemv_fp8row(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                   const float *x, int64_t M, float *y, void *stream);
+
+/* FP8-head quantizer, per row of fp32 w[N, K]: for c = 1.0, 0.95, 0.90 the multiplier word
+ * bf16(c * amax / 448) (nearest, ties to even; skipped when zero or not finite), codes the
+ * nearest E4M3FN words of w / s (ties to the even fraction, saturating at 448, sign kept), the
+ * squared error of the fp32 decode in double -- summed as 64 partials over k = l (mod 64) in
+ * increasing k, then the partials in increasing l -- smallest error wins, ties keep the earlier
+ * multiplier. An all-zero row (or one whose candidates are all skipped) is multiplier +0 with
+ * codes 0x00. status (int32[N], optional) = 1 for a row holding a NaN or infinity (written as the
+ * zero row). Every step runs in fp64 in the order stated, so these rules fix every output bit. */
+int pn_fp8row_quantize_rows(const float *w, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,
+                            int32_t *status, void *stream);
 
 #ifdef __cplusplus
 }
