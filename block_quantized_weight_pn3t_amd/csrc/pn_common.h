@@ -64,6 +64,22 @@ __device__ __forceinline__ uint32_t block_word(const RawBlock &rb, int i)
     return __builtin_amdgcn_alignbit(hi, rb.dw[i], rb.shift);
 }
 
+// Non-temporal (streaming) loads, for data that one load instruction consumes whole: each cache line
+// is requested once, so marking it for early eviction loses nothing and keeps the caches for x.
+// (The PN block reader does not use them: its three loads per block share cache lines.)
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt16(const void *p)
+{
+    const u32x4v t = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 load_nt8(const void *p)
+{
+    const u32x2v t = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(p));
+    return make_uint2(t.x, t.y);
+}
+
 // The fp16 scale d of the block in the low 16 bits (upper bits undefined).
 __device__ __forceinline__ uint32_t block_d_bits(const RawBlock &rb)
 {

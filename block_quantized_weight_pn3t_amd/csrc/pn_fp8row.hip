@@ -14,7 +14,8 @@
 //    consecutive chunks hit 8 distinct bank groups. Its loads are issued before the first weight
 //    loads (the memory counter retires loads in order, so waiting for x never waits for weights).
 //  * A wave takes its rows R at a time; lane l owns the 16-byte code chunks l, l + 64, ... of the
-//    phase ("items" of 64 chunks), streamed through a ring of D items. Per chunk and row: 8
+//    phase ("items" of 64 chunks), streamed through a ring of D items with non-temporal loads
+//    (every chunk is read once: 6.7 TB/s against 5.6 with ordinary loads on the head at M = 1). Per chunk and row: 8
 //    v_cvt_pk_f32_fp8 (two exact E4M3FN values each) and 16 FMA per token, x read from LDS once
 //    for the R rows.
 //  * Per group: a transposed permlane/DPP reduction of the R x M partial sums, times the row's
@@ -155,7 +156,7 @@ __global__ void __launch_bounds__(512) fp8row_gemv_kernel(const uint8_t *__restr
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 const int row = min(g * R + r, max(nrows - 1, 0));
-                buf[r] = *reinterpret_cast<const uint4 *>(wbase + (int64_t)row * K + 16 * j);
+                buf[r] = load_nt16(wbase + (int64_t)row * K + 16 * j);
             }
         };
         uint4 buf[D][R];
@@ -245,6 +246,92 @@ __global__ void __launch_bounds__(512) fp8row_gemv_kernel(const uint8_t *__restr
                 load_item(buf[(s + D - 1) % D], it + D - 1);
                 if (it < nitems)
                     compute_item(buf[s], it);
+            }
+        }
+    }
+}
+
+// One token, rows of at most 1024*CPL codes (CPL <= 5: registers): x in registers. Lane l owns chunks l, l + 64, ...,
+// l + 64*(CPL-1) of every row (its 16*CPL x values live in VGPRs: no LDS, no barrier), and each
+// wave streams its contiguous row range front to back (the access pattern of a plain copy) through
+// a ring of D rows; partial sums of 4 rows are reduced together (transposed reduction), times
+// each row's multiplier.
+template <int CPL, int D>
+__global__ void __launch_bounds__(512) fp8row_gemv_xreg_kernel(const uint8_t *__restrict__ codes,
+                                                               const uint16_t *__restrict__ scales,
+                                                               int64_t N, int64_t K,
+                                                               const float *__restrict__ x,
+                                                               float *__restrict__ y, RowSplit sp,
+                                                               int fnum)
+{
+    static_assert(D % 4 == 0, "ring size must be a multiple of the rows per reduction");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t r_begin;
+    int nrows;
+    wave_rows(N, sp, wave, 8, fnum, r_begin, nrows);
+    const int last = max(nrows - 1, 0);
+    const int nch = (int)(K >> 4);
+
+    // x of this lane's chunks (clamped past the row's end; their products are dropped)
+    float xr[CPL][16];
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int j = min(lane + 64 * i, nch - 1);
+        const float4 *src = reinterpret_cast<const float4 *>(x + 16 * (int64_t)j);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float4 t = src[q];
+            xr[i][4 * q + 0] = t.x;
+            xr[i][4 * q + 1] = t.y;
+            xr[i][4 * q + 2] = t.z;
+            xr[i][4 * q + 3] = t.w;
+        }
+    }
+
+    const uint8_t *wbase = codes + r_begin * K;
+    auto load_row = [&](uint4 (&rb)[CPL], int it) {
+        const uint8_t *rp = wbase + (int64_t)min(it, last) * K;
+#pragma unroll
+        for (int i = 0; i < CPL; i++)
+            rb[i] = load_nt16(rp + 16 * (int64_t)min(lane + 64 * i, nch - 1));
+    };
+    uint4 buf[D][CPL];
+#pragma unroll
+    for (int p = 0; p < D - 1; p++)
+        load_row(buf[p], p);
+
+    float vals[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it0 = 0; it0 < nrows; it0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; s++) {
+            const int it = it0 + s;
+            load_row(buf[(s + D - 1) % D], it + D - 1);
+            if (it < nrows) {
+                float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                for (int i = 0; i < CPL; i++) {
+                    float c0 = 0.0f, c1 = 0.0f;
+                    chunk_fma(buf[s][i], xr[i], c0, c1);
+                    // selected, not multiplied by a mask: clamped chunks stay out
+                    const bool ok = lane + 64 * i < nch;
+                    a0 += ok ? c0 : 0.0f;
+                    a1 += ok ? c1 : 0.0f;
+                }
+                const int slot = s & 3;
+                vals[slot] = a0 + a1;
+                if (slot == 3 || it == nrows - 1) {
+                    float tot[1];
+                    transpose_reduce<4>(vals, tot);
+                    if ((lane & 15) == 0) {
+                        const int jr = lane >> 4;
+                        if (jr <= slot) {
+                            const int64_t row = r_begin + it - slot + jr;
+                            y[row] = bf16_bits_to_f32(scales[row]) * tot[0];
+                        }
+                    }
+                    vals[0] = vals[1] = vals[2] = vals[3] = 0.0f;
+                }
             }
         }
     }
@@ -393,11 +480,11 @@ static int fp8_num_cus()
     return cus;
 }
 
-template <int M, int QX>
+template <int M, int QX, int D>
 static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                               const float *x, float *y, hipStream_t s)
 {
-    constexpr int R = 2, D = 4;
+    constexpr int R = 2;
     auto kern = fp8row_gemv_kernel<M, R, D, QX>;
     static bool attr_set = false;
     if (!attr_set) {
@@ -413,9 +500,26 @@ static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int6
     const size_t lds = (size_t)M * phase_ch * kChunkStride * sizeof(float);
     const int grid = (int)std::min<int64_t>(fp8_num_cus(), (N + 3) / 4);
     const char *e = getenv("PN_GEMV_SPLIT");
-    const int fnum = e ? std::max(4, std::min(15, atoi(e))) : 12;
+    const int fnum = e ? std::max(4, std::min(15, atoi(e))) : 8;  // measured best here
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, codes, scales, N, K, x, y,
                        row_split(N, grid), fnum, phase_ch, aligned(x, 16) ? 1 : 0);
+    return launch_status();
+}
+
+template <int CPL>
+static int launch_fp8row_xreg(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                              const float *x, float *y, hipStream_t s)
+{
+    const int grid = (int)std::min<int64_t>(fp8_num_cus(), (N + 3) / 4);
+    const char *e = getenv("PN_GEMV_SPLIT");
+    const int fnum = e ? std::max(4, std::min(15, atoi(e))) : 12;
+    const char *d = getenv("PN_FP8ROW_DEPTH");  // ring of 8 rows (registers allow it up to CPL 4)
+    if (CPL <= 4 && d && atoi(d) >= 8)
+        hipLaunchKernelGGL((fp8row_gemv_xreg_kernel<CPL, 8>), dim3((unsigned)grid), dim3(512), 0, s,
+                           codes, scales, N, K, x, y, row_split(N, grid), fnum);
+    else
+        hipLaunchKernelGGL((fp8row_gemv_xreg_kernel<CPL, 4>), dim3((unsigned)grid), dim3(512), 0, s,
+                           codes, scales, N, K, x, y, row_split(N, grid), fnum);
     return launch_status();
 }
 
@@ -477,11 +581,19 @@ extern "C" int pn_gemv_fp8row(const uint8_t *codes, const uint16_t *scales, int6
         return st;
     hipStream_t s = (hipStream_t)stream;
     // float4 x loads per thread for one phase: M * min(K/16, 512) * 4 / 512
+    // one token, K <= 5120, x 16-byte aligned: x in registers (PN_GEMV_NO_XREG selects the LDS
+    // kernel, for tests)
+    const int64_t nch = K >> 4;
+    if (M == 1 && nch <= 64 * 5 && aligned(x, 16) && !getenv("PN_GEMV_NO_XREG")) {
+        return nch <= 64 * 2   ? launch_fp8row_xreg<2>(codes, scales, N, K, x, y, s)
+               : nch <= 64 * 4 ? launch_fp8row_xreg<4>(codes, scales, N, K, x, y, s)
+                               : launch_fp8row_xreg<5>(codes, scales, N, K, x, y, s);
+    }
     switch (M) {
-    case 1: return launch_fp8row_gemv<1, 4>(codes, scales, N, K, x, y, s);
-    case 2: return launch_fp8row_gemv<2, 8>(codes, scales, N, K, x, y, s);
-    case 3: return launch_fp8row_gemv<3, 12>(codes, scales, N, K, x, y, s);
-    default: return launch_fp8row_gemv<4, 16>(codes, scales, N, K, x, y, s);
+    case 1: return launch_fp8row_gemv<1, 4, 4>(codes, scales, N, K, x, y, s);
+    case 2: return launch_fp8row_gemv<2, 8, 4>(codes, scales, N, K, x, y, s);
+    case 3: return launch_fp8row_gemv<3, 12, 4>(codes, scales, N, K, x, y, s);
+    default: return launch_fp8row_gemv<4, 16, 4>(codes, scales, N, K, x, y, s);
     }
 }
 

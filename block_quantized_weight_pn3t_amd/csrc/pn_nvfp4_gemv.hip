@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(512) nvfp4_gemv_xreg_kernel(const uint8_t *__r
 #pragma unroll
         for (int i = 0; i < GPL; i++) {
             const int j = min(lane + 64 * i, ng - 1);
-            rw.c[i] = *reinterpret_cast<const uint2 *>(cp + 8 * (int64_t)j);
+            rw.c[i] = load_nt8(cp + 8 * (int64_t)j);  // each 8-byte piece is read once
             rw.s[i] = sc[j];
         }
     };

@@ -129,6 +129,17 @@ def test_gemv(env, M, N, K):
         assert_within(gemv(pn, torch, dev, codes, scales, N, K, x, off), y_ref, bound)
 
 
+@pytest.mark.parametrize("N,K", [(37, 1040), (300, 5120)])
+def test_gemv_lds_kernel_one_token(env, monkeypatch, N, K):
+    """At one token the x-in-registers kernel is the default; the LDS kernel, forced."""
+    pn, torch, dev = env
+    monkeypatch.setenv("PN_GEMV_NO_XREG", "1")
+    _, codes, scales = head_like(N, K, 325 + K % 13)
+    x = synth.activations(326, 1, K)
+    y_ref, bound = oracle.fp8row_gemv(codes, scales, N, K, x)
+    assert_within(gemv(pn, torch, dev, codes, scales, N, K, x), y_ref, bound)
+
+
 def test_gemv_one_hot_exact(env):
     pn, torch, dev = env
     N, K = 70, 2048
