@@ -19,7 +19,8 @@ __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_ro
 PN3T = 124
 PN4T = 125
 GROUP = {PN3T: 80, PN4T: 64}
-MAX_TOKENS = 4
+MAX_TOKENS = 4         # NVFP4 and row-scaled E4M3 GEMV
+GEMV_MAX_TOKENS = 16   # PN GEMV
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpn.so")

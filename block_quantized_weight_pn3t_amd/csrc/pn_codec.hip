@@ -176,7 +176,7 @@ const char *pn_status_string(int status)
     case PN_OK: return "ok";
     case PN_ERR_TYPE: return "unknown PN type";
     case PN_ERR_SHAPE: return "K is not a positive whole number of blocks (or a size is negative)";
-    case PN_ERR_TOKENS: return "token count M outside 0..4";
+    case PN_ERR_TOKENS: return "token count M out of range (0..16 for PN, 0..4 for NVFP4 and row-scaled E4M3)";
     case PN_ERR_NULL: return "required pointer is NULL";
     case PN_ERR_ALIGN: return "pointer misaligned";
     case PN_ERR_HIP: return "HIP runtime error";

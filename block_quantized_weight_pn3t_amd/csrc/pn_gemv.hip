@@ -1116,6 +1116,9 @@ static int ring_depth()
     return (e && atoi(e) >= 8) ? 8 : 4;
 }
 
+int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
+                int cus, hipStream_t s);
+
 template <int TYPE>
 static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
                       hipStream_t s)
@@ -1137,9 +1140,15 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
         if (flat && (st = launch_flat<TYPE, 2>(W, N, K, x, y, s)) != kNotApplicable)
             return st;
         return launch_lds<TYPE, 2, 2, 2>(W, N, K, x, y, s);
-    case 3: return launch_lds<TYPE, 3, 1, 2>(W, N, K, x, y, s);
-    default: return launch_lds<TYPE, 4, 2, 2>(W, N, K, x, y, s);
+    default: break;
     }
+    // five or more tokens: the matrix-core path (its own file). At three and four the vector-unit
+    // kernel is faster for now; PN_GEMV_MFMA takes them to the matrix cores too (tests, timing).
+    if (M > 4 || getenv("PN_GEMV_MFMA"))
+        return launch_mfma(TYPE, W, N, K, x, (int)M, y, num_cus(), s);
+    if (M == 3)
+        return launch_lds<TYPE, 3, 1, 2>(W, N, K, x, y, s);
+    return launch_lds<TYPE, 4, 2, 2>(W, N, K, x, y, s);
 }
 
 }  // namespace pn
@@ -1153,7 +1162,7 @@ extern "C" int pn_gemv(int type, const void *W, int64_t N, int64_t K, const floa
         return PN_ERR_TYPE;
     if (N < 0 || pn_row_bytes(type, K) == 0)
         return PN_ERR_SHAPE;
-    if (M < 0 || M > PN_MAX_TOKENS)
+    if (M < 0 || M > PN_GEMV_MAX_TOKENS)
         return PN_ERR_TOKENS;
     if (N == 0 || M == 0)
         return PN_OK;

@@ -45,7 +45,7 @@ enum {
     PN_OK = 0,
     PN_ERR_TYPE = -1,   /* type is neither PN_TYPE_PN3T nor PN_TYPE_PN4T */
     PN_ERR_SHAPE = -2,  /* K is not a positive whole number of blocks, or a size is negative */
-    PN_ERR_TOKENS = -3, /* M (tokens) outside 0..4 */
+    PN_ERR_TOKENS = -3, /* M (tokens) outside 0..16 (PN GEMV) or 0..4 (NVFP4, row-scaled E4M3) */
     PN_ERR_NULL = -4,   /* a required pointer is NULL */
     PN_ERR_ALIGN = -5,  /* W not 2-byte aligned, x / y / w not 4-byte aligned, bf16 x not 2-byte,
                            NVFP4 codes not 8-byte aligned */
@@ -54,7 +54,8 @@ enum {
 };
 
 /* Maximum tokens per GEMV call. */
-#define PN_MAX_TOKENS 4
+#define PN_MAX_TOKENS 4        /* NVFP4 and row-scaled E4M3 GEMV */
+#define PN_GEMV_MAX_TOKENS 16  /* PN GEMV */
 
 /* Bytes of one PN row of K weights: 34*K/80 (pn3t) or 34*K/64 (pn4t); 0 if K is not a positive
  * multiple of the block size or type is unknown. Host-only, no device work. */
@@ -81,17 +82,25 @@ int pn_dequantize_rows(int type, const void *W, int64_t nrows, int64_t K, float 
 int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *stream);
 
 /* ---- PN GEMV -------------------------------------------------------------------------------
- * y[m*N + n] = sum_k w[n, k] * x[m*K + k] for m < M (1 <= M <= 4 tokens), with w the decode above,
+ * y[m*N + n] = sum_k w[n, k] * x[m*K + k] for m < M (1 <= M <= 16 tokens), with w the decode above,
  * accumulated in fp32. x is fp32[M, K] row-major, y fp32[M, N] row-major (overwritten).
- * Accuracy: |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100, under two
- * conditions that activations of ordinary dynamic range meet by a wide margin:
+ * Accuracy: |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100 and
+ * sum_k |w x| >= 2^-126 (below that an fp32 y cannot resolve 1e-5 of the sum), under the
+ * conditions below, which activations of ordinary dynamic range meet by a wide margin:
  *  - The zero point is folded per block, d * (sum n x - z * sum x), with the unsigned codes n, in
- *    fp32 chains of at most 16 terms, so the rounding error scales with a block's sum n|x| rather
+ *    fp32 chains of at most 16 terms (on the matrix cores: one chain of 4-6 MFMA steps per
+ *    block), so the rounding error scales with a block's sum n|x| rather
  *    than its sum |n - z||x|. It stays inside the bound unless, in the blocks that dominate a
  *    row, sum n|x| exceeds about 8 * sum |n - z||x| (a large x meeting a code next to z).
  *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
  *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
  *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
+ *  - M >= 5 runs on the matrix cores and carries each x as an fp16 (hi, lo) pair with one
+ *    exponent per token, chosen from the token's largest |x|: exact to 2^-22 relative or to
+ *    2^-33 (pn3t; 2^-35 pn4t) of that largest |x|, whichever is larger. The bound then needs
+ *    sum_k |w||x| >= 2^-16 * max|x| * sum_k |w| per token and row, i.e. the x that meet a row's
+ *    weights must not all be tiny next to the token's largest |x| -- activations of any ordinary
+ *    shape, outliers included, meet it by orders of magnitude.
  *    Every other path uses x exactly (scaled by powers of two). Rows are not
  * validated here (validate at load); an invalid row gives an unspecified value but no
  * out-of-bounds access. Deterministic: the same inputs and launch give the same bits on every

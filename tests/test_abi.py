@@ -51,7 +51,7 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_gemv(124, fake, 4, 650, fake, 1, fake, None) == -2        # K not whole blocks
     assert L.pn_gemv(124, fake, 4, 0, fake, 1, fake, None) == -2          # K = 0
     assert L.pn_gemv(124, fake, -1, 640, fake, 1, fake, None) == -2       # negative N
-    assert L.pn_gemv(124, fake, 4, 640, fake, 5, fake, None) == -3        # M > 4
+    assert L.pn_gemv(124, fake, 4, 640, fake, 17, fake, None) == -3       # M > 16
     assert L.pn_gemv(124, fake, 4, 640, fake, -1, fake, None) == -3
     assert L.pn_gemv(124, fake, 0, 640, fake, 1, fake, None) == 0         # N = 0: no-op
     assert L.pn_gemv(124, fake, 4, 640, fake, 0, fake, None) == 0         # M = 0: no-op
@@ -63,6 +63,8 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_quantize_rows(124, fake, 2, 81, fake, None, None) == -2
     assert L.pn_gemv_nvfp4(fake, fake, C.c_float(1.0), 4, 24, fake, 1, fake, None) == -2
     assert L.pn_gemv_nvfp4(fake, fake, C.c_float(1.0), 4, 32, fake, 9, fake, None) == -3
+    assert L.pn_gemv_nvfp4(fake, fake, C.c_float(1.0), 4, 32, fake, 5, fake, None) == -3
+    assert L.pn_gemv_fp8row(fake, fake, 4, 32, fake, 5, fake, None) == -3
     assert L.pn_gemv_nvfp4(P(0x1004), fake, C.c_float(1.0), 4, 32, fake, 1, fake, None) == -5
     assert L.pn_nvfp4_validate_rows(fake, C.c_float(1.0), 4, 8, fake, None) == -2
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):

@@ -273,7 +273,7 @@ def test_empty_inputs_are_noops(env):
     with pytest.raises(pn.PNError):
         pn.gemv(PN3T, Wd, 8, 650, x, y)
     with pytest.raises(pn.PNError):
-        pn.gemv(PN3T, Wd, 8, 640, x, y, M=5)
+        pn.gemv(PN3T, Wd, 8, 640, x, y, M=17)  # rejected by the host check, before any launch
 
 
 def test_invalid_rows_are_memory_safe(env):
