@@ -11,15 +11,18 @@
 //
 //  * A masked 16-bit half that holds a code n at bit p (p <= 6 for pn3t, <= 4 for pn4t) reads as
 //    the fp16 subnormal n * 2^(p-24), exactly. So `word & 0x00070007` (and its shifted masks) is a
-//    pair of fp16 operands with no conversion: one AND per two weights. These are the B operand
-//    of v_mfma_f32_16x16x32_f16 (k = code position, n = output row), 16 rows per tile.
-//  * x is the A operand (rows = tokens). It is staged in LDS once per workgroup as an fp16 (hi, lo)
-//    pair x * 2^(E + 24 - p) per code position; hi and lo are fed as two MFMAs on the same codes,
-//    so the sum of both is ~22-bit exact x. E is one exponent per token (and phase) chosen from
-//    the largest |x| so that hi stays below 2^15.
-//  * Each block's MFMA chain starts from C = -z * 2^E * sum(x of the block), so the chain ends at
-//    2^E * sum (n - z) x for the block's 16 rows x 16 token slots, and one FMA per token adds
-//    d * chain into the row's sum. The block's scale d therefore never meets a code in fp16.
+//    pair of fp16 operands with no conversion, and one packed fp16 add of -z * 2^(p-24) makes it
+//    (n - z) * 2^(p-24), still exact: two instructions per two weights. These are the B operand
+//    of v_mfma_f32_16x16x32_f16 (k = code position, n = output row), 16 rows per tile. Taking z
+//    off each code (instead of folding d * (sum n x - z sum x)) leaves no cancellation for the
+//    matrix cores' accumulation to round.
+//  * x is the A operand (rows = tokens), staged in LDS once per workgroup as an fp16 (hi, lo) pair
+//    x * 2^(E + 24 - p) per code position, E one exponent per block and token chosen from the
+//    block's largest |x| so that hi stays below 2^15: the sum of hi and lo is ~22-bit exact x. Up
+//    to 8 tokens, hi and lo are two token slots of one operand; up to 16, two operands.
+//  * Each block's chain gives 2^E * sum (n - z) x for 16 rows x 16 token slots; one multiply by
+//    d and one exact 2^-E scaling per token add it into the row's sum. The block's scale d never
+//    meets a code in fp16.
 //
 // Operand layout (measured on gfx950 with a one-wave probe): for 16x16x32, lane l holds
 // A[l % 16][8 (l / 16) + j] and B[8 (l / 16) + j][l % 16] for j < 8, and the result
@@ -29,27 +32,29 @@
 // tokens 4g..4g+3 of row n.
 //
 // Work split: one workgroup of 8 waves per CU owns a contiguous range of rows (tiles of 16, the
-// last one masked). The 8 waves split the blocks of every tile; a wave walks its blocks in order
-// and, for each block, all tiles of its group, so each x operand is read from LDS once per block.
-// Partial sums meet in LDS at the end and are added in wave order: deterministic. x larger than
-// LDS is staged in phases of blocks; a later phase may only lower the exponent (the running sums
-// are rescaled by a power of two), so nothing overflows.
+// last one masked). Its 8 waves split the (tile, block) work of each phase of x; partial sums
+// meet in LDS at the end and are added in wave order: deterministic. x larger than LDS is staged
+// in phases of blocks. Two kernels: one stages the weights through LDS with whole-line copies
+// (W 16-byte aligned, rows of a multiple of 8 blocks), the other reads each lane's bytes directly
+// (any 2-byte aligned W and block count).
 #include "pn_common.h"
 
 namespace pn {
 
 typedef float mf_f4 __attribute__((ext_vector_type(4)));
+
+bool mfma_stages_weights(int type, const void *W, int64_t K);
 typedef uint32_t mf_u2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 template <int TYPE> struct MTile;
 template <> struct MTile<PN_TYPE_PN3T> {
-    static constexpr int G = 80, PERG = 20, CHUNKS = 6, Z = 4;
+    static constexpr int G = 80, PERG = 20, KSTEPS = 3, Z = 4;
     // bit position (after the decode's one shift) of code kl of a lane's 20: pairs t = 0..9 of a
     // word sit at 0, 3, 6 and, after >> 9, at 0, 3
     static constexpr int pe(int kl) { return 3 * ((((kl % 10) >> 1)) % 3); }
 };
 template <> struct MTile<PN_TYPE_PN4T> {
-    static constexpr int G = 64, PERG = 16, CHUNKS = 4, Z = 8;
+    static constexpr int G = 64, PERG = 16, KSTEPS = 2, Z = 8;
     // pairs t = 0..7 of a word sit at 0, 4 and, after >> 8, at 0, 4
     static constexpr int pe(int kl) { return ((kl >> 1) & 1) * 4; }
 };
@@ -81,20 +86,37 @@ __device__ __forceinline__ void mfma_issue(const uint8_t *rowp, int b, int g, Mf
     r.sh = mis << 3;
 }
 
-// The lane's two words as MFMA B operands (fp16 subnormal code pairs, see the file comment).
+// A masked pair of codes n at bit p (fp16 subnormals n 2^(p-24)) plus the pair (-z 2^(p-24)):
+// (n - z) 2^(p-24), exactly (every value stays on the subnormal grid). The zero point is thus
+// taken off each code before the matrix cores, and no sum of large terms cancels afterwards.
+typedef _Float16 mf_h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t minus_z(uint32_t pair, uint32_t negz)
+{
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_bit_cast(mf_h2, pair) + __builtin_bit_cast(mf_h2, negz));
+}
+
+// The lane's two words as MFMA B operands: fp16 subnormal pairs (n - z) 2^(p-24).
 template <int TYPE> struct MfmaB;
 template <> struct MfmaB<PN_TYPE_PN3T> {
     u32x4v b0, b1, b2;
     __device__ __forceinline__ void decode(const MfmaRaw &r)
     {
-        const uint32_t w0 = __builtin_amdgcn_alignbit(r.w.y, r.w.x, r.sh);
-        const uint32_t w1 = __builtin_amdgcn_alignbit(r.tail, r.w.y, r.sh);
+        words(__builtin_amdgcn_alignbit(r.w.y, r.w.x, r.sh),
+              __builtin_amdgcn_alignbit(r.tail, r.w.y, r.sh));
+    }
+    __device__ __forceinline__ void words(uint32_t w0, uint32_t w1)
+    {
+        // -z 2^(p-24) for z = 4 at p = 0, 3, 6: fp16 words 0x8004, 0x8020, 0x8100
+        constexpr uint32_t z0 = 0x80048004u, z3 = 0x80208020u, z6 = 0x81008100u;
         const uint32_t s0 = w0 >> 9, s1 = w1 >> 9;
-        b0 = u32x4v{w0 & 0x00070007u, w0 & 0x00380038u, w0 & 0x01C001C0u, s0 & 0x00070007u};
-        b1 = u32x4v{s0 & 0x00380038u, w1 & 0x00070007u, w1 & 0x00380038u, w1 & 0x01C001C0u};
+        b0 = u32x4v{minus_z(w0 & 0x00070007u, z0), minus_z(w0 & 0x00380038u, z3),
+                    minus_z(w0 & 0x01C001C0u, z6), minus_z(s0 & 0x00070007u, z0)};
+        b1 = u32x4v{minus_z(s0 & 0x00380038u, z3), minus_z(w1 & 0x00070007u, z0),
+                    minus_z(w1 & 0x00380038u, z3), minus_z(w1 & 0x01C001C0u, z6)};
         // the last four codes fill half of a 16x16x32 step; the other half meets zero x (any
         // finite code words do), here a copy of the same two
-        const uint32_t v8 = s1 & 0x00070007u, v9 = s1 & 0x00380038u;
+        const uint32_t v8 = minus_z(s1 & 0x00070007u, z0), v9 = minus_z(s1 & 0x00380038u, z3);
         b2 = u32x4v{v8, v9, v8, v9};
     }
 };
@@ -102,15 +124,25 @@ template <> struct MfmaB<PN_TYPE_PN4T> {
     u32x4v b0, b1;
     __device__ __forceinline__ void decode(const MfmaRaw &r)
     {
-        const uint32_t w0 = __builtin_amdgcn_alignbit(r.w.y, r.w.x, r.sh);
-        const uint32_t w1 = __builtin_amdgcn_alignbit(r.tail, r.w.y, r.sh);
+        words(__builtin_amdgcn_alignbit(r.w.y, r.w.x, r.sh),
+              __builtin_amdgcn_alignbit(r.tail, r.w.y, r.sh));
+    }
+    __device__ __forceinline__ void words(uint32_t w0, uint32_t w1)
+    {
+        // -z 2^(p-24) for z = 8 at p = 0, 4: fp16 words 0x8008, 0x8080
+        constexpr uint32_t z0 = 0x80088008u, z4 = 0x80808080u;
         const uint32_t s0 = w0 >> 8, s1 = w1 >> 8;
-        b0 = u32x4v{w0 & 0x000F000Fu, w0 & 0x00F000F0u, s0 & 0x000F000Fu, s0 & 0x00F000F0u};
-        b1 = u32x4v{w1 & 0x000F000Fu, w1 & 0x00F000F0u, s1 & 0x000F000Fu, s1 & 0x00F000F0u};
+        b0 = u32x4v{minus_z(w0 & 0x000F000Fu, z0), minus_z(w0 & 0x00F000F0u, z4),
+                    minus_z(s0 & 0x000F000Fu, z0), minus_z(s0 & 0x00F000F0u, z4)};
+        b1 = u32x4v{minus_z(w1 & 0x000F000Fu, z0), minus_z(w1 & 0x00F000F0u, z4),
+                    minus_z(s1 & 0x000F000Fu, z0), minus_z(s1 & 0x00F000F0u, z4)};
     }
 };
 
-// x operands of one block for lane (token, g): CHUNKS x 16 bytes (hi and lo halves).
+typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+
+// x operands of one block for one lane: SLOT, c[ks] (slot = the lane's token row); K-split,
+// c[2 ks + h]. The upper half of pn3t's last step stays zero.
 struct MfmaA {
     u32x4v c[6];
 };
@@ -158,6 +190,97 @@ __device__ __forceinline__ mf_f4 mfma_block<PN_TYPE_PN4T>(const MfmaA &a,
     return c;
 }
 
+// Two blocks of one 16-row tile at once: two independent chains interleaved (each step depends
+// on the one two steps back), in place, with the same explicit independent cycles as mfma_block.
+// SLOT: one A operand per k-step (hi and lo in token slots). K-split: hi and lo A operands.
+template <int TYPE, bool SLOT> struct MfmaPair;
+template <> struct MfmaPair<PN_TYPE_PN3T, true> {
+    static __device__ __forceinline__ void run(mf_f4 &c0, mf_f4 &c1, const MfmaA &a0,
+                                               const MfmaA &a1, const MfmaB<PN_TYPE_PN3T> &b0,
+                                               const MfmaB<PN_TYPE_PN3T> &b1)
+    {
+        asm volatile("s_nop 2\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %8, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %3, %9, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %6, %12, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %4, %10, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %7, %13, %1\n\t"
+                     "s_nop 7\n\t"
+                     "s_nop 7"
+                     : "+v"(c0), "+v"(c1)
+                     : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a1.c[0]), "v"(a1.c[1]),
+                       "v"(a1.c[2]), "v"(b0.b0), "v"(b0.b1), "v"(b0.b2), "v"(b1.b0), "v"(b1.b1),
+                       "v"(b1.b2));
+    }
+};
+template <> struct MfmaPair<PN_TYPE_PN4T, true> {
+    static __device__ __forceinline__ void run(mf_f4 &c0, mf_f4 &c1, const MfmaA &a0,
+                                               const MfmaA &a1, const MfmaB<PN_TYPE_PN4T> &b0,
+                                               const MfmaB<PN_TYPE_PN4T> &b1)
+    {
+        asm volatile("s_nop 2\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %6, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %4, %8, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %3, %7, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %5, %9, %1\n\t"
+                     "s_nop 7\n\t"
+                     "s_nop 7"
+                     : "+v"(c0), "+v"(c1)
+                     : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a1.c[0]), "v"(a1.c[1]), "v"(b0.b0),
+                       "v"(b0.b1), "v"(b1.b0), "v"(b1.b1));
+    }
+};
+template <> struct MfmaPair<PN_TYPE_PN3T, false> {
+    static __device__ __forceinline__ void run(mf_f4 &c0, mf_f4 &c1, const MfmaA &a0,
+                                               const MfmaA &a1, const MfmaB<PN_TYPE_PN3T> &b0,
+                                               const MfmaB<PN_TYPE_PN3T> &b1)
+    {
+        asm volatile("s_nop 2\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %14, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %3, %14, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %9, %17, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %4, %15, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %10, %18, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %5, %15, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %11, %18, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %6, %16, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %12, %19, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %7, %16, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %13, %19, %1\n\t"
+                     "s_nop 7\n\t"
+                     "s_nop 7"
+                     : "+v"(c0), "+v"(c1)
+                     : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a0.c[3]), "v"(a0.c[4]),
+                       "v"(a0.c[5]), "v"(a1.c[0]), "v"(a1.c[1]), "v"(a1.c[2]), "v"(a1.c[3]),
+                       "v"(a1.c[4]), "v"(a1.c[5]), "v"(b0.b0), "v"(b0.b1), "v"(b0.b2),
+                       "v"(b1.b0), "v"(b1.b1), "v"(b1.b2));
+    }
+};
+template <> struct MfmaPair<PN_TYPE_PN4T, false> {
+    static __device__ __forceinline__ void run(mf_f4 &c0, mf_f4 &c1, const MfmaA &a0,
+                                               const MfmaA &a1, const MfmaB<PN_TYPE_PN4T> &b0,
+                                               const MfmaB<PN_TYPE_PN4T> &b1)
+    {
+        asm volatile("s_nop 2\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %10, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %6, %12, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %3, %10, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %7, %12, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %4, %11, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %8, %13, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %5, %11, %0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %9, %13, %1\n\t"
+                     "s_nop 7\n\t"
+                     "s_nop 7"
+                     : "+v"(c0), "+v"(c1)
+                     : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a0.c[3]), "v"(a1.c[0]),
+                       "v"(a1.c[1]), "v"(a1.c[2]), "v"(a1.c[3]), "v"(b0.b0), "v"(b0.b1),
+                       "v"(b1.b0), "v"(b1.b1));
+    }
+};
+
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi)
 {
     const _Float16 a = (_Float16)lo, b = (_Float16)hi;
@@ -184,33 +307,159 @@ __device__ __forceinline__ void mfma_load_unit(const float *__restrict__ x, int6
     }
 }
 
+// Bytes of one block's x operands in LDS: 16 bytes per (k-step of 8 codes, k-group, slot) for
+// full steps; pn3t's last step of 4 codes takes 8 bytes (its other half is zero in registers).
+// Then 16 exponents (one per token slot).
+template <int TYPE> __host__ __device__ constexpr int mfma_a_bytes(int M)
+{
+    return TYPE == PN_TYPE_PN3T ? 320 * M : 256 * M;
+}
+template <int TYPE> __host__ __device__ constexpr int mfma_block_bytes(int M)
+{
+    return mfma_a_bytes<TYPE>(M) + 64;
+}
+
+// LDS byte offset of the A operand (k-step ks, hi or lo h) of token m in k-group g.
+template <int TYPE, bool SLOT>
+__device__ __forceinline__ int mfma_a_off(int ks, int h, int g, int m, int M)
+{
+    if (ks < 2)
+        return SLOT ? ((ks * 4 + g) * 2 * M + 2 * m + h) * 16
+                    : (((2 * ks + h) * 4 + g) * M + m) * 16;
+    return 256 * M + (SLOT ? (g * 2 * M + 2 * m + h) * 8 : ((h * 4 + g) * M + m) * 8);
+}
+
+// A operands of one block for lane (n16, g) from the x area: SLOT, slot n16 (token n16 / 2, hi or
+// lo by parity); K-split, token n16, hi and lo.
+template <int TYPE, bool SLOT>
+__device__ __forceinline__ void mfma_read_a(MfmaA &a, const uint8_t *blk, int g, int n16, int M)
+{
+    const int m = SLOT ? n16 >> 1 : n16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int h = 0; h < (SLOT ? 1 : 2); h++)
+            a.c[SLOT ? ks : 2 * ks + h] = *reinterpret_cast<const u32x4v *>(
+                blk + mfma_a_off<TYPE, SLOT>(ks, SLOT ? (n16 & 1) : h, g, m, M));
+    if constexpr (MTile<TYPE>::KSTEPS == 3) {
+#pragma unroll
+        for (int h = 0; h < (SLOT ? 1 : 2); h++) {
+            const u32x2v v = *reinterpret_cast<const u32x2v *>(
+                blk + mfma_a_off<TYPE, SLOT>(2, SLOT ? (n16 & 1) : h, g, m, M));
+            a.c[SLOT ? 2 : 4 + h].x = v.x;
+            a.c[SLOT ? 2 : 4 + h].y = v.y;
+        }
+    }
+}
+
+// Stages x for the blocks [pb0, pb0 + npb) of a phase into the x area xa (mfma_block_bytes per
+// block). Every thread of the workgroup calls it; it holds two barriers. One unit = one token m,
+// one block, one k-group g: PERG consecutive x values; the four units of a (block, token) sit in
+// one lane quad. Per block and token, the exponent E is chosen from the block's largest |x| (so
+// that |x| * 2^(E + 24) < 2^15) and x * 2^(E + 24 - p) is split into fp16 hi + lo; E is stored
+// beside the operands and undone after the block's MFMA chain.
+// Layout SLOT (up to 8 tokens): hi and lo are token slots 2m, 2m+1 of one A operand, so one MFMA
+// per k-step covers both; K-split (up to 16 tokens): hi and lo are two A operands on the same
+// codes. `first` runs before the x loads are issued (a caller's weight prefetch).
+template <int TYPE, bool SLOT, class F>
+__device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *__restrict__ x, int64_t K,
+                                           int M, int pb0, int npb, int xvec4, F first)
+{
+    using T = MTile<TYPE>;
+    constexpr int PERG = T::PERG;
+    const int tid = threadIdx.x;
+    const int per_block = mfma_block_bytes<TYPE>(M), e_off = mfma_a_bytes<TYPE>(M);
+    const int U = npb * M * 4;
+    const int nch = (U + kMfmaThreads * kMfmaUnits - 1) / (kMfmaThreads * kMfmaUnits);
+    __syncthreads();  // earlier readers of the x area are done
+    first();
+    for (int c = 0; c < nch; c++) {
+        float xr[kMfmaUnits][PERG];
+#pragma unroll
+        for (int ub = 0; ub < kMfmaUnits; ub++) {
+            const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
+            if (u < U) {
+                const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
+                mfma_load_unit<TYPE>(x, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4,
+                                     xr[ub]);
+            }
+        }
+#pragma unroll
+        for (int ub = 0; ub < kMfmaUnits; ub++) {
+            const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
+            if (u < U) {  // U is a multiple of 4: whole quads take this branch
+                const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
+                float mx = 0.f;
+#pragma unroll
+                for (int e = 0; e < PERG; e++)
+                    mx = fmaxf(mx, fabsf(xr[ub][e]));
+                mx = fmaxf(mx, PN_DPP(mx, 0xB1));  // quad_perm [1,0,3,2]
+                mx = fmaxf(mx, PN_DPP(mx, 0x4E));  // quad_perm [2,3,0,1]
+                int ex = 0;
+                frexpf(mx, &ex);
+                const int E = mx > 0.f ? -9 - ex : 0;
+                const int eb = E + 24;
+                uint32_t hw[PERG / 2], lw[PERG / 2];
+#pragma unroll
+                for (int e = 0; e < PERG; e += 2) {
+                    const float v0 = ldexpf(xr[ub][e], eb - T::pe(e));
+                    const float v1 = ldexpf(xr[ub][e + 1], eb - T::pe(e + 1));
+                    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+                    hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    lw[e / 2] = pack_h2(v0 - (float)h0, v1 - (float)h1);
+                }
+                uint8_t *blk = xa + brel * per_block;
+                auto put16 = [&](int ks, int h, u32x4v v) {
+                    *reinterpret_cast<u32x4v *>(blk + mfma_a_off<TYPE, SLOT>(ks, h, gg, m, M)) = v;
+                };
+                put16(0, 0, u32x4v{hw[0], hw[1], hw[2], hw[3]});
+                put16(0, 1, u32x4v{lw[0], lw[1], lw[2], lw[3]});
+                put16(1, 0, u32x4v{hw[4], hw[5], hw[6], hw[7]});
+                put16(1, 1, u32x4v{lw[4], lw[5], lw[6], lw[7]});
+                if constexpr (T::KSTEPS == 3) {  // the last 4 codes
+                    *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 0, gg, m, M)) =
+                        u32x2v{hw[8], hw[9]};
+                    *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 1, gg, m, M)) =
+                        u32x2v{lw[8], lw[9]};
+                }
+                if (gg == 0) {
+                    int *es = reinterpret_cast<int *>(blk + e_off);
+                    if (SLOT)
+                        es[2 * m] = es[2 * m + 1] = E;
+                    else
+                        es[m] = E;
+                }
+            }
+        }
+    }
+    const int used = SLOT ? 2 * M : M;
+    for (int i = tid; i < npb * 16; i += kMfmaThreads)
+        if ((i & 15) >= used)
+            reinterpret_cast<int *>(xa + (i >> 4) * per_block + e_off)[i & 15] = 0;
+    __syncthreads();
+}
+
 template <int TYPE, int TG>
 __global__ void __launch_bounds__(kMfmaThreads)
 pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
                     const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
                     int64_t rq, int rr, int Pb, int nph, int xvec4)
 {
-    using T = MTile<TYPE>;
     constexpr int P = (8 + TG - 1) / TG;  // block steps of loads in flight (about 8 tiles' worth)
-    constexpr int PERG = T::PERG, CH = T::CHUNKS;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ uint32_t smax[2][16];
-    __shared__ int sexp[2][16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
-    const int per_block = 64 * (CH * M + 1);
-    const int zs_off = CH * 64 * M;
+    const int per_block = mfma_block_bytes<TYPE>(M);
+    const int e_off = mfma_a_bytes<TYPE>(M);
 
     const int64_t wg = blockIdx.x;
     const int64_t r0 = wg * rq + (wg < rr ? wg : rr);
     const int64_t r1 = r0 + rq + (wg < rr ? 1 : 0);
     const int ntiles = (int)((r1 - r0 + 15) >> 4);
     const int ngroups = (ntiles + TG - 1) / TG;
-
-    if (tid < 32)
-        (&smax[0][0])[tid] = 0u;
 
     for (int grp = 0; grp < ngroups; grp++) {
         const int t0 = grp * TG;
@@ -228,104 +477,8 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
             acc[t] = mf_f4{0.f, 0.f, 0.f, 0.f};
 
         for (int p = 0; p < nph; p++) {
-            const int q = grp * nph + p;
             const int pb0 = p * Pb, npb = min(nb, pb0 + Pb) - pb0;
-            const int U = npb * M * 4;
-            const int nch = (U + kMfmaThreads * kMfmaUnits - 1) / (kMfmaThreads * kMfmaUnits);
-
-            // ---- stage x for blocks [pb0, pb0 + npb) ----
-            __syncthreads();  // earlier readers of the x area, sexp and smax are done
-            if (tid < 16)
-                smax[(q + 1) & 1][tid] = 0u;
-            float xr[kMfmaUnits][PERG];
-            for (int c = 0; c < nch; c++) {
-#pragma unroll
-                for (int ub = 0; ub < kMfmaUnits; ub++) {
-                    const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
-                    if (u < U) {
-                        const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
-                        mfma_load_unit<TYPE>(x, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg,
-                                             xvec4, xr[ub]);
-                        float mx = 0.f;
-#pragma unroll
-                        for (int e = 0; e < PERG; e++)
-                            mx = fmaxf(mx, fabsf(xr[ub][e]));
-                        atomicMax(&smax[q & 1][m], __float_as_uint(mx));
-                    }
-                }
-            }
-            __syncthreads();
-            if (tid < 16) {
-                const uint32_t mb = smax[q & 1][tid];
-                int E = 1 << 20;  // an all-zero token keeps the previous exponent
-                if (mb != 0u) {
-                    int ex;
-                    frexpf(__uint_as_float(mb), &ex);
-                    E = -9 - ex;  // largest |x| * 2^(E + 24) < 2^15
-                }
-                if (p > 0)
-                    E = min(E, sexp[(q - 1) & 1][tid]);
-                sexp[q & 1][tid] = E;
-            }
-            __syncthreads();
-            for (int c = 0; c < nch; c++) {
-#pragma unroll
-                for (int ub = 0; ub < kMfmaUnits; ub++) {
-                    const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
-                    if (u < U) {  // U is a multiple of 4: whole quads take this branch
-                        const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
-                        if (nch > 1)
-                            mfma_load_unit<TYPE>(x, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg,
-                                                 xvec4, xr[ub]);
-                        const int eb = sexp[q & 1][m] + 24;
-                        uint32_t hw[PERG / 2], lw[PERG / 2];
-                        float s = 0.f;
-#pragma unroll
-                        for (int e = 0; e < PERG; e += 2) {
-                            s += xr[ub][e];
-                            s += xr[ub][e + 1];
-                            const float v0 = ldexpf(xr[ub][e], eb - T::pe(e));
-                            const float v1 = ldexpf(xr[ub][e + 1], eb - T::pe(e + 1));
-                            const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-                            hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                            lw[e / 2] = pack_h2(v0 - (float)h0, v1 - (float)h1);
-                        }
-                        uint8_t *blk = lds + brel * per_block;
-                        auto chunk = [&](int ch) {
-                            return reinterpret_cast<u32x4v *>(blk + ((ch * 4 + gg) * M + m) * 16);
-                        };
-                        *chunk(0) = u32x4v{hw[0], hw[1], hw[2], hw[3]};
-                        *chunk(1) = u32x4v{lw[0], lw[1], lw[2], lw[3]};
-                        *chunk(2) = u32x4v{hw[4], hw[5], hw[6], hw[7]};
-                        *chunk(3) = u32x4v{lw[4], lw[5], lw[6], lw[7]};
-                        if constexpr (CH == 6) {  // the last 4 codes, zero-padded to a full step
-                            *chunk(4) = u32x4v{hw[8], hw[9], 0u, 0u};
-                            *chunk(5) = u32x4v{lw[8], lw[9], 0u, 0u};
-                        }
-                        // sum of the block's x for the zero point: k-groups 0+1, 2+3, then both
-                        s += PN_DPP(s, 0xB1);  // quad_perm [1,0,3,2]
-                        s += PN_DPP(s, 0x4E);  // quad_perm [2,3,0,1]
-                        if (gg == 0)
-                            reinterpret_cast<float *>(blk + zs_off)[m] =
-                                -(float)T::Z * ldexpf(s, sexp[q & 1][m]);
-                    }
-                }
-            }
-            for (int i = tid; i < npb * 16; i += kMfmaThreads)
-                if ((i & 15) >= M)
-                    reinterpret_cast<float *>(lds + (i >> 4) * per_block + zs_off)[i & 15] = 0.f;
-            __syncthreads();
-
-            if (p > 0) {  // the running sums move to this phase's (lower or equal) exponent
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int dE = sexp[q & 1][4 * g + j] - sexp[(q - 1) & 1][4 * g + j];
-#pragma unroll
-                    for (int t = 0; t < TG; t++)
-                        acc[t][j] = ldexpf(acc[t][j], dE);
-                }
-            }
+            mfma_stage<TYPE, false>(lds, x, K, M, pb0, npb, xvec4, [] {});
 
             // ---- this wave's blocks of the phase, every tile of the group ----
             const int kb0 = pb0 + (wave * npb) / kMfmaWaves;
@@ -351,13 +504,10 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
                         const int st = i + s;
                         const int brel = min(st, ns - 1) + kb0 - pb0;
                         const uint8_t *blk = lds + brel * per_block;
-                        if (n16 < M) {
-#pragma unroll
-                            for (int ch = 0; ch < CH; ch++)
-                                a.c[ch] = *reinterpret_cast<const u32x4v *>(
-                                    blk + ((ch * 4 + g) * M + n16) * 16);
-                        }
-                        const mf_f4 c0 = *reinterpret_cast<const mf_f4 *>(blk + zs_off + 16 * g);
+                        if (n16 < M)
+                            mfma_read_a<TYPE, false>(a, blk, g, n16, M);
+                        const mf_f4 c0 = {0.f, 0.f, 0.f, 0.f};
+                        const i32x4v ex = *reinterpret_cast<const i32x4v *>(blk + e_off + 16 * g);
                         const int nxt = kb0 + min(st + P, ns - 1);
                         // No branch around the use of a ring slot: a step past the wave's last
                         // block or a tile past the group's last one is computed on clamped (valid)
@@ -375,7 +525,7 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
                             const mf_f4 dd = mfma_block<TYPE>(a, bop, c0);
 #pragma unroll
                             for (int j = 0; j < 4; j++)
-                                acc[t][j] = fmaf(dv, dd[j], acc[t][j]);
+                                acc[t][j] += ldexpf(dv * dd[j], -ex[j]);
                         }
                     }
                 }
@@ -389,7 +539,6 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
         for (int t = 0; t < TG; t++)
             red[(t * kMfmaWaves + wave) * 64 + lane] = acc[t];
         __syncthreads();
-        const int ql = (grp * nph + nph - 1) & 1;
         for (int i = tid; i < gt * 64; i += kMfmaThreads) {
             const int t = i >> 6, l = i & 63;
             mf_f4 s = red[(t * kMfmaWaves) * 64 + l];
@@ -402,7 +551,183 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
                 for (int j = 0; j < 4; j++) {
                     const int m = 4 * (l >> 4) + j;
                     if (m < M)
-                        y[(int64_t)m * N + row] = ldexpf(s[j], -sexp[ql][m]);
+                        y[(int64_t)m * N + row] = s[j];
+                }
+            }
+        }
+    }
+}
+
+// ---- weights staged through LDS: 16 rows x 8 blocks per wave and step --------------------------
+//
+// Rows of a multiple of 8 blocks are 16-byte aligned when W is (8 * 34 = 272 = 17 * 16). A wave
+// then copies 16 rows x 8 blocks (4352 bytes) straight from HBM into a private LDS slot with
+// 16-byte loads that fill whole lines (global_load_lds_dwordx4: 4 wave loads + 16 lanes), and
+// each lane reads its two words per block from there. The direct loads of the general kernel
+// above touch 16-20 cache lines for 512 bytes per instruction; these touch about 12 per 1 KB.
+// The slot is double-buffered: the next step's copy is in flight while this one is computed.
+// The waits on the copies are explicit (the compiler does not order LDS reads after them).
+constexpr int kChunkBytes = 16 * 8 * kBlockBytes;  // 4352
+constexpr int kLdsRing = 2;                         // slots per wave
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int TYPE, int TG, bool SLOT>
+__global__ void __launch_bounds__(kMfmaThreads)
+pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
+                        const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
+                        int64_t rq, int rr, int Pb, int nph, int xvec4)
+{
+    constexpr int ACC = SLOT ? 2 : 4;       // tokens per lane
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int per_block = mfma_block_bytes<TYPE>(M);
+    const int e_off = mfma_a_bytes<TYPE>(M);
+    const int alim = SLOT ? 2 * M : M;  // lanes (by n16) that hold A operands
+    uint8_t *const ring = lds + wave * kLdsRing * kChunkBytes;
+    uint8_t *const xa = lds + kMfmaWaves * kLdsRing * kChunkBytes;
+
+    const int64_t wg = blockIdx.x;
+    const int64_t r0 = wg * rq + (wg < rr ? wg : rr);
+    const int64_t r1 = r0 + rq + (wg < rr ? 1 : 0);
+    const int ntiles = (int)((r1 - r0 + 15) >> 4);
+    const int ngroups = (ntiles + TG - 1) / TG;
+
+    // This lane's 16-byte pieces of a step: piece 64 j + lane is row (piece / 17), column
+    // (piece % 17); j = 4 only for lanes < 16 (272 pieces).
+    int prow[5], pcol[5];
+#pragma unroll
+    for (int j = 0; j < 5; j++) {
+        const int pc = 64 * j + lane;
+        prow[j] = pc / 17;
+        pcol[j] = pc % 17;
+    }
+    auto issue = [&](int tile, int c8, int slot) {  // tile: index within the workgroup
+        uint8_t *dst = ring + slot * kChunkBytes;
+#pragma unroll
+        for (int j = 0; j < 5; j++) {
+            if (j < 4 || lane < 16) {
+                int64_t r = r0 + 16 * (int64_t)tile + prow[j];
+                r = r < r1 ? r : r1 - 1;
+                const uint8_t *src = W + r * row_bytes + (int64_t)c8 * (8 * kBlockBytes) + 16 * pcol[j];
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(dst + 1024 * j), 16, 0, 0);
+            }
+        }
+    };
+
+    MfmaA a0, a1;
+#pragma unroll
+    for (int ch = 0; ch < 6; ch++)
+        a0.c[ch] = a1.c[ch] = u32x4v{0u, 0u, 0u, 0u};
+
+    for (int grp = 0; grp < ngroups; grp++) {
+        const int t0 = grp * TG;
+        const int gt = min(TG, ntiles - t0);
+        float acc[TG][ACC];
+#pragma unroll
+        for (int t = 0; t < TG; t++)
+#pragma unroll
+            for (int j = 0; j < ACC; j++)
+                acc[t][j] = 0.f;
+
+        for (int p = 0; p < nph; p++) {
+            const int pb0 = p * Pb, npb = min(nb, pb0 + Pb) - pb0;  // both multiples of 8
+            const int n8 = npb >> 3, c80 = pb0 >> 3;
+            // items (tile, 8-block step), tile-major, split evenly over the 8 waves
+            const int items = gt * n8;
+            const int i0 = (wave * items) / kMfmaWaves, i1 = ((wave + 1) * items) / kMfmaWaves;
+            mfma_stage<TYPE, SLOT>(xa, x, K, M, pb0, npb, xvec4, [&] {
+                if (i0 < i1)
+                    issue(t0 + i0 / n8, c80 + i0 % n8, i0 % kLdsRing);
+            });
+#pragma unroll
+            for (int t = 0; t < TG; t++) {
+                const int lo = max(i0, t * n8), hi = min(i1, (t + 1) * n8);
+                for (int it = lo; it < hi; it++) {
+                    // refill the other slot, then wait for this step's copy (loads retire in
+                    // order: at most the 5 just issued may stay outstanding)
+                    asm volatile("" ::: "memory");  // this slot's earlier reads stay before
+                    if (it + 1 < i1) {
+                        issue(t0 + (it + 1) / n8, c80 + (it + 1) % n8, (it + 1) % kLdsRing);
+                        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+                    } else {
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    }
+                    const uint8_t *cr = ring + (it % kLdsRing) * kChunkBytes + 272 * n16;
+                    const uint8_t *cw = cr + 8 * g;
+                    const uint8_t *xb = xa + ((it % n8) * 8) * per_block;
+#pragma unroll
+                    for (int jp = 0; jp < 4; jp++) {
+                        // block 2jp: words 2 mod 4 aligned (read 12 bytes from 2 before);
+                        // block 2jp+1: words 4-byte aligned
+                        const int j0 = 2 * jp, j1 = 2 * jp + 1;
+                        const uint32_t *e = reinterpret_cast<const uint32_t *>(cw + 34 * j0);
+                        const uint32_t *o = reinterpret_cast<const uint32_t *>(cw + 34 * j1 + 2);
+                        const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], o0 = o[0], o1 = o[1];
+                        const float d0 = f16_bits_to_f32(
+                            *reinterpret_cast<const uint16_t *>(cr + 34 * j0));
+                        const float d1 = f16_bits_to_f32(
+                            *reinterpret_cast<const uint16_t *>(cr + 34 * j1));
+                        const uint8_t *x0 = xb + j0 * per_block, *x1 = xb + j1 * per_block;
+                        if (n16 < alim) {
+                            mfma_read_a<TYPE, SLOT>(a0, x0, g, n16, M);
+                            mfma_read_a<TYPE, SLOT>(a1, x1, g, n16, M);
+                        }
+                        mf_f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                        const i32x4v ex0 = *reinterpret_cast<const i32x4v *>(x0 + e_off + 16 * g);
+                        const i32x4v ex1 = *reinterpret_cast<const i32x4v *>(x1 + e_off + 16 * g);
+                        MfmaB<TYPE> b0, b1;
+                        b0.words(__builtin_amdgcn_alignbit(e1, e0, 16),
+                                 __builtin_amdgcn_alignbit(e2, e1, 16));
+                        b1.words(o0, o1);
+                        MfmaPair<TYPE, SLOT>::run(c0, c1, a0, a1, b0, b1);
+                        // undo the block's exponent: d * chain * 2^-E (the product first, so that
+                        // neither factor leaves the fp32 range)
+                        if (SLOT) {
+                            acc[t][0] += ldexpf(d0 * (c0[0] + c0[1]), -ex0[0]);
+                            acc[t][1] += ldexpf(d0 * (c0[2] + c0[3]), -ex0[2]);
+                            acc[t][0] += ldexpf(d1 * (c1[0] + c1[1]), -ex1[0]);
+                            acc[t][1] += ldexpf(d1 * (c1[2] + c1[3]), -ex1[2]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; j++) {
+                                acc[t][j] += ldexpf(d0 * c0[j], -ex0[j]);
+                                acc[t][j] += ldexpf(d1 * c1[j], -ex1[j]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---- partial sums of the 8 waves, added in wave order ----
+        __syncthreads();  // every wave is done with its slots and the x area
+        mf_f4 *red = reinterpret_cast<mf_f4 *>(lds);
+#pragma unroll
+        for (int t = 0; t < TG; t++) {
+            mf_f4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < ACC; j++)
+                v[j] = acc[t][j];
+            red[(t * kMfmaWaves + wave) * 64 + lane] = v;
+        }
+        __syncthreads();
+        for (int i = tid; i < gt * 64; i += kMfmaThreads) {
+            const int t = i >> 6, l = i & 63;
+            mf_f4 sm = red[(t * kMfmaWaves) * 64 + l];
+#pragma unroll
+            for (int w = 1; w < kMfmaWaves; w++)
+                sm += red[(t * kMfmaWaves + w) * 64 + l];
+            const int64_t row = r0 + 16 * (int64_t)(t0 + t) + (l & 15);
+            if (row < r1) {
+#pragma unroll
+                for (int j = 0; j < ACC; j++) {
+                    const int m = ACC * (l >> 4) + j;
+                    if (m < M)
+                        y[(int64_t)m * N + row] = sm[j];
                 }
             }
         }
@@ -416,8 +741,7 @@ template <int TYPE, int TG>
 static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, int M,
                           float *y, int64_t rq, int rr, int grid, int Pb, int nph, hipStream_t s)
 {
-    using T = MTile<TYPE>;
-    const size_t lds = std::max<size_t>((size_t)Pb * 64 * (T::CHUNKS * M + 1),
+    const size_t lds = std::max<size_t>((size_t)Pb * mfma_block_bytes<TYPE>(M),
                                         (size_t)TG * kMfmaWaves * 64 * 16);
     auto kern = pn_gemv_mfma_kernel<TYPE, TG>;
     static bool attr_set = false;
@@ -433,6 +757,56 @@ static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, i
     return launch_status();
 }
 
+template <int TYPE, int TG, bool SLOT>
+static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K,
+                              int M, float *y, int64_t rq, int rr, int grid, int Pb, int nph,
+                              size_t lds, hipStream_t s)
+{
+    auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, SLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMfmaLds) != hipSuccess)
+            return PN_ERR_HIP;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaThreads), lds, s, W, N, nb,
+                       (int64_t)nb * kBlockBytes, x, K, M, y, rq, rr, Pb, nph,
+                       aligned(x, 16) ? 1 : 0);
+    return launch_status();
+}
+
+template <int TYPE, bool SLOT>
+static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, int M,
+                             float *y, int grid, int64_t rq, int rr, hipStream_t s)
+{
+    // tiles per group: 9, except pn3t with hi and lo as separate operands (more registers)
+    constexpr int max_tg = (TYPE == PN_TYPE_PN3T && !SLOT) ? 3 : kMfmaMaxTG;
+    const int64_t tiles_max = (rq + (rr ? 1 : 0) + 15) / 16;
+    const int64_t ng = (tiles_max + max_tg - 1) / max_tg;
+    const int TG = (int)((tiles_max + ng - 1) / ng);
+    const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
+    const int per_block = mfma_block_bytes<TYPE>(M);
+    const int pb_max = ((kMfmaLds - ring) / per_block) & ~7;
+    const int nph = (nb + pb_max - 1) / pb_max;
+    const int Pb = ((nb + nph - 1) / nph + 7) & ~7;
+    const size_t lds = (size_t)ring + std::max<size_t>((size_t)Pb * per_block,
+                                                       (size_t)std::max(0, TG * 8192 - ring));
+    switch (TG) {
+#define PN_MFMA_CASE(tg)                                                                           \
+    case tg:                                                                                       \
+        if constexpr (tg <= max_tg)                                                                \
+            return launch_mfma_lds_tg<TYPE, tg, SLOT>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,     \
+                                                      nph, lds, s);                                \
+        else                                                                                       \
+            return PN_ERR_SHAPE;
+    PN_MFMA_CASE(1) PN_MFMA_CASE(2) PN_MFMA_CASE(3) PN_MFMA_CASE(4) PN_MFMA_CASE(5)
+    PN_MFMA_CASE(6) PN_MFMA_CASE(7) PN_MFMA_CASE(8) PN_MFMA_CASE(9)
+#undef PN_MFMA_CASE
+    default: return PN_ERR_SHAPE;
+    }
+}
+
 template <int TYPE>
 static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
                          int cus, hipStream_t s)
@@ -445,7 +819,12 @@ static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x,
     const int64_t tiles_max = (rq + (rr ? 1 : 0) + 15) / 16;
     const int64_t ng = (tiles_max + kMfmaMaxTG - 1) / kMfmaMaxTG;
     const int TG = (int)((tiles_max + ng - 1) / ng);
-    const int per_block = 64 * (T::CHUNKS * M + 1);
+    // weights staged through LDS when rows are whole 16-byte lines (W 16-byte aligned, a multiple
+    // of 8 blocks per row); PN_GEMV_MFMA_DIRECT keeps the direct-load kernel (tests, timing)
+    if (mfma_stages_weights(TYPE, W, K))
+        return M <= 8 ? launch_mfma_lds_t<TYPE, true>(W, N, nb, x, K, M, y, grid, rq, rr, s)
+                      : launch_mfma_lds_t<TYPE, false>(W, N, nb, x, K, M, y, grid, rq, rr, s);
+    const int per_block = mfma_block_bytes<TYPE>(M);
     const int pb_max = kMfmaLds / per_block;
     const int nph = (nb + pb_max - 1) / pb_max;
     const int Pb = (nb + nph - 1) / nph;
@@ -457,6 +836,14 @@ static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x,
 #undef PN_MFMA_CASE
     default: return PN_ERR_SHAPE;
     }
+}
+
+// Whether the matrix-core path stages these weights through LDS (16-byte aligned, rows of a
+// multiple of 8 blocks).
+bool mfma_stages_weights(int type, const void *W, int64_t K)
+{
+    const int64_t nb = K / (type == PN_TYPE_PN3T ? 80 : 64);
+    return aligned(W, 16) && nb % 8 == 0 && !getenv("PN_GEMV_MFMA_DIRECT");
 }
 
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,

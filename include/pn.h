@@ -87,20 +87,19 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  * Accuracy: |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100 and
  * sum_k |w x| >= 2^-126 (below that an fp32 y cannot resolve 1e-5 of the sum), under the
  * conditions below, which activations of ordinary dynamic range meet by a wide margin:
- *  - The zero point is folded per block, d * (sum n x - z * sum x), with the unsigned codes n, in
- *    fp32 chains of at most 16 terms (on the matrix cores: one chain of 4-6 MFMA steps per
- *    block), so the rounding error scales with a block's sum n|x| rather
- *    than its sum |n - z||x|. It stays inside the bound unless, in the blocks that dominate a
+ *  - On the vector units the zero point is folded per block, d * (sum n x - z * sum x), with the
+ *    unsigned codes n, in fp32 chains of at most 16 terms, so the rounding error scales with a
+ *    block's sum n|x| rather than its sum |n - z||x|. It stays inside the bound unless, in the blocks that dominate a
  *    row, sum n|x| exceeds about 8 * sum |n - z||x| (a large x meeting a code next to z).
  *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
  *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
  *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
- *  - M >= 5 runs on the matrix cores and carries each x as an fp16 (hi, lo) pair with one
- *    exponent per token, chosen from the token's largest |x|: exact to 2^-22 relative or to
- *    2^-33 (pn3t; 2^-35 pn4t) of that largest |x|, whichever is larger. The bound then needs
- *    sum_k |w||x| >= 2^-16 * max|x| * sum_k |w| per token and row, i.e. the x that meet a row's
- *    weights must not all be tiny next to the token's largest |x| -- activations of any ordinary
- *    shape, outliers included, meet it by orders of magnitude.
+ *  - M >= 3 on the matrix cores (3 and 4 tokens when W is 16-byte aligned and rows hold a
+ *    multiple of 8 blocks; every shape from 5 tokens): the zero point is taken off each code
+ *    exactly (no fold), and each x is carried as an fp16 (hi, lo) pair with one exponent per
+ *    block and token: exact to 2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the largest |x|
+ *    in its block, whichever is larger -- every x that meets a nonzero weight must be within
+ *    about 2^14 of the largest |x| of its block, or its block's other terms must dominate.
  *    Every other path uses x exactly (scaled by powers of two). Rows are not
  * validated here (validate at load); an invalid row gives an unspecified value but no
  * out-of-bounds access. Deterministic: the same inputs and launch give the same bits on every

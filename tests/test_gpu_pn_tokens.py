@@ -64,16 +64,19 @@ def test_gemv_tokens_phases(env, typ, N, nb, M):
     assert_within(y, y_ref, bound)
 
 
-@pytest.mark.parametrize("N,M", [(256 * 16 * 10 + 333, 5), (256 * 16 * 10 + 333, 11), (256 * 16 * 23 + 7, 6)])
-def test_gemv_tokens_tile_groups(env, N, M):
-    """More than ten tiles of 16 rows per workgroup: each workgroup walks several groups of tiles,
-    the last group partly empty."""
+@pytest.mark.parametrize("N,M,nb", [(256 * 16 * 10 + 333, 5, 2), (256 * 16 * 10 + 333, 11, 2),
+                                    (256 * 16 * 23 + 7, 6, 2), (256 * 16 * 10 + 333, 5, 8),
+                                    (256 * 16 * 12 + 5, 11, 8)])
+def test_gemv_tokens_tile_groups(env, N, M, nb):
+    """More than nine tiles of 16 rows per workgroup: each workgroup walks several groups of
+    tiles, the last group partly empty -- for both weight paths (rows of 8 blocks staged through
+    LDS, rows of 2 blocks read directly)."""
     pn, torch, dev = env
-    typ, nb = PN3T, 2
-    K, W = case(typ, N, nb, 9400 + M)
+    typ = PN3T
+    K, W = case(typ, N, nb, 9400 + M + nb)
     x = synth.activations(9500 + M, M, K)
     y_ref, bound = oracle.gemv(typ, W, N, K, x)
-    y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, 2), N, K, x)
+    y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
     assert_within(y, y_ref, bound)
 
 
@@ -152,3 +155,30 @@ def test_gemv_matrix_cores_forced(env, monkeypatch, typ, N, nb, M):
     for offset in (0, 2):
         y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
         assert_within(y, y_ref, bound)
+
+
+@pytest.mark.parametrize("M", [5, 12])
+@pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 45, 128)])
+def test_gemv_direct_weight_loads_forced(env, monkeypatch, typ, N, nb, M):
+    """The direct-load kernel on shapes that the LDS-staged one would take (16-byte aligned
+    weights, rows of a multiple of 8 blocks)."""
+    pn, torch, dev = env
+    monkeypatch.setenv("PN_GEMV_MFMA_DIRECT", "1")
+    K, W = case(typ, N, nb, 9800 + nb)
+    x = synth.activations(9900 + nb, M, K)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
+    assert_within(y, y_ref, bound)
+
+
+@pytest.mark.parametrize("M", [3, 4])
+@pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 45, 128)])
+def test_gemv_vector_kernel_forced(env, monkeypatch, typ, N, nb, M):
+    """The vector-unit kernel at 3-4 tokens on shapes the matrix cores take by default."""
+    pn, torch, dev = env
+    monkeypatch.setenv("PN_GEMV_NO_MFMA", "1")
+    K, W = case(typ, N, nb, 9950 + nb)
+    x = synth.activations(9960 + nb, M, K)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
+    assert_within(y, y_ref, bound)
