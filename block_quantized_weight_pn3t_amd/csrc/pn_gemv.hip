@@ -1118,7 +1118,7 @@ static int ring_depth()
 
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
                 int cus, hipStream_t s);
-bool mfma_stages_weights(int type, const void *W, int64_t K);
+bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K);
 
 template <int TYPE>
 static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
@@ -1147,7 +1147,7 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
     // the weights through LDS beats the vector-unit kernel; other shapes keep the latter
     // (PN_GEMV_MFMA forces the matrix cores, PN_GEMV_NO_MFMA the vector units: tests, timing).
     if (M > 4 || getenv("PN_GEMV_MFMA") ||
-        (!getenv("PN_GEMV_NO_MFMA") && mfma_stages_weights(TYPE, W, K)))
+        (!getenv("PN_GEMV_NO_MFMA") && mfma_stages_weights(TYPE, W, N, K)))
         return launch_mfma(TYPE, W, N, K, x, (int)M, y, num_cus(), s);
     if (M == 3)
         return launch_lds<TYPE, 3, 1, 2>(W, N, K, x, y, s);

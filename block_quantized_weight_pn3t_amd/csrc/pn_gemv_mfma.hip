@@ -35,7 +35,7 @@
 // last one masked). Its 8 waves split the (tile, block) work of each phase of x; partial sums
 // meet in LDS at the end and are added in wave order: deterministic. x larger than LDS is staged
 // in phases of blocks. Two kernels: one stages the weights through LDS with whole-line copies
-// (W 16-byte aligned, rows of a multiple of 8 blocks), the other reads each lane's bytes directly
+// (W 4-byte aligned, rows of a multiple of 4 blocks), the other reads each lane's bytes directly
 // (any 2-byte aligned W and block count).
 #include "pn_common.h"
 
@@ -43,7 +43,7 @@ namespace pn {
 
 typedef float mf_f4 __attribute__((ext_vector_type(4)));
 
-bool mfma_stages_weights(int type, const void *W, int64_t K);
+bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K);
 typedef uint32_t mf_u2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 template <int TYPE> struct MTile;
@@ -115,9 +115,9 @@ template <> struct MfmaB<PN_TYPE_PN3T> {
         b1 = u32x4v{minus_z(s0 & 0x00380038u, z3), minus_z(w1 & 0x00070007u, z0),
                     minus_z(w1 & 0x00380038u, z3), minus_z(w1 & 0x01C001C0u, z6)};
         // the last four codes fill half of a 16x16x32 step; the other half meets zero x (any
-        // finite code words do), here a copy of the same two
-        const uint32_t v8 = minus_z(s1 & 0x00070007u, z0), v9 = minus_z(s1 & 0x00380038u, z3);
-        b2 = u32x4v{v8, v9, v8, v9};
+        // finite words do): the same codes before the zero point comes off
+        const uint32_t m8 = s1 & 0x00070007u, m9 = s1 & 0x00380038u;
+        b2 = u32x4v{minus_z(m8, z0), minus_z(m9, z3), m8, m9};
     }
 };
 template <> struct MfmaB<PN_TYPE_PN4T> {
@@ -147,21 +147,22 @@ struct MfmaA {
     u32x4v c[6];
 };
 
-// One block of one 16-row tile: c <- c + codes . x over the block, hi and lo passes. The chain is
-// one asm block so that the accumulator stays in place (destination = C operand) from step to
+// One block of one 16-row tile: codes . x over the block, hi and lo passes, from C = 0. The chain
+// is one asm block so that the accumulator stays in place (destination = C operand) from step to
 // step, and the independent cycles around it are explicit: 3 before (operands just written by
 // vector instructions) and 16 after (the result is read, and the sources may be rewritten, by
 // vector instructions). Left to the compiler, a vector write to a register still being read as
 // the C operand of an in-flight 16x16x32 step was scheduled too close on gfx950 and corrupted
 // the sum.
 template <int TYPE>
-__device__ __forceinline__ mf_f4 mfma_block(const MfmaA &a, const MfmaB<TYPE> &b, mf_f4 c);
+__device__ __forceinline__ mf_f4 mfma_block(const MfmaA &a, const MfmaB<TYPE> &b);
 template <>
 __device__ __forceinline__ mf_f4 mfma_block<PN_TYPE_PN3T>(const MfmaA &a,
-                                                          const MfmaB<PN_TYPE_PN3T> &b, mf_f4 c)
+                                                          const MfmaB<PN_TYPE_PN3T> &b)
 {
+    mf_f4 c;
     asm volatile("s_nop 2\n\t"
-                 "v_mfma_f32_16x16x32_f16 %0, %1, %7, %0\n\t"
+                 "v_mfma_f32_16x16x32_f16 %0, %1, %7, 0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %2, %7, %0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %3, %8, %0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %4, %8, %0\n\t"
@@ -169,23 +170,24 @@ __device__ __forceinline__ mf_f4 mfma_block<PN_TYPE_PN3T>(const MfmaA &a,
                  "v_mfma_f32_16x16x32_f16 %0, %6, %9, %0\n\t"
                  "s_nop 7\n\t"
                  "s_nop 7"
-                 : "+v"(c)
+                 : "=&v"(c)
                  : "v"(a.c[0]), "v"(a.c[1]), "v"(a.c[2]), "v"(a.c[3]), "v"(a.c[4]), "v"(a.c[5]),
                    "v"(b.b0), "v"(b.b1), "v"(b.b2));
     return c;
 }
 template <>
 __device__ __forceinline__ mf_f4 mfma_block<PN_TYPE_PN4T>(const MfmaA &a,
-                                                          const MfmaB<PN_TYPE_PN4T> &b, mf_f4 c)
+                                                          const MfmaB<PN_TYPE_PN4T> &b)
 {
+    mf_f4 c;
     asm volatile("s_nop 2\n\t"
-                 "v_mfma_f32_16x16x32_f16 %0, %1, %5, %0\n\t"
+                 "v_mfma_f32_16x16x32_f16 %0, %1, %5, 0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %2, %5, %0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %3, %6, %0\n\t"
                  "v_mfma_f32_16x16x32_f16 %0, %4, %6, %0\n\t"
                  "s_nop 7\n\t"
                  "s_nop 7"
-                 : "+v"(c)
+                 : "=&v"(c)
                  : "v"(a.c[0]), "v"(a.c[1]), "v"(a.c[2]), "v"(a.c[3]), "v"(b.b0), "v"(b.b1));
     return c;
 }
@@ -200,15 +202,15 @@ template <> struct MfmaPair<PN_TYPE_PN3T, true> {
                                                const MfmaB<PN_TYPE_PN3T> &b1)
     {
         asm volatile("s_nop 2\n\t"
-                     "v_mfma_f32_16x16x32_f16 %0, %2, %8, %0\n\t"
-                     "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %8, 0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %5, %11, 0\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %3, %9, %0\n\t"
                      "v_mfma_f32_16x16x32_f16 %1, %6, %12, %1\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %4, %10, %0\n\t"
                      "v_mfma_f32_16x16x32_f16 %1, %7, %13, %1\n\t"
                      "s_nop 7\n\t"
                      "s_nop 7"
-                     : "+v"(c0), "+v"(c1)
+                     : "=&v"(c0), "=&v"(c1)
                      : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a1.c[0]), "v"(a1.c[1]),
                        "v"(a1.c[2]), "v"(b0.b0), "v"(b0.b1), "v"(b0.b2), "v"(b1.b0), "v"(b1.b1),
                        "v"(b1.b2));
@@ -220,13 +222,13 @@ template <> struct MfmaPair<PN_TYPE_PN4T, true> {
                                                const MfmaB<PN_TYPE_PN4T> &b1)
     {
         asm volatile("s_nop 2\n\t"
-                     "v_mfma_f32_16x16x32_f16 %0, %2, %6, %0\n\t"
-                     "v_mfma_f32_16x16x32_f16 %1, %4, %8, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %6, 0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %4, %8, 0\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %3, %7, %0\n\t"
                      "v_mfma_f32_16x16x32_f16 %1, %5, %9, %1\n\t"
                      "s_nop 7\n\t"
                      "s_nop 7"
-                     : "+v"(c0), "+v"(c1)
+                     : "=&v"(c0), "=&v"(c1)
                      : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a1.c[0]), "v"(a1.c[1]), "v"(b0.b0),
                        "v"(b0.b1), "v"(b1.b0), "v"(b1.b1));
     }
@@ -237,8 +239,8 @@ template <> struct MfmaPair<PN_TYPE_PN3T, false> {
                                                const MfmaB<PN_TYPE_PN3T> &b1)
     {
         asm volatile("s_nop 2\n\t"
-                     "v_mfma_f32_16x16x32_f16 %0, %2, %14, %0\n\t"
-                     "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %14, 0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %8, %17, 0\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %3, %14, %0\n\t"
                      "v_mfma_f32_16x16x32_f16 %1, %9, %17, %1\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %4, %15, %0\n\t"
@@ -251,7 +253,7 @@ template <> struct MfmaPair<PN_TYPE_PN3T, false> {
                      "v_mfma_f32_16x16x32_f16 %1, %13, %19, %1\n\t"
                      "s_nop 7\n\t"
                      "s_nop 7"
-                     : "+v"(c0), "+v"(c1)
+                     : "=&v"(c0), "=&v"(c1)
                      : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a0.c[3]), "v"(a0.c[4]),
                        "v"(a0.c[5]), "v"(a1.c[0]), "v"(a1.c[1]), "v"(a1.c[2]), "v"(a1.c[3]),
                        "v"(a1.c[4]), "v"(a1.c[5]), "v"(b0.b0), "v"(b0.b1), "v"(b0.b2),
@@ -264,8 +266,8 @@ template <> struct MfmaPair<PN_TYPE_PN4T, false> {
                                                const MfmaB<PN_TYPE_PN4T> &b1)
     {
         asm volatile("s_nop 2\n\t"
-                     "v_mfma_f32_16x16x32_f16 %0, %2, %10, %0\n\t"
-                     "v_mfma_f32_16x16x32_f16 %1, %6, %12, %1\n\t"
+                     "v_mfma_f32_16x16x32_f16 %0, %2, %10, 0\n\t"
+                     "v_mfma_f32_16x16x32_f16 %1, %6, %12, 0\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %3, %10, %0\n\t"
                      "v_mfma_f32_16x16x32_f16 %1, %7, %12, %1\n\t"
                      "v_mfma_f32_16x16x32_f16 %0, %4, %11, %0\n\t"
@@ -274,7 +276,7 @@ template <> struct MfmaPair<PN_TYPE_PN4T, false> {
                      "v_mfma_f32_16x16x32_f16 %1, %9, %13, %1\n\t"
                      "s_nop 7\n\t"
                      "s_nop 7"
-                     : "+v"(c0), "+v"(c1)
+                     : "=&v"(c0), "=&v"(c1)
                      : "v"(a0.c[0]), "v"(a0.c[1]), "v"(a0.c[2]), "v"(a0.c[3]), "v"(a1.c[0]),
                        "v"(a1.c[1]), "v"(a1.c[2]), "v"(a1.c[3]), "v"(b0.b0), "v"(b0.b1),
                        "v"(b1.b0), "v"(b1.b1));
@@ -287,17 +289,21 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi)
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+typedef __attribute__((address_space(1))) const float gfloat_t;
+typedef float mf_x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const mf_x4 gfloat4_t;
+
 // One staging unit: token m, block brel of the phase, k-group g (PERG consecutive x values).
 template <int TYPE>
-__device__ __forceinline__ void mfma_load_unit(const float *__restrict__ x, int64_t K, int m,
+__device__ __forceinline__ void mfma_load_unit(gfloat_t *x, int64_t K, int m,
                                                int64_t k0, int xvec4, float (&v)[MTile<TYPE>::PERG])
 {
     constexpr int PERG = MTile<TYPE>::PERG;
-    const float *src = x + (int64_t)m * K + k0;
+    gfloat_t *src = x + (int64_t)m * K + k0;
     if (xvec4) {
 #pragma unroll
         for (int q = 0; q < PERG / 4; q++) {
-            const float4 f = reinterpret_cast<const float4 *>(src)[q];
+            const mf_x4 f = reinterpret_cast<gfloat4_t *>(src)[q];
             v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
         }
     } else {
@@ -354,84 +360,112 @@ __device__ __forceinline__ void mfma_read_a(MfmaA &a, const uint8_t *blk, int g,
 
 // Stages x for the blocks [pb0, pb0 + npb) of a phase into the x area xa (mfma_block_bytes per
 // block). Every thread of the workgroup calls it; it holds two barriers. One unit = one token m,
-// one block, one k-group g: PERG consecutive x values; the four units of a (block, token) sit in
-// one lane quad. Per block and token, the exponent E is chosen from the block's largest |x| (so
-// that |x| * 2^(E + 24) < 2^15) and x * 2^(E + 24 - p) is split into fp16 hi + lo; E is stored
-// beside the operands and undone after the block's MFMA chain.
+// one block, one k-group g: PERG consecutive x values; the 4 EG units of a group of EG blocks
+// and one token sit in adjacent lanes. Per group and token, the exponent E is chosen from the
+// group's largest |x| (so that |x| * 2^(E + 24) < 2^15) and x * 2^(E + 24 - p) is split into fp16
+// hi + lo; -E is stored beside each block's operands and applied after the MFMA chains.
 // Layout SLOT (up to 8 tokens): hi and lo are token slots 2m, 2m+1 of one A operand, so one MFMA
 // per k-step covers both; K-split (up to 16 tokens): hi and lo are two A operands on the same
-// codes. `first` runs before the x loads are issued (a caller's weight prefetch).
-template <int TYPE, bool SLOT, class F>
-__device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *__restrict__ x, int64_t K,
-                                           int M, int pb0, int npb, int xvec4, F first)
+// codes. `after_loads` runs once the first x loads are issued (a caller's weight prefetch: loads
+// retire in order, so waiting for x then leaves the prefetch in flight).
+template <int TYPE, bool SLOT, int EG, class F>
+__device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t K, int M,
+                                           int ML, int pb0, int npb, int xvec4, F after_loads)
 {
     using T = MTile<TYPE>;
     constexpr int PERG = T::PERG;
     const int tid = threadIdx.x;
-    const int per_block = mfma_block_bytes<TYPE>(M), e_off = mfma_a_bytes<TYPE>(M);
+    const int per_block = mfma_block_bytes<TYPE>(ML), e_off = mfma_a_bytes<TYPE>(ML);
     const int U = npb * M * 4;
     const int nch = (U + kMfmaThreads * kMfmaUnits - 1) / (kMfmaThreads * kMfmaUnits);
+    // unit u: k-group u % 4, then the block within its group of EG, then the token, then the group
+    auto unit_coords = [&](int u, int &gg, int &m, int &brel) {
+        gg = u & 3;
+        const int v = u >> 2, bi = v % EG, w = v / EG;
+        m = w % M;
+        brel = EG * (w / M) + bi;
+    };
     __syncthreads();  // earlier readers of the x area are done
-    first();
-    for (int c = 0; c < nch; c++) {
-        float xr[kMfmaUnits][PERG];
+    // x is a restrict kernel argument, so its loads may otherwise move past the prefetch below;
+    // through an opaque copy of the address they stay in program order
+    uint64_t xaddr = reinterpret_cast<uint64_t>(x);
+    asm volatile("" : "+s"(xaddr));
+    gfloat_t *xg = reinterpret_cast<gfloat_t *>(xaddr);
+    float xr[kMfmaUnits][PERG];
+    // loads outside any branch (a unit past the end loads the last one again), so the waits for
+    // them can leave the weight prefetch issued after them in flight
+    auto load = [&](int c) {
 #pragma unroll
         for (int ub = 0; ub < kMfmaUnits; ub++) {
-            const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
-            if (u < U) {
-                const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
-                mfma_load_unit<TYPE>(x, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4,
-                                     xr[ub]);
-            }
+            const int u = min((c * kMfmaUnits + ub) * kMfmaThreads + tid, U - 1);
+            int gg, m, brel;
+            unit_coords(u, gg, m, brel);
+            mfma_load_unit<TYPE>(xg, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4, xr[ub]);
         }
-#pragma unroll
-        for (int ub = 0; ub < kMfmaUnits; ub++) {
-            const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
-            if (u < U) {  // U is a multiple of 4: whole quads take this branch
-                const int gg = u & 3, m = (u >> 2) % M, brel = (u >> 2) / M;
-                float mx = 0.f;
-#pragma unroll
-                for (int e = 0; e < PERG; e++)
-                    mx = fmaxf(mx, fabsf(xr[ub][e]));
-                mx = fmaxf(mx, PN_DPP(mx, 0xB1));  // quad_perm [1,0,3,2]
-                mx = fmaxf(mx, PN_DPP(mx, 0x4E));  // quad_perm [2,3,0,1]
-                int ex = 0;
-                frexpf(mx, &ex);
-                const int E = mx > 0.f ? -9 - ex : 0;
-                const int eb = E + 24;
-                uint32_t hw[PERG / 2], lw[PERG / 2];
-#pragma unroll
-                for (int e = 0; e < PERG; e += 2) {
-                    const float v0 = ldexpf(xr[ub][e], eb - T::pe(e));
-                    const float v1 = ldexpf(xr[ub][e + 1], eb - T::pe(e + 1));
-                    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-                    hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    lw[e / 2] = pack_h2(v0 - (float)h0, v1 - (float)h1);
-                }
-                uint8_t *blk = xa + brel * per_block;
-                auto put16 = [&](int ks, int h, u32x4v v) {
-                    *reinterpret_cast<u32x4v *>(blk + mfma_a_off<TYPE, SLOT>(ks, h, gg, m, M)) = v;
-                };
-                put16(0, 0, u32x4v{hw[0], hw[1], hw[2], hw[3]});
-                put16(0, 1, u32x4v{lw[0], lw[1], lw[2], lw[3]});
-                put16(1, 0, u32x4v{hw[4], hw[5], hw[6], hw[7]});
-                put16(1, 1, u32x4v{lw[4], lw[5], lw[6], lw[7]});
-                if constexpr (T::KSTEPS == 3) {  // the last 4 codes
-                    *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 0, gg, m, M)) =
-                        u32x2v{hw[8], hw[9]};
-                    *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 1, gg, m, M)) =
-                        u32x2v{lw[8], lw[9]};
-                }
-                if (gg == 0) {
-                    int *es = reinterpret_cast<int *>(blk + e_off);
-                    if (SLOT)
-                        es[2 * m] = es[2 * m + 1] = E;
-                    else
-                        es[m] = E;
+    };
+    auto convert = [&](int c) {
+    #pragma unroll
+            for (int ub = 0; ub < kMfmaUnits; ub++) {
+                const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
+                if (u < U) {  // U is a multiple of 4 EG: whole lane groups take this branch
+                    int gg, m, brel;
+                    unit_coords(u, gg, m, brel);
+                    float mx = 0.f;
+    #pragma unroll
+                    for (int e = 0; e < PERG; e++)
+                        mx = fmaxf(mx, fabsf(xr[ub][e]));
+                    mx = fmaxf(mx, PN_DPP(mx, 0xB1));      // quad_perm [1,0,3,2]
+                    mx = fmaxf(mx, PN_DPP(mx, 0x4E));      // quad_perm [2,3,0,1]
+                    if (EG == 4) {
+                        mx = fmaxf(mx, PN_DPP(mx, 0x124));  // row_ror:4
+                        mx = fmaxf(mx, PN_DPP(mx, 0x128));  // row_ror:8
+                    }
+                    int ex = 0;
+                    frexpf(mx, &ex);
+                    const int E = mx > 0.f ? -9 - ex : 0;
+                    const int eb = E + 24;
+                    uint32_t hw[PERG / 2], lw[PERG / 2];
+    #pragma unroll
+                    for (int e = 0; e < PERG; e += 2) {
+                        const float v0 = ldexpf(xr[ub][e], eb - T::pe(e));
+                        const float v1 = ldexpf(xr[ub][e + 1], eb - T::pe(e + 1));
+                        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+                        hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        lw[e / 2] = pack_h2(v0 - (float)h0, v1 - (float)h1);
+                    }
+                    uint8_t *blk = xa + brel * per_block;
+                    auto put16 = [&](int ks, int h, u32x4v v) {
+                        *reinterpret_cast<u32x4v *>(blk + mfma_a_off<TYPE, SLOT>(ks, h, gg, m, ML)) = v;
+                    };
+                    put16(0, 0, u32x4v{hw[0], hw[1], hw[2], hw[3]});
+                    put16(0, 1, u32x4v{lw[0], lw[1], lw[2], lw[3]});
+                    put16(1, 0, u32x4v{hw[4], hw[5], hw[6], hw[7]});
+                    put16(1, 1, u32x4v{lw[4], lw[5], lw[6], lw[7]});
+                    if constexpr (T::KSTEPS == 3) {  // the last 4 codes
+                        *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 0, gg, m, ML)) =
+                            u32x2v{hw[8], hw[9]};
+                        *reinterpret_cast<u32x2v *>(blk + mfma_a_off<TYPE, SLOT>(2, 1, gg, m, ML)) =
+                            u32x2v{lw[8], lw[9]};
+                    }
+                    if (gg == 0) {
+                        int *es = reinterpret_cast<int *>(blk + e_off);
+                        if (SLOT)
+                            es[2 * m] = es[2 * m + 1] = -E;
+                        else
+                            es[m] = -E;
+                    }
                 }
             }
-        }
+    };
+    load(0);
+    asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
+    after_loads();
+    asm volatile("" ::: "memory");
+    convert(0);
+    for (int c = 1; c < nch; c++) {
+        load(c);
+        convert(c);
     }
     const int used = SLOT ? 2 * M : M;
     for (int i = tid; i < npb * 16; i += kMfmaThreads)
@@ -478,7 +512,7 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
 
         for (int p = 0; p < nph; p++) {
             const int pb0 = p * Pb, npb = min(nb, pb0 + Pb) - pb0;
-            mfma_stage<TYPE, false>(lds, x, K, M, pb0, npb, xvec4, [] {});
+            mfma_stage<TYPE, false, 1>(lds, x, K, M, M, pb0, npb, xvec4, [] {});
 
             // ---- this wave's blocks of the phase, every tile of the group ----
             const int kb0 = pb0 + (wave * npb) / kMfmaWaves;
@@ -506,7 +540,6 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
                         const uint8_t *blk = lds + brel * per_block;
                         if (n16 < M)
                             mfma_read_a<TYPE, false>(a, blk, g, n16, M);
-                        const mf_f4 c0 = {0.f, 0.f, 0.f, 0.f};
                         const i32x4v ex = *reinterpret_cast<const i32x4v *>(blk + e_off + 16 * g);
                         const int nxt = kb0 + min(st + P, ns - 1);
                         // No branch around the use of a ring slot: a step past the wave's last
@@ -522,10 +555,10 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
                                 (live && t < gt) ? f16_bits_to_f32(raw[s][t].dbits) : 0.f;
                             mfma_issue(rowp[t], nxt, g, raw[s][t]);
                             __builtin_amdgcn_sched_barrier(0);
-                            const mf_f4 dd = mfma_block<TYPE>(a, bop, c0);
+                            const mf_f4 dd = mfma_block<TYPE>(a, bop);
 #pragma unroll
                             for (int j = 0; j < 4; j++)
-                                acc[t][j] += ldexpf(dv * dd[j], -ex[j]);
+                                acc[t][j] += ldexpf(dv * dd[j], ex[j]);
                         }
                     }
                 }
@@ -558,37 +591,46 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
     }
 }
 
-// ---- weights staged through LDS: 16 rows x 8 blocks per wave and step --------------------------
+// ---- weights staged through LDS: 16 rows x 4 blocks per wave and step ------------------------
 //
-// Rows of a multiple of 8 blocks are 16-byte aligned when W is (8 * 34 = 272 = 17 * 16). A wave
-// then copies 16 rows x 8 blocks (4352 bytes) straight from HBM into a private LDS slot with
-// 16-byte loads that fill whole lines (global_load_lds_dwordx4: 4 wave loads + 16 lanes), and
-// each lane reads its two words per block from there. The direct loads of the general kernel
-// above touch 16-20 cache lines for 512 bytes per instruction; these touch about 12 per 1 KB.
-// The slot is double-buffered: the next step's copy is in flight while this one is computed.
-// The waits on the copies are explicit (the compiler does not order LDS reads after them).
-constexpr int kChunkBytes = 16 * 8 * kBlockBytes;  // 4352
-constexpr int kLdsRing = 2;                         // slots per wave
+// A wave copies 16 rows x 4 blocks (16 segments of 136 contiguous bytes, 2176 bytes) straight from
+// HBM into a private LDS slot with 9 buffer loads of one dword per lane (each covers 256
+// contiguous bytes; the 9th, bytes 1920..2175 of the step, rewrites 128 of them with the same
+// values), and each lane reads its two words per block from there. The direct loads of the
+// other kernel touch 16-20 cache lines for 512 bytes per instruction; these, 2-3 per 256. Each
+// wave keeps 3 steps in flight in a ring of 4 slots. The offsets within a step are constant per
+// lane; the step's position is one scalar offset, and the buffer's bounds check reads rows past
+// the matrix end as zero. Past its last step a wave re-issues its last one, so that exactly 27
+// loads follow every step it waits for. The waits are explicit (the compiler does not order LDS
+// reads after these copies).
+constexpr int kChunkBlocks = 4;
+constexpr int kChunkBytes = 16 * kChunkBlocks * kBlockBytes;  // 2176
+constexpr int kLdsRing = 4;                                    // slots per wave (a power of 2)
+constexpr int kStepLoads = 9;                                  // buffer loads per step
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int TYPE, int TG, bool SLOT>
+// MC: the token capacity of the x layout (4, 8 or 16; M <= MC), so that every LDS offset of
+// the loop is a constant. Up to 8, hi and lo are token slots.
+template <int TYPE, int TG, int MC>
 __global__ void __launch_bounds__(kMfmaThreads)
 pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
                         const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
                         int64_t rq, int rr, int Pb, int nph, int xvec4)
 {
+    constexpr bool SLOT = MC <= 8;
     constexpr int ACC = SLOT ? 2 : 4;       // tokens per lane
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
-    const int per_block = mfma_block_bytes<TYPE>(M);
-    const int e_off = mfma_a_bytes<TYPE>(M);
+    constexpr int per_block = mfma_block_bytes<TYPE>(MC);
+    constexpr int e_off = mfma_a_bytes<TYPE>(MC);
     const int alim = SLOT ? 2 * M : M;  // lanes (by n16) that hold A operands
-    uint8_t *const ring = lds + wave * kLdsRing * kChunkBytes;
-    uint8_t *const xa = lds + kMfmaWaves * kLdsRing * kChunkBytes;
+    // x area first (its offsets fit the 16-bit immediates of LDS instructions), then the slots
+    uint8_t *const xa = lds;
+    uint8_t *const ring = lds + Pb * per_block + wave * kLdsRing * kChunkBytes;
 
     const int64_t wg = blockIdx.x;
     const int64_t r0 = wg * rq + (wg < rr ? wg : rr);
@@ -596,26 +638,24 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
     const int ntiles = (int)((r1 - r0 + 15) >> 4);
     const int ngroups = (ntiles + TG - 1) / TG;
 
-    // This lane's 16-byte pieces of a step: piece 64 j + lane is row (piece / 17), column
-    // (piece % 17); j = 4 only for lanes < 16 (272 pieces).
-    int prow[5], pcol[5];
+    // dword k of a step (row k / 34, byte 4 (k % 34) of its segment): k = 64 j + lane for
+    // j < 8, k = 480 + lane for the 9th load
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)(N * row_bytes), 0x00020000);
+    uint32_t voff[kStepLoads];
 #pragma unroll
-    for (int j = 0; j < 5; j++) {
-        const int pc = 64 * j + lane;
-        prow[j] = pc / 17;
-        pcol[j] = pc % 17;
+    for (int j = 0; j < kStepLoads; j++) {
+        const int k = j < 8 ? 64 * j + lane : 480 + lane;
+        voff[j] = (uint32_t)((k / 34) * row_bytes + 4 * (k % 34));
     }
-    auto issue = [&](int tile, int c8, int slot) {  // tile: index within the workgroup
+    auto issue = [&](int tile, int c4, int slot) {  // tile: index within the workgroup
         uint8_t *dst = ring + slot * kChunkBytes;
+        const uint32_t soff = (uint32_t)((r0 + 16 * (int64_t)tile) * row_bytes) +
+                              (uint32_t)(c4 * kChunkBlocks * kBlockBytes);
 #pragma unroll
-        for (int j = 0; j < 5; j++) {
-            if (j < 4 || lane < 16) {
-                int64_t r = r0 + 16 * (int64_t)tile + prow[j];
-                r = r < r1 ? r : r1 - 1;
-                const uint8_t *src = W + r * row_bytes + (int64_t)c8 * (8 * kBlockBytes) + 16 * pcol[j];
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(dst + 1024 * j), 16, 0, 0);
-            }
-        }
+        for (int j = 0; j < kStepLoads; j++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)(dst + (j < 8 ? 256 * j : 1920)),
+                                                     4, voff[j], soff, 0, 0);
     };
 
     MfmaA a0, a1;
@@ -634,33 +674,47 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
                 acc[t][j] = 0.f;
 
         for (int p = 0; p < nph; p++) {
-            const int pb0 = p * Pb, npb = min(nb, pb0 + Pb) - pb0;  // both multiples of 8
-            const int n8 = npb >> 3, c80 = pb0 >> 3;
-            // items (tile, 8-block step), tile-major, split evenly over the 8 waves
-            const int items = gt * n8;
+            const int pb0 = p * Pb, npb = min(nb, pb0 + Pb) - pb0;  // both multiples of 4
+            const int n4 = npb >> 2, c40 = pb0 >> 2;
+            // items (tile, 4-block step), tile-major, split evenly over the 8 waves
+            const int items = gt * n4;
             const int i0 = (wave * items) / kMfmaWaves, i1 = ((wave + 1) * items) / kMfmaWaves;
-            mfma_stage<TYPE, SLOT>(xa, x, K, M, pb0, npb, xvec4, [&] {
-                if (i0 < i1)
-                    issue(t0 + i0 / n8, c80 + i0 % n8, i0 % kLdsRing);
+            // prefetch cursor: item pf (slot pf % 4) is (tile pt, step pc); past the wave's last
+            // item it stays on that item (the copy is re-issued, nothing reads it)
+            int pf = i0, pt = i0 / n4, pc = i0 % n4;
+            auto issue_next = [&]() {
+                issue(t0 + pt, c40 + pc, pf & (kLdsRing - 1));
+                if (pf + 1 < i1 && ++pc == n4) {
+                    pc = 0;
+                    ++pt;
+                }
+                ++pf;
+            };
+            mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
+                issue_next();
+                issue_next();
+                issue_next();
             });
 #pragma unroll
             for (int t = 0; t < TG; t++) {
-                const int lo = max(i0, t * n8), hi = min(i1, (t + 1) * n8);
+                const int lo = max(i0, t * n4), hi = min(i1, (t + 1) * n4);
                 for (int it = lo; it < hi; it++) {
-                    // refill the other slot, then wait for this step's copy (loads retire in
-                    // order: at most the 5 just issued may stay outstanding)
-                    asm volatile("" ::: "memory");  // this slot's earlier reads stay before
-                    if (it + 1 < i1) {
-                        issue(t0 + (it + 1) / n8, c80 + (it + 1) % n8, (it + 1) % kLdsRing);
-                        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-                    } else {
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    }
-                    const uint8_t *cr = ring + (it % kLdsRing) * kChunkBytes + 272 * n16;
+                    // refill the slot read one step ago, then wait for this step's copy: loads
+                    // retire in order and exactly 3 steps (27 loads) were issued after it
+                    asm volatile("" ::: "memory");  // that slot's reads stay before
+                    issue_next();
+                    asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+                    const uint8_t *cr = ring + (it & (kLdsRing - 1)) * kChunkBytes + 136 * n16;
                     const uint8_t *cw = cr + 8 * g;
-                    const uint8_t *xb = xa + ((it % n8) * 8) * per_block;
+                    const uint8_t *xb = xa + ((it - t * n4) * kChunkBlocks) * per_block;
+                    // the step's 4 blocks share one exponent per token (-E stored per block)
+                    const i32x4v nE = *reinterpret_cast<const i32x4v *>(xb + e_off + 16 * g);
+                    float sacc[ACC];
 #pragma unroll
-                    for (int jp = 0; jp < 4; jp++) {
+                    for (int j = 0; j < ACC; j++)
+                        sacc[j] = 0.f;
+#pragma unroll
+                    for (int jp = 0; jp < 2; jp++) {
                         // block 2jp: words 2 mod 4 aligned (read 12 bytes from 2 before);
                         // block 2jp+1: words 4-byte aligned
                         const int j0 = 2 * jp, j1 = 2 * jp + 1;
@@ -673,34 +727,35 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
                             *reinterpret_cast<const uint16_t *>(cr + 34 * j1));
                         const uint8_t *x0 = xb + j0 * per_block, *x1 = xb + j1 * per_block;
                         if (n16 < alim) {
-                            mfma_read_a<TYPE, SLOT>(a0, x0, g, n16, M);
-                            mfma_read_a<TYPE, SLOT>(a1, x1, g, n16, M);
+                            mfma_read_a<TYPE, SLOT>(a0, x0, g, n16, MC);
+                            mfma_read_a<TYPE, SLOT>(a1, x1, g, n16, MC);
                         }
-                        mf_f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-                        const i32x4v ex0 = *reinterpret_cast<const i32x4v *>(x0 + e_off + 16 * g);
-                        const i32x4v ex1 = *reinterpret_cast<const i32x4v *>(x1 + e_off + 16 * g);
+                        mf_f4 c0, c1;
                         MfmaB<TYPE> b0, b1;
                         b0.words(__builtin_amdgcn_alignbit(e1, e0, 16),
                                  __builtin_amdgcn_alignbit(e2, e1, 16));
                         b1.words(o0, o1);
                         MfmaPair<TYPE, SLOT>::run(c0, c1, a0, a1, b0, b1);
-                        // undo the block's exponent: d * chain * 2^-E (the product first, so that
-                        // neither factor leaves the fp32 range)
-                        if (SLOT) {
-                            acc[t][0] += ldexpf(d0 * (c0[0] + c0[1]), -ex0[0]);
-                            acc[t][1] += ldexpf(d0 * (c0[2] + c0[3]), -ex0[2]);
-                            acc[t][0] += ldexpf(d1 * (c1[0] + c1[1]), -ex1[0]);
-                            acc[t][1] += ldexpf(d1 * (c1[2] + c1[3]), -ex1[2]);
+                        if (SLOT) {  // hi + lo slots, times d
+                            sacc[0] = fmaf(d0, c0[0] + c0[1], sacc[0]);
+                            sacc[1] = fmaf(d0, c0[2] + c0[3], sacc[1]);
+                            sacc[0] = fmaf(d1, c1[0] + c1[1], sacc[0]);
+                            sacc[1] = fmaf(d1, c1[2] + c1[3], sacc[1]);
                         } else {
 #pragma unroll
                             for (int j = 0; j < 4; j++) {
-                                acc[t][j] += ldexpf(d0 * c0[j], -ex0[j]);
-                                acc[t][j] += ldexpf(d1 * c1[j], -ex1[j]);
+                                sacc[j] = fmaf(d0, c0[j], sacc[j]);
+                                sacc[j] = fmaf(d1, c1[j], sacc[j]);
                             }
                         }
                     }
+                    // undo the step's exponent: an exact scaling of the step's sum
+#pragma unroll
+                    for (int j = 0; j < ACC; j++)
+                        acc[t][j] += ldexpf(sacc[j], nE[SLOT ? 2 * j : j]);
                 }
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the re-issued steps too
         }
 
         // ---- partial sums of the 8 waves, added in wave order ----
@@ -757,12 +812,12 @@ static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, i
     return launch_status();
 }
 
-template <int TYPE, int TG, bool SLOT>
+template <int TYPE, int TG, int MC>
 static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K,
                               int M, float *y, int64_t rq, int rr, int grid, int Pb, int nph,
                               size_t lds, hipStream_t s)
 {
-    auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, SLOT>;
+    auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -776,27 +831,27 @@ static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *
     return launch_status();
 }
 
-template <int TYPE, bool SLOT>
+template <int TYPE, int MC>
 static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, int M,
                              float *y, int grid, int64_t rq, int rr, hipStream_t s)
 {
-    // tiles per group: 9, except pn3t with hi and lo as separate operands (more registers)
-    constexpr int max_tg = (TYPE == PN_TYPE_PN3T && !SLOT) ? 3 : kMfmaMaxTG;
+    // tiles of 16 rows per group
+    constexpr int max_tg = kMfmaMaxTG;
     const int64_t tiles_max = (rq + (rr ? 1 : 0) + 15) / 16;
     const int64_t ng = (tiles_max + max_tg - 1) / max_tg;
     const int TG = (int)((tiles_max + ng - 1) / ng);
     const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
-    const int per_block = mfma_block_bytes<TYPE>(M);
-    const int pb_max = ((kMfmaLds - ring) / per_block) & ~7;
+    const int per_block = mfma_block_bytes<TYPE>(MC);
+    const int pb_max = ((kMfmaLds - ring) / per_block) & ~(kChunkBlocks - 1);
     const int nph = (nb + pb_max - 1) / pb_max;
-    const int Pb = ((nb + nph - 1) / nph + 7) & ~7;
-    const size_t lds = (size_t)ring + std::max<size_t>((size_t)Pb * per_block,
-                                                       (size_t)std::max(0, TG * 8192 - ring));
+    const int Pb = ((nb + nph - 1) / nph + kChunkBlocks - 1) & ~(kChunkBlocks - 1);
+    // x area (Pb blocks), then the slots; the partial sums at the end alias the start
+    const size_t lds = std::max<size_t>((size_t)Pb * per_block + ring, (size_t)TG * 8192);
     switch (TG) {
 #define PN_MFMA_CASE(tg)                                                                           \
     case tg:                                                                                       \
         if constexpr (tg <= max_tg)                                                                \
-            return launch_mfma_lds_tg<TYPE, tg, SLOT>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,     \
+            return launch_mfma_lds_tg<TYPE, tg, MC>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,       \
                                                       nph, lds, s);                                \
         else                                                                                       \
             return PN_ERR_SHAPE;
@@ -819,11 +874,12 @@ static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x,
     const int64_t tiles_max = (rq + (rr ? 1 : 0) + 15) / 16;
     const int64_t ng = (tiles_max + kMfmaMaxTG - 1) / kMfmaMaxTG;
     const int TG = (int)((tiles_max + ng - 1) / ng);
-    // weights staged through LDS when rows are whole 16-byte lines (W 16-byte aligned, a multiple
-    // of 8 blocks per row); PN_GEMV_MFMA_DIRECT keeps the direct-load kernel (tests, timing)
-    if (mfma_stages_weights(TYPE, W, K))
-        return M <= 8 ? launch_mfma_lds_t<TYPE, true>(W, N, nb, x, K, M, y, grid, rq, rr, s)
-                      : launch_mfma_lds_t<TYPE, false>(W, N, nb, x, K, M, y, grid, rq, rr, s);
+    // weights staged through LDS (4-byte aligned W, rows of a multiple of 4 blocks);
+    // PN_GEMV_MFMA_DIRECT keeps the direct-load kernel (tests, timing)
+    if (mfma_stages_weights(TYPE, W, N, K))
+        return M <= 4   ? launch_mfma_lds_t<TYPE, 4>(W, N, nb, x, K, M, y, grid, rq, rr, s)
+               : M <= 8 ? launch_mfma_lds_t<TYPE, 8>(W, N, nb, x, K, M, y, grid, rq, rr, s)
+                        : launch_mfma_lds_t<TYPE, 16>(W, N, nb, x, K, M, y, grid, rq, rr, s);
     const int per_block = mfma_block_bytes<TYPE>(M);
     const int pb_max = kMfmaLds / per_block;
     const int nph = (nb + pb_max - 1) / pb_max;
@@ -838,12 +894,13 @@ static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x,
     }
 }
 
-// Whether the matrix-core path stages these weights through LDS (16-byte aligned, rows of a
-// multiple of 8 blocks).
-bool mfma_stages_weights(int type, const void *W, int64_t K)
+// Whether the matrix-core path stages these weights through LDS: 4-byte aligned, rows of a
+// multiple of 4 blocks, offsets (rows + a tile) within 31 bits.
+bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K)
 {
     const int64_t nb = K / (type == PN_TYPE_PN3T ? 80 : 64);
-    return aligned(W, 16) && nb % 8 == 0 && !getenv("PN_GEMV_MFMA_DIRECT");
+    return aligned(W, 4) && nb % kChunkBlocks == 0 && (N + 16) * nb * kBlockBytes < (int64_t(1) << 31) &&
+           !getenv("PN_GEMV_MFMA_DIRECT");
 }
 
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,

@@ -94,8 +94,8 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
  *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
  *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
- *  - M >= 3 on the matrix cores (3 and 4 tokens when W is 16-byte aligned and rows hold a
- *    multiple of 8 blocks; every shape from 5 tokens): the zero point is taken off each code
+ *  - M >= 3 on the matrix cores (3 and 4 tokens when W is 4-byte aligned and rows hold a
+ *    multiple of 4 blocks; every shape from 5 tokens): the zero point is taken off each code
  *    exactly (no fold), and each x is carried as an fp16 (hi, lo) pair with one exponent per
  *    block and token: exact to 2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the largest |x|
  *    in its block, whichever is larger -- every x that meets a nonzero weight must be within
