@@ -17,12 +17,13 @@
 //    off each code (instead of folding d * (sum n x - z sum x)) leaves no cancellation for the
 //    matrix cores' accumulation to round.
 //  * x is the A operand (rows = tokens), staged in LDS once per workgroup as an fp16 (hi, lo) pair
-//    x * 2^(E + 24 - p) per code position, E one exponent per block and token chosen from the
-//    block's largest |x| so that hi stays below 2^15: the sum of hi and lo is ~22-bit exact x. Up
-//    to 8 tokens, hi and lo are two token slots of one operand; up to 16, two operands.
+//    x * 2^(E + 24 - p) per code position, E one exponent per token and group of blocks (one
+//    block in the direct-load kernel, four in the LDS-staged one) chosen from the group's largest
+//    |x| so that hi stays below 2^15: the sum of hi and lo is ~22-bit exact x. Up to 8 tokens, hi
+//    and lo are two token slots of one operand; up to 16, two operands.
 //  * Each block's chain gives 2^E * sum (n - z) x for 16 rows x 16 token slots; one multiply by
-//    d and one exact 2^-E scaling per token add it into the row's sum. The block's scale d never
-//    meets a code in fp16.
+//    d per block and one exact 2^-E scaling per token and group add it into the row's sum. The
+//    block's scale d never meets a code in fp16.
 //
 // Operand layout (measured on gfx950 with a one-wave probe): for 16x16x32, lane l holds
 // A[l % 16][8 (l / 16) + j] and B[8 (l / 16) + j][l % 16] for j < 8, and the result
