@@ -287,7 +287,7 @@ def main():
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only: run with --gpus 1 "
-                          "(the GEMV shards by rows; see the design notes)"}))
+                          "(the GEMV shards by rows, with no new kernels; several GPUs are not measured)"}))
         sys.exit(2)
 
     import torch

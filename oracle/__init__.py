@@ -57,6 +57,8 @@ def _sigs():
         "or_pn_validate_rows": (None, [I32, P, I64, I64, P]),
         "or_pn_quantize_rows": (I32, [I32, P, I64, I64, P, P]),
         "or_pn_gemv": (None, [I32, P, I64, I64, P, I64, P, P]),
+        "or_hadamard_rows": (None, [P, I64, I64, I64, P, P]),
+        "or_pn_gemv_dx": (None, [I32, P, I64, I64, P, P, I64, P, P, P]),
         "or_nvfp4_dequantize_rows": (None, [P, P, C.c_float, I64, I64, P]),
         "or_nvfp4_validate_rows": (None, [P, C.c_float, I64, I64, P]),
         "or_nvfp4_global_scale": (C.c_float, [P, I64]),
@@ -249,6 +251,57 @@ def gemv(type_: int, W: np.ndarray, N: int, K: int, x: np.ndarray, threads: int 
     with ThreadPoolExecutor(len(parts)) as ex:
         list(ex.map(run, range(len(parts))))
     return np.concatenate(ys, axis=1), np.concatenate(bs, axis=1)
+
+
+# ---- Hadamard-rotated activations ----------------------------------------------------------------
+
+def hadamard(x: np.ndarray, B: int):
+    """(out, mass) float64 [M, K]: each slice of B elements of each row of x multiplied by the
+    orthonormal Sylvester Walsh-Hadamard matrix; mass = (1/sqrt B) * sum of |x| over the slice."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    if x.ndim == 1:
+        x = x[None, :]
+    M, K = x.shape
+    if B < 1 or B & (B - 1) or K % B:
+        raise ValueError("B must be a power of two that divides K")
+    out = np.empty((M, K), dtype=np.float64)
+    mass = np.empty((M, K), dtype=np.float64)
+    L = lib()
+    parts = _row_split(M, _threads(M))
+
+    def run(i):
+        s, e = parts[i]
+        L.or_hadamard_rows(_p(x) + s * K * 8, e - s, K, B, _p(out) + s * K * 8,
+                           _p(mass) + s * K * 8)
+
+    with ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run, range(len(parts))))
+    return out, mass
+
+
+def gemv_hadamard(type_: int, W: np.ndarray, N: int, K: int, x: np.ndarray, B: int,
+                  threads: int | None = None):
+    """The PN GEMV over Hadamard-rotated activations: (y, bound, rot_bound) float64 [M, N] with
+    y = W (H x), bound = sum_k |w_k x'_k| and rot_bound = sum_k |w_k| mass_k (mass from hadamard)."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    xr, mass = hadamard(np.asarray(x, dtype=np.float32).astype(np.float64), B)
+    M = xr.shape[0]
+    rb = row_bytes(type_, K)
+    L = lib()
+    parts = _row_split(N, threads or _threads(N))
+    ys, bs, ms = [None] * len(parts), [None] * len(parts), [None] * len(parts)
+
+    def run(i):
+        s, e = parts[i]
+        y = np.empty((M, e - s), dtype=np.float64)
+        b = np.empty((M, e - s), dtype=np.float64)
+        mb = np.empty((M, e - s), dtype=np.float64)
+        L.or_pn_gemv_dx(type_, _p(W) + s * rb, e - s, K, _p(xr), _p(mass), M, _p(y), _p(b), _p(mb))
+        ys[i], bs[i], ms[i] = y, b, mb
+
+    with ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run, range(len(parts))))
+    return (np.concatenate(ys, axis=1), np.concatenate(bs, axis=1), np.concatenate(ms, axis=1))
 
 
 # ---- NVFP4 -------------------------------------------------------------------------------------

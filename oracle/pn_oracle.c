@@ -30,6 +30,9 @@
  *   GEMV        exact rational brute force on small rows; one-hot and block-indicator x.
  *   quantizers  invariants and brute-force re-scans only: parity unpinned against the engines'
  *               own quantizers (no printed vectors exist on the pages).
+ *   Hadamard    against an independent library construction of the Sylvester matrix (scipy),
+ *               the textbook H_2 / H_4, involution (H_B / sqrt(B) is symmetric and orthogonal),
+ *               norm preservation; the rotated GEMV against a dense product of those.
  *   row E4M3    decode by the section 3.4 product over all 256 code words at power-of-two and
  *               other scales; each validity clause of section 3.4 on its own; the bf16 rounding
  *               against the integer round-half-even of binary32 words.
@@ -465,6 +468,89 @@ void or_pn_gemv(int type, const uint8_t *W, int64_t N, int64_t K, const float *x
         for (int64_t m = 0; m < M; m++) {
             y[m * N + n] = acc[m];
             bound[m * N + n] = abs_acc[m];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Hadamard-rotated activations ([PN] "Files that use PN": the model applies a Hadamard rotation */
+/* to the activations that reach the PN weights; the engine performs it). The page gives neither */
+/* the order of the transform nor its normalisation. Reading: K is cut into consecutive slices   */
+/* of B elements (B a power of two dividing K), and each slice is multiplied by the orthonormal  */
+/* Sylvester-ordered Walsh-Hadamard matrix H_B / sqrt(B), with H_B[i][j] = (-1)^popcount(i & j) */
+/* (the closed form of the Sylvester doubling H_2n = [[H, H], [H, -H]]).                         */
+/* ------------------------------------------------------------------------------------------ */
+
+static int popcount64(uint64_t v)
+{
+    int c = 0;
+    while (v) {
+        c += (int)(v & 1);
+        v >>= 1;
+    }
+    return c;
+}
+
+/* out[m, k] = (1/sqrt(B)) sum_{j < B} H_B[i][j] x[m, base + j] for k = base + i, the matrix product
+ * written out (B^2 terms per slice), in double. mass[m, k] = (1/sqrt(B)) sum_j |x[m, base + j]|:
+ * the sum of the magnitudes that meet in out[m, k] (used by the tests to bound rounding). Either
+ * output may be NULL. */
+void or_hadamard_rows(const double *x, int64_t M, int64_t K, int64_t B, double *out, double *mass)
+{
+    const double inv = 1.0 / sqrt((double)B);
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t base = 0; base < K; base += B) {
+            const double *xs = x + m * K + base;
+            double amass = 0.0;
+            for (int64_t j = 0; j < B; j++)
+                amass += fabs(xs[j]);
+            for (int64_t i = 0; i < B; i++) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < B; j++)
+                    acc += (popcount64((uint64_t)(i & j)) & 1) ? -xs[j] : xs[j];
+                if (out)
+                    out[m * K + base + i] = acc * inv;
+                if (mass)
+                    mass[m * K + base + i] = amass * inv;
+            }
+        }
+    }
+}
+
+/* The GEMV of "PN weight format" with activations given in double (the rotated x above):
+ * y[m, n] = sum_k w[n, k] x[m, k] in double, bound[m, n] = sum_k |w[n, k] x[m, k]|, and, when
+ * xmass is given, mbound[m, n] = sum_k |w[n, k]| xmass[m, k]. */
+void or_pn_gemv_dx(int type, const uint8_t *W, int64_t N, int64_t K, const double *x,
+                   const double *xmass, int64_t M, double *y, double *bound, double *mbound)
+{
+    int64_t rb = or_pn_row_bytes(type, K);
+    int bits, G, cpw, z;
+    or_pn_params(type, &bits, &G, &cpw, &z);
+    uint8_t codes[80];
+    double acc[M], abs_acc[M], m_acc[M];
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t m = 0; m < M; m++)
+            acc[m] = abs_acc[m] = m_acc[m] = 0.0;
+        for (int64_t b = 0; b < K / G; b++) {
+            uint16_t d16;
+            or_pn_unpack_block(type, W + n * rb + 34 * b, &d16, codes);
+            float d = (float)or_f16_to_double(d16);
+            for (int e = 0; e < G; e++) {
+                double w_nk = (double)(d * (float)(codes[e] - z));
+                for (int64_t m = 0; m < M; m++) {
+                    double p = w_nk * x[m * K + b * G + e];
+                    acc[m] += p;
+                    abs_acc[m] += fabs(p);
+                    if (xmass)
+                        m_acc[m] += fabs(w_nk) * xmass[m * K + b * G + e];
+                }
+            }
+        }
+        for (int64_t m = 0; m < M; m++) {
+            y[m * N + n] = acc[m];
+            bound[m * N + n] = abs_acc[m];
+            if (mbound)
+                mbound[m * N + n] = m_acc[m];
         }
     }
 }

@@ -52,6 +52,18 @@ MUTANTS = {
     "fp8row_zero_scale_clause_dropped": ("            if (s == 0 && (c & 0x7F) != 0)\n                ok = 0;",
                                          "",
                                          ["test_oracle_fp8row.py"]),
+    "hadamard_sign_from_or": ("acc += (popcount64((uint64_t)(i & j)) & 1) ? -xs[j] : xs[j];",
+                              "acc += (popcount64((uint64_t)(i | j)) & 1) ? -xs[j] : xs[j];",
+                              ["test_oracle_hadamard.py"]),
+    "rotated_gemv_drops_zero_point": ("double w_nk = (double)(d * (float)(codes[e] - z));",
+                                      "double w_nk = (double)(d * (float)codes[e]);",
+                                      ["test_oracle_hadamard.py"]),
+    "hadamard_unnormalised": ("const double inv = 1.0 / sqrt((double)B);",
+                              "const double inv = 1.0;",
+                              ["test_oracle_hadamard.py"]),
+    "hadamard_every_slice_reads_the_first": ("const double *xs = x + m * K + base;",
+                                             "const double *xs = x + m * K;",
+                                             ["test_oracle_hadamard.py"]),
     "bf16_rounding_truncates": ("    double r = rint(ldexp(a, 7 - E)); /* in [128, 256] */",
                                 "    double r = floor(ldexp(a, 7 - E)); /* in [128, 256] */",
                                 ["test_oracle_fp8row.py"]),
