@@ -11,7 +11,8 @@ import ctypes as C
 import os
 
 __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
-           "dequantize_rows", "dequantize_row", "gemv", "quantize_rows", "nvfp4_validate_rows",
+           "dequantize_rows", "dequantize_row", "gemv", "quantize_rows", "hadamard_rows",
+           "gemv_hadamard", "nvfp4_validate_rows",
            "nvfp4_dequantize_rows", "gemv_nvfp4", "nvfp4_global_scale", "nvfp4_quantize_rows",
            "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row", "fp8row_quantize_rows",
            "library_path", "status_string", "lib"]
@@ -21,6 +22,7 @@ PN4T = 125
 GROUP = {PN3T: 80, PN4T: 64}
 MAX_TOKENS = 4         # NVFP4 and row-scaled E4M3 GEMV
 GEMV_MAX_TOKENS = 16   # PN GEMV
+GEMV_HADAMARD_MAX_TOKENS = 2  # PN GEMV with the rotation fused
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpn.so")
@@ -39,6 +41,8 @@ _SIGS = {
     "pn_dequantize_row": (_I32, [_I32, _P, _I64, _P, _P]),
     "pn_gemv": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _P]),
     "pn_quantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
+    "pn_hadamard_rows": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
+    "pn_gemv_hadamard": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
     "pn_nvfp4_validate_rows": (_I32, [_P, _F, _I64, _I64, _P, _P]),
     "pn_nvfp4_dequantize_rows": (_I32, [_P, _P, _F, _I64, _I64, _P, _P]),
     "pn_gemv_nvfp4": (_I32, [_P, _P, _F, _I64, _I64, _P, _I64, _P, _P]),
@@ -140,6 +144,34 @@ def gemv(type_, W, N, K, x, y, M=None, stream=None):
 def gemv_ptr(type_, W_ptr, N, K, x_ptr, M, y_ptr, stream_handle):
     """Raw-pointer form for timing loops: returns the status instead of raising."""
     return _lib.pn_gemv(type_, W_ptr, N, K, x_ptr, M, y_ptr, stream_handle)
+
+
+def hadamard_rows(x, B, out, M=None, K=None, stream=None):
+    """out[M, K] <- x rotated by the orthonormal Walsh-Hadamard matrix on slices of B elements."""
+    import torch
+    _dev(x, "x", torch.float32)
+    _dev(out, "out", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    if K is None:
+        K = x.shape[-1]
+    _check(_lib.pn_hadamard_rows(_ptr(x), M, K, B, _ptr(out), _stream(stream)), "pn_hadamard_rows")
+
+
+def gemv_hadamard(type_, W, N, K, x, B, y, M=None, stream=None):
+    """y[M, N] <- W[N, K] . (H x)[M, K]^T, the rotation fused into the GEMV (M <= 2)."""
+    import torch
+    _dev(x, "x", torch.float32)
+    _dev(y, "y", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    _check(_lib.pn_gemv_hadamard(type_, _ptr(W), N, K, _ptr(x), M, B, _ptr(y), _stream(stream)),
+           "pn_gemv_hadamard")
+
+
+def gemv_hadamard_ptr(type_, W_ptr, N, K, x_ptr, M, B, y_ptr, stream_handle):
+    """Raw-pointer form for timing loops: returns the status instead of raising."""
+    return _lib.pn_gemv_hadamard(type_, W_ptr, N, K, x_ptr, M, B, y_ptr, stream_handle)
 
 
 def quantize_rows(type_, w, W, status=None, stream=None):

@@ -181,6 +181,7 @@ const char *pn_status_string(int status)
     case PN_ERR_ALIGN: return "pointer misaligned";
     case PN_ERR_HIP: return "HIP runtime error";
     case PN_ERR_DEVICE: return "current device is not gfx950";
+    case PN_ERR_HADAMARD: return "Hadamard slice size is not a power of two in 2..16384 dividing K";
     default: return "unknown status";
     }
 }

@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "pn_common.h"
+#include "pn_hadamard.h"
 
 namespace pn {
 
@@ -473,12 +474,16 @@ constexpr int kFlatWaves = 8;  // waves per workgroup of the flat kernel (two pe
 //
 // Staging: all x loads of the workgroup are issued before the first weight loads, so waiting for
 // x never waits for weights (the memory counter retires loads in order).
-template <int TYPE, int M, int R, int D, int QPT>
+// ROT: x is first rotated, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the Hadamard
+// rotation of "Files that use PN", as read in pn_hadamard.h), in the registers that hold it
+// (stages 0-7) and through the x area of LDS (stages 8 and up), before it is staged.
+template <int TYPE, int M, int R, int D, int QPT, bool ROT>
 __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
                                                             const float *__restrict__ x, int64_t K,
                                                             float *__restrict__ y, int64_t gq,
-                                                            int gr, int x_vec4, int fnum)
+                                                            int gr, int x_vec4, int fnum, int hL,
+                                                            float hscale)
 {
     using F = Fmt<TYPE>;
     constexpr int V = ((M * R + 3) / 4) * 4;
@@ -516,7 +521,8 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     const int nq = (total + kFlatWaves * 64 - 1) / (kFlatWaves * 64);
     // Each workgroup walks x from its own starting block (rotated by the workgroup index) so that
     // the CUs of an XCD do not all request the same lines of x, i.e. the same L2 channel, at once.
-    const int rot = (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB;
+    // (not with ROT: its waves must hold whole 256-element pieces of x)
+    const int rot = ROT ? 0 : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB;
     auto rotq = [&](int q) { q += rot; return q >= total ? q - total : q; };
     auto token_of = [](int q, int per) {  // q / per for q < M * per, without a division
         int m = 0;
@@ -575,6 +581,37 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
 #pragma unroll
     for (int p = 0; p < D - 1; p++)
         load_next(buf[p], p);
+
+    // 2b. the rotation (ROT), while those loads are in flight: lanes hold consecutive float4 of x,
+    // so a wave holds 256 consecutive elements at a multiple of 256, and slices never straddle
+    // tokens (B divides K). Lanes past the end hold a clamped copy, in slices of their own.
+    if constexpr (ROT) {
+#pragma unroll
+        for (int u = 0; u < QPT; u++)
+            if (u < nq)
+                hadamard_wave(xv[u], hL, hscale);
+        if (hL > 8) {  // uniform
+            lds_f32 *hb = (lds_f32 *)lds;
+#pragma unroll
+            for (int u = 0; u < QPT; u++) {
+                const int q = (int)threadIdx.x + u * kFlatWaves * 64;
+                if (u < nq && q < total) {
+                    hb[4 * q + 0] = xv[u].x;
+                    hb[4 * q + 1] = xv[u].y;
+                    hb[4 * q + 2] = xv[u].z;
+                    hb[4 * q + 3] = xv[u].w;
+                }
+            }
+            hadamard_lds_stages<kFlatWaves * 64>(hb, 4 * total, hL, hscale);
+#pragma unroll
+            for (int u = 0; u < QPT; u++) {
+                const int q = min((int)threadIdx.x + u * kFlatWaves * 64, total - 1);
+                if (u < nq)
+                    xv[u] = make_float4(hb[4 * q], hb[4 * q + 1], hb[4 * q + 2], hb[4 * q + 3]);
+            }
+            __syncthreads();  // step 3 writes the same area
+        }
+    }
 
     // 3. stage x: pn4t x * 2^9 in k order, the block's plain sum at offset G (a DPP row of 16
     // lanes holds one block); pn3t x * 2^(24-p), sums in a second pass.
@@ -806,12 +843,15 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
 // pn4t keeps fp32 * 2^9 in slot order (fp8-conversion decode). A wave streams its rows one at a
 // time through a ring of D row buffers (D - 1 rows of loads in flight) and reduces 4 / M rows at
 // once with the transposed reduction.
-template <int TYPE, int M, int D>
+// ROT: x is first rotated into LDS, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the
+// Hadamard rotation of "Files that use PN", as read in pn_hadamard.h); the staging then reads x'.
+template <int TYPE, int M, int D, bool ROT>
 __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
                                                             const float *__restrict__ x, int64_t K,
                                                             float *__restrict__ y, RowSplit sp,
-                                                            int x_vec4, int fnum)
+                                                            int x_vec4, int fnum, int hL,
+                                                            float hscale)
 {
     using F = Fmt<TYPE>;
     constexpr int RPR = 4 / M;  // rows per reduction
@@ -832,16 +872,34 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     const int bb = ((threadIdx.x >> 3) + blockIdx.x * 5) & 63, i = threadIdx.x & 7;
     const bool have = bb < nb;
     float xv[M][F::CPW];
+    auto load_x = [&](const float *xs, int vec) {
 #pragma unroll
-    for (int m = 0; m < M; m++) {
-        const float *src = x + (int64_t)m * K + (int64_t)min(bb, nb - 1) * F::G + i * F::CPW;
+        for (int m = 0; m < M; m++) {
+            const float *src = xs + (int64_t)m * K + (int64_t)min(bb, nb - 1) * F::G + i * F::CPW;
 #pragma unroll
-        for (int t = 0; t < F::CPW; t += 2) {
-            const float2 p = x_vec4 ? *reinterpret_cast<const float2 *>(src + t)
-                                    : make_float2(src[t], src[t + 1]);
-            xv[m][t] = have ? p.x : 0.0f;
-            xv[m][t + 1] = have ? p.y : 0.0f;
+            for (int t = 0; t < F::CPW; t += 2) {
+                const float2 p = vec ? *reinterpret_cast<const float2 *>(src + t)
+                                     : make_float2(src[t], src[t + 1]);
+                xv[m][t] = have ? p.x : 0.0f;
+                xv[m][t + 1] = have ? p.y : 0.0f;
+            }
         }
+    };
+    // ROT: x as consecutive float4 per lane (a wave holds 256 consecutive elements), at most
+    // 64 blocks of M tokens over 512 lanes
+    constexpr int HQ = ROT ? (M * 64 * F::G / 4 + 511) / 512 : 1;
+    const int total4 = (int)(M * K / 4), nh = (total4 + 511) >> 9;
+    float4 hv[HQ];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int u = 0; u < HQ; u++) {
+            const float *src = x + 4 * min((int)threadIdx.x + 512 * u, total4 - 1);
+            if (u < nh)
+                hv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
+                               : make_float4(src[0], src[1], src[2], src[3]);
+        }
+    } else {
+        load_x(x, x_vec4);
     }
 
     // Loads are never inside a branch (row indices are clamped to the wave's last row; a clamped
@@ -851,6 +909,29 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
 #pragma unroll
     for (int p = 0; p < D - 1; p++)
         load_block(wbase + (int64_t)min(p, last) * row_bytes, buf[p]);
+
+    if constexpr (ROT) {  // the rotation, while the weight loads are in flight
+        extern __shared__ float4 hx_dyn[];  // M * K floats
+        lds_f32 *hb = (lds_f32 *)(float *)hx_dyn;
+#pragma unroll
+        for (int u = 0; u < HQ; u++) {
+            const int q = (int)threadIdx.x + 512 * u;
+            if (u < nh) {
+                hadamard_wave(hv[u], hL, hscale);
+                if (q < total4) {
+                    hb[4 * q + 0] = hv[u].x;
+                    hb[4 * q + 1] = hv[u].y;
+                    hb[4 * q + 2] = hv[u].z;
+                    hb[4 * q + 3] = hv[u].w;
+                }
+            }
+        }
+        if (hL > 8)
+            hadamard_lds_stages<512>(hb, 4 * total4, hL, hscale);
+        else
+            __syncthreads();
+        load_x((const float *)hx_dyn, 1);
+    }
 
     // The block's amax and sum by a DPP butterfly over its 8 lanes; the staged words go to LDS,
     // then every lane lifts its own block into registers.
@@ -1048,28 +1129,39 @@ static int launch_lds(const uint8_t *W, int64_t N, int64_t K, const float *x, fl
     return launch_status();
 }
 
-template <int TYPE, int M, int D>
+template <int TYPE, int M, int D, bool ROT = false>
 static int launch_xreg(const uint8_t *W, int64_t N, int64_t K, const float *x, float *y,
-                       hipStream_t s)
+                       hipStream_t s, int hL = 0, float hscale = 1.0f)
 {
     using F = Fmt<TYPE>;
     const int nb = (int)(K / F::G);
     const int grid = (int)std::min<int64_t>(num_cus(), (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
+    auto kern = pn_gemv_xreg_kernel<TYPE, M, D, ROT>;
+    const size_t lds = ROT ? (size_t)M * K * sizeof(float) : 0;  // the rotated x
+    if (ROT) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)((size_t)M * 64 * F::G * sizeof(float))) != hipSuccess)
+                return PN_ERR_HIP;
+            attr_set = true;
+        }
+    }
     // 512 threads: the cooperative staging gives each thread one word of one block
-    hipLaunchKernelGGL((pn_gemv_xreg_kernel<TYPE, M, D>), dim3((unsigned)grid), dim3(512), 0, s, W,
-                       N, nb, (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), vec4,
-                       older_share(12));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, W, N, nb,
+                       (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), vec4,
+                       older_share(12), hL, hscale);
     return launch_status();
 }
 
 constexpr int kNotApplicable = 1;  // internal: the flat kernel does not take this shape
 
-template <int TYPE, int M, int QPT>
+template <int TYPE, int M, int QPT, bool ROT>
 static int launch_flat_q(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, float *y,
-                         int grid, int64_t NP, size_t lds, hipStream_t s)
+                         int grid, int64_t NP, size_t lds, hipStream_t s, int hL, float hscale)
 {
-    auto kern = pn_gemv_flat_kernel<TYPE, M, 2, 4, QPT>;
+    auto kern = pn_gemv_flat_kernel<TYPE, M, 2, 4, QPT, ROT>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1080,15 +1172,15 @@ static int launch_flat_q(const uint8_t *W, int64_t N, int nb, const float *x, in
     const int vec4 = aligned(x, 16) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kFlatWaves), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, y, NP / grid, (int)(NP % grid), vec4,
-                       older_share(10));
+                       older_share(10), hL, hscale);
     return launch_status();
 }
 
 // The flat kernel takes rows of at least 64 blocks whose x (M tokens) fits in LDS at once and
 // whose staging needs at most 32 16-byte loads per thread; otherwise kNotApplicable.
-template <int TYPE, int M>
+template <int TYPE, int M, bool ROT = false>
 static int launch_flat(const uint8_t *W, int64_t N, int64_t K, const float *x, float *y,
-                       hipStream_t s)
+                       hipStream_t s, int hL = 0, float hscale = 1.0f)
 {
     using F = Fmt<TYPE>;
     constexpr int R = 2, V = ((M * R + 3) / 4) * 4;
@@ -1102,10 +1194,10 @@ static int launch_flat(const uint8_t *W, int64_t N, int64_t K, const float *x, f
     if (nb < 64 || lds > (size_t)kMaxLds || need > 32 || per_wg * nb >= (int64_t(1) << 30))
         return kNotApplicable;
     if (need <= 8)
-        return launch_flat_q<TYPE, M, 8>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
+        return launch_flat_q<TYPE, M, 8, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
     if (need <= 16)
-        return launch_flat_q<TYPE, M, 16>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
-    return launch_flat_q<TYPE, M, 32>(W, N, (int)nb, x, K, y, grid, NP, lds, s);
+        return launch_flat_q<TYPE, M, 16, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
+    return launch_flat_q<TYPE, M, 32, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
 }
 
 // Rows in flight per wave in the short-row kernel at M = 1 (ring size 4 or 8); PN_GEMV_DEPTH
@@ -1154,9 +1246,62 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
     return launch_lds<TYPE, 4, 2, 2>(W, N, K, x, y, s);
 }
 
+// The GEMV over Hadamard-rotated x, with the rotation fused into the x staging of the register
+// kernel (rows of at most 64 blocks) and the long-row kernel (x of the call fits its LDS area).
+template <int TYPE>
+static int dispatch_hadamard(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M,
+                             float *y, int hL, float hscale, hipStream_t s)
+{
+    const bool short_rows = K / Fmt<TYPE>::G <= 64;
+    int st;
+    if (M == 1) {
+        if (short_rows)
+            return launch_xreg<TYPE, 1, 4, true>(W, N, K, x, y, s, hL, hscale);
+        if ((st = launch_flat<TYPE, 1, true>(W, N, K, x, y, s, hL, hscale)) != kNotApplicable)
+            return st;
+        return PN_ERR_SHAPE;
+    }
+    if (short_rows)
+        return launch_xreg<TYPE, 2, 2, true>(W, N, K, x, y, s, hL, hscale);
+    if ((st = launch_flat<TYPE, 2, true>(W, N, K, x, y, s, hL, hscale)) != kNotApplicable)
+        return st;
+    return PN_ERR_SHAPE;
+}
+
+int hadamard_log(int64_t B, int64_t K);
+float hadamard_scale(int L);
+
 }  // namespace pn
 
 using namespace pn;
+
+extern "C" int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x,
+                                int64_t M, int64_t B, float *y, void *stream)
+{
+    if (type != PN_TYPE_PN3T && type != PN_TYPE_PN4T)
+        return PN_ERR_TYPE;
+    if (N < 0 || pn_row_bytes(type, K) == 0)
+        return PN_ERR_SHAPE;
+    if (M < 0 || M > PN_GEMV_HADAMARD_MAX_TOKENS)
+        return PN_ERR_TOKENS;
+    const int L = hadamard_log(B, K);
+    if (L < 0)
+        return PN_ERR_HADAMARD;
+    if (N == 0 || M == 0)
+        return PN_OK;
+    if (!W || !x || !y)
+        return PN_ERR_NULL;
+    if (!aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4))
+        return PN_ERR_ALIGN;
+    int st = check_device();
+    if (st != PN_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const float hs = hadamard_scale(L);
+    if (type == PN_TYPE_PN3T)
+        return dispatch_hadamard<PN_TYPE_PN3T>((const uint8_t *)W, N, K, x, M, y, L, hs, s);
+    return dispatch_hadamard<PN_TYPE_PN4T>((const uint8_t *)W, N, K, x, M, y, L, hs, s);
+}
 
 extern "C" int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                        float *y, void *stream)

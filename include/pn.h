@@ -50,12 +50,14 @@ enum {
     PN_ERR_ALIGN = -5,  /* W not 2-byte aligned, x / y / w not 4-byte aligned, bf16 x not 2-byte,
                            NVFP4 codes not 8-byte aligned */
     PN_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
-    PN_ERR_DEVICE = -7  /* the current device is not gfx950 */
+    PN_ERR_DEVICE = -7, /* the current device is not gfx950 */
+    PN_ERR_HADAMARD = -8 /* Hadamard slice size B is not a power of two in 2..16384 dividing K */
 };
 
 /* Maximum tokens per GEMV call. */
 #define PN_MAX_TOKENS 4        /* NVFP4 and row-scaled E4M3 GEMV */
 #define PN_GEMV_MAX_TOKENS 16  /* PN GEMV */
+#define PN_GEMV_HADAMARD_MAX_TOKENS 2  /* PN GEMV with the rotation fused */
 
 /* Bytes of one PN row of K weights: 34*K/80 (pn3t) or 34*K/64 (pn4t); 0 if K is not a positive
  * multiple of the block size or type is unknown. Host-only, no device work. */
@@ -108,6 +110,33 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  * call. */
 int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
             void *stream);
+
+/* ---- Hadamard-rotated activations ("PN weight format", "Files that use PN") ----------------
+ * The page states that the model rotates the activations that reach the PN weights with a
+ * Hadamard transform, done by the engine, and fixes neither its order nor its normalisation.
+ * Reading used here: each row of x[M, K] is cut into consecutive slices of B elements (B a power
+ * of two, 2 <= B <= 16384, dividing K; otherwise PN_ERR_HADAMARD), and each slice is multiplied by
+ * the orthonormal Sylvester-ordered Walsh-Hadamard matrix H_B / sqrt(B),
+ * H_B[i][j] = (-1)^popcount(i & j):  x'[m, s*B + i] = sum_j H_B[i][j] x[m, s*B + j] / sqrt(B).
+ * Computed in fp32 as log2(B) butterfly stages and one multiply by fp32(1/sqrt B) (exact for even
+ * log2 B): |x' - x'_exact| <= (log2(B) + 2) * 2^-24 * sum_j |x[m, s*B + j]| / sqrt(B) per element
+ * (up to terms in 2^-48). Deterministic. */
+
+/* out[M, K] = the rotation of x[M, K] (fp32, row-major). K must be a multiple of 4
+ * (PN_ERR_SHAPE). out may equal x (in place); otherwise they must not overlap. */
+int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out, void *stream);
+
+/* y = W x' for M = 1..2 tokens: the PN GEMV (pn_gemv) over the rotated x, the rotation fused into
+ * the kernels' x staging (each workgroup rotates x in its registers and LDS while its first
+ * weight loads are in flight; x itself is not modified). Arguments as pn_gemv, plus B as in
+ * pn_hadamard_rows. M outside 0..2 gives PN_ERR_TOKENS. The fused staging takes rows of at most
+ * 64 blocks, and longer rows whose x (M * K floats) fits the long-row kernel's LDS area (K up to
+ * about 34,000 at one token, 17,000 at two); other shapes give PN_ERR_SHAPE: rotate with
+ * pn_hadamard_rows, then call pn_gemv. Gives the same bits as pn_hadamard_rows followed by pn_gemv
+ * on the same shape (the same transform, then the same kernel), so the accuracy of pn_gemv
+ * applies to the rotated x, plus the rotation's own error above. */
+int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
+                     int64_t B, float *y, void *stream);
 
 /* ---- PN reference quantizer ("PN weight format", "Reference quantizer") ---------------------
  * Quantizes fp32 w[nrows, K] (row-major) into PN rows W (nrows * pn_row_bytes bytes), one group of

@@ -67,5 +67,21 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_gemv_fp8row(fake, fake, 4, 32, fake, 5, fake, None) == -3
     assert L.pn_gemv_nvfp4(P(0x1004), fake, C.c_float(1.0), 4, 32, fake, 1, fake, None) == -5
     assert L.pn_nvfp4_validate_rows(fake, C.c_float(1.0), 4, 8, fake, None) == -2
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+    # Hadamard rotation and the fused GEMV
+    assert L.pn_hadamard_rows(fake, 1, 640, 3, fake, None) == -8       # B not a power of two
+    assert L.pn_hadamard_rows(fake, 1, 640, 256, fake, None) == -8     # B does not divide K
+    assert L.pn_hadamard_rows(fake, 1, 32768, 32768, fake, None) == -8  # B above 16384
+    assert L.pn_hadamard_rows(fake, 1, 640, 1, fake, None) == -8       # B = 1
+    assert L.pn_hadamard_rows(fake, 1, 6, 2, fake, None) == -2         # K not a multiple of 4
+    assert L.pn_hadamard_rows(fake, -1, 640, 64, fake, None) == -2
+    assert L.pn_hadamard_rows(fake, 0, 640, 64, fake, None) == 0       # M = 0: no-op
+    assert L.pn_hadamard_rows(None, 1, 640, 64, fake, None) == -4
+    assert L.pn_hadamard_rows(fake, 1, 640, 64, P(0x1002), None) == -5
+    assert L.pn_gemv_hadamard(124, fake, 4, 640, fake, 3, 64, fake, None) == -3  # M above 2
+    assert L.pn_gemv_hadamard(124, fake, 4, 640, fake, 1, 256, fake, None) == -8
+    assert L.pn_gemv_hadamard(124, fake, 4, 650, fake, 1, 64, fake, None) == -2
+    assert L.pn_gemv_hadamard(7, fake, 4, 640, fake, 1, 64, fake, None) == -1
+    assert L.pn_gemv_hadamard(124, fake, 0, 640, fake, 1, 64, fake, None) == 0
+    assert L.pn_gemv_hadamard(124, None, 4, 640, fake, 1, 64, fake, None) == -4
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert isinstance(pn.status_string(s), str)
