@@ -190,8 +190,30 @@ def extra_workloads(pn, torch, dev, reps, warmup):
             tot_us += e["us"]
         out[f"layer_set_M{M}"] = {"GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
                                    "per_matrix_us": {k: v["us"] for k, v in per.items()}}
-    del mats
     log("[bench] extra: layer set done")
+
+    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1, 2, on the same
+    # layer set, against the plain launches above; and the rotation on its own
+    xr = torch.empty((4, 17408), dtype=torch.float32, device=dev)
+    for M in (1, 2):
+        per, tot_b, tot_us, tot_plain = {}, 0, 0.0, 0.0
+        for name, typ, N, K, Ws in mats:
+            us = time_launches(torch, stream, lambda c: check(pn.gemv_hadamard_ptr(
+                typ, Ws[c].data_ptr(), N, K, xs[K].data_ptr(), M, 1024, y.data_ptr(), sh),
+                "pn_gemv_hadamard"), len(Ws), reps, warmup)
+            per[name] = round(us, 3)
+            tot_b += Ws[0].numel()
+            tot_us += us
+            tot_plain += out[f"layer_set_M{M}"]["per_matrix_us"][name]
+        out[f"hadamard1024_layer_set_M{M}"] = {
+            "GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
+            "plain_us": round(tot_plain, 2), "per_matrix_us": per}
+    for M, K in ((1, 5120), (1, 17408), (2, 17408), (4, 17408)):
+        us = time_launches(torch, stream, lambda c: check(pn.lib().pn_hadamard_rows(
+            xs[K].data_ptr(), M, K, 1024, xr.data_ptr(), sh), "pn_hadamard_rows"), 1, reps, warmup)
+        out[f"hadamard_rows_1024_M{M}_K{K}_us"] = round(us, 3)
+    del mats
+    log("[bench] extra: Hadamard done")
 
     # NVFP4 17408 x 5120, clip-search quantized on the GPU, x bf16, M = 1..4, 11 copies
     N, K = 17408, 5120
@@ -280,7 +302,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured configurations (pn4t 5120x6144, layer set at "
-                         "M=1..4, NVFP4 at M=1..4, row-scaled E4M3 head at M=1..4)")
+                         "M=1..4, the layer set with Hadamard-rotated x at M=1,2, NVFP4 at M=1..4, "
+                         "row-scaled E4M3 head at M=1..4)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
     args = ap.parse_args()

@@ -521,8 +521,11 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     const int nq = (total + kFlatWaves * 64 - 1) / (kFlatWaves * 64);
     // Each workgroup walks x from its own starting block (rotated by the workgroup index) so that
     // the CUs of an XCD do not all request the same lines of x, i.e. the same L2 channel, at once.
-    // (not with ROT: its waves must hold whole 256-element pieces of x)
-    const int rot = ROT ? 0 : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB;
+    // (with ROT by whole 256-element pieces, which its waves transform: 64 float4 units, where
+    // x holds a whole number of them)
+    const int rot = !ROT ? (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB
+                    : (total & 63) ? 0
+                                   : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(total >> 6)) * 64;
     auto rotq = [&](int q) { q += rot; return q >= total ? q - total : q; };
     auto token_of = [](int q, int per) {  // q / per for q < M * per, without a division
         int m = 0;
@@ -540,6 +543,8 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
             const float *src = x + (int64_t)m * K + 4 * (q - m * per_tok);
             xv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
                            : make_float4(src[0], src[1], src[2], src[3]);
+        } else if (ROT) {
+            xv[u] = make_float4(0.f, 0.f, 0.f, 0.f);  // transformed with the rest, never staged
         }
     }
 
@@ -586,16 +591,18 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     // so a wave holds 256 consecutive elements at a multiple of 256, and slices never straddle
     // tokens (B divides K). Lanes past the end hold a clamped copy, in slices of their own.
     if constexpr (ROT) {
+        // four float4 at a time (their lane exchanges in flight together), only as many as hold x
 #pragma unroll
-        for (int u = 0; u < QPT; u++)
-            if (u < nq)
-                hadamard_wave(xv[u], hL, hscale);
+        for (int g0 = 0; g0 < QPT; g0 += 4)
+            if (g0 < nq)  // uniform
+                hadamard_wave_n<4>(*reinterpret_cast<float4(*)[4]>(&xv[g0]), hL, hscale);
         if (hL > 8) {  // uniform
             lds_f32 *hb = (lds_f32 *)lds;
 #pragma unroll
             for (int u = 0; u < QPT; u++) {
-                const int q = (int)threadIdx.x + u * kFlatWaves * 64;
-                if (u < nq && q < total) {
+                const int q0 = (int)threadIdx.x + u * kFlatWaves * 64;
+                if (u < nq && q0 < total) {
+                    const int q = rotq(q0);
                     hb[4 * q + 0] = xv[u].x;
                     hb[4 * q + 1] = xv[u].y;
                     hb[4 * q + 2] = xv[u].z;
@@ -605,7 +612,7 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
             hadamard_lds_stages<kFlatWaves * 64>(hb, 4 * total, hL, hscale);
 #pragma unroll
             for (int u = 0; u < QPT; u++) {
-                const int q = min((int)threadIdx.x + u * kFlatWaves * 64, total - 1);
+                const int q = rotq(min((int)threadIdx.x + u * kFlatWaves * 64, total - 1));
                 if (u < nq)
                     xv[u] = make_float4(hb[4 * q], hb[4 * q + 1], hb[4 * q + 2], hb[4 * q + 3]);
             }
@@ -889,14 +896,21 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     // 64 blocks of M tokens over 512 lanes
     constexpr int HQ = ROT ? (M * 64 * F::G / 4 + 511) / 512 : 1;
     const int total4 = (int)(M * K / 4), nh = (total4 + 511) >> 9;
+    // workgroups start at different 256-element pieces of x (as the plain staging rotates its
+    // blocks), so that the CUs of an XCD do not request the same lines at once
+    const int hrot = (!ROT || (total4 & 63)) ? 0
+                     : (int)(((uint32_t)blockIdx.x * 5u) % (uint32_t)(total4 >> 6)) * 64;
+    auto hq = [&](int q) { q += hrot; return q >= total4 ? q - total4 : q; };
     float4 hv[HQ];
     if constexpr (ROT) {
 #pragma unroll
         for (int u = 0; u < HQ; u++) {
-            const float *src = x + 4 * min((int)threadIdx.x + 512 * u, total4 - 1);
+            const float *src = x + 4 * hq(min((int)threadIdx.x + 512 * u, total4 - 1));
             if (u < nh)
                 hv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
                                : make_float4(src[0], src[1], src[2], src[3]);
+            else
+                hv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     } else {
         load_x(x, x_vec4);
@@ -913,12 +927,13 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     if constexpr (ROT) {  // the rotation, while the weight loads are in flight
         extern __shared__ float4 hx_dyn[];  // M * K floats
         lds_f32 *hb = (lds_f32 *)(float *)hx_dyn;
+        hadamard_wave_n<HQ>(hv, hL, hscale);
 #pragma unroll
         for (int u = 0; u < HQ; u++) {
-            const int q = (int)threadIdx.x + 512 * u;
+            const int q0 = (int)threadIdx.x + 512 * u;
             if (u < nh) {
-                hadamard_wave(hv[u], hL, hscale);
-                if (q < total4) {
+                if (q0 < total4) {
+                    const int q = hq(q0);
                     hb[4 * q + 0] = hv[u].x;
                     hb[4 * q + 1] = hv[u].y;
                     hb[4 * q + 2] = hv[u].z;

@@ -15,11 +15,15 @@
 // whose constant carries one more rounding when L is odd).
 //
 // Layout: a lane holds 4 consecutive elements (one float4), so stages 0-1 run in its registers;
-// the 64 lanes of a wave hold 256 consecutive elements, so stages 2-7 pair lanes lane ^ 2^(s-2)
-// (ds_swizzle within 32 lanes, ds_bpermute across the halves); stages 8 and up pair elements
-// held by other waves and go through LDS, 1-4 stages per pass.
+// the 64 lanes of a wave hold 256 consecutive elements, so stages 2-7 pair lanes lane ^ 2^(s-2),
+// all on the vector ALU: DPP moves for lane xor 1, 2, 4 (a half-row mirror, i -> i ^ 7, then a
+// quad reverse, i -> i ^ 3) and 8 (a row rotation by 8); gfx950's permlane16/32 swaps for xor 16
+// and 32, two registers at a time (swap, add and subtract, swap back). Stages 8 and up pair
+// elements held by other waves and go through LDS, 1-3 stages per pass.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "pn_common.h"
 
 namespace pn {
 
@@ -27,29 +31,57 @@ typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kHadamardMaxLog = 14;  // B <= 16384
 
+// The value of lane ^ MASK (MASK 1, 2, 4 or 8), by DPP within rows of 16 lanes.
 template <int MASK>
 __device__ __forceinline__ float hx_partner(float v)
 {
-    if constexpr (MASK == 32)
-        return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2),
-                                                           __float_as_int(v)));
-    else  // bit-mask swizzle: and 0x1F, or 0, xor MASK
-        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MASK << 10) | 0x1F));
+    if constexpr (MASK == 1)
+        return PN_DPP(v, 0xB1);  // quad_perm [1,0,3,2]
+    else if constexpr (MASK == 2)
+        return PN_DPP(v, 0x4E);  // quad_perm [2,3,0,1]
+    else if constexpr (MASK == 4)
+        return PN_DPP(PN_DPP(v, 0x141), 0x1B);  // row_half_mirror, then quad_perm [3,2,1,0]
+    else
+        return PN_DPP(v, 0x128);  // row_ror:8
 }
 
-// The lower element of a pair takes a + b, the upper a - b (its partner holds a).
+// One butterfly stage across lanes lane ^ MASK: the lower lane of a pair takes a + b, the upper
+// a - b (a held by the lower lane). For MASK 16 and 32 two registers go together: after a swap
+// of rows (16) or halves (32) between them, one holds the lower halves of both and the other the
+// upper halves; their sum and difference, swapped back, are the two results.
+template <int MASK>
+__device__ __forceinline__ void hx_swap_bfly(float &a, float &b)
+{
+    if constexpr (MASK == 32)
+        swap32(a, b);
+    else
+        swap16(a, b);
+    const float s = a + b, d = a - b;
+    a = s;
+    b = d;
+    if constexpr (MASK == 32)
+        swap32(a, b);
+    else
+        swap16(a, b);
+}
+
 template <int MASK>
 __device__ __forceinline__ void hx_lane_stage(float4 &v, bool upper)
 {
-    float p;
-    p = hx_partner<MASK>(v.x);
-    v.x = upper ? p - v.x : p + v.x;
-    p = hx_partner<MASK>(v.y);
-    v.y = upper ? p - v.y : p + v.y;
-    p = hx_partner<MASK>(v.z);
-    v.z = upper ? p - v.z : p + v.z;
-    p = hx_partner<MASK>(v.w);
-    v.w = upper ? p - v.w : p + v.w;
+    if constexpr (MASK >= 16) {
+        hx_swap_bfly<MASK>(v.x, v.y);
+        hx_swap_bfly<MASK>(v.z, v.w);
+    } else {
+        float p;
+        p = hx_partner<MASK>(v.x);
+        v.x = upper ? p - v.x : p + v.x;
+        p = hx_partner<MASK>(v.y);
+        v.y = upper ? p - v.y : p + v.y;
+        p = hx_partner<MASK>(v.z);
+        v.z = upper ? p - v.z : p + v.z;
+        p = hx_partner<MASK>(v.w);
+        v.w = upper ? p - v.w : p + v.w;
+    }
 }
 
 // Stages 0 .. min(L, 8) - 1 on the float4 of this lane: elements 4 * lane .. 4 * lane + 3 of the
@@ -99,38 +131,94 @@ __device__ __forceinline__ void hadamard_wave(float4 &v, int L, float scale)
     }
 }
 
-// R stages s .. s+R-1 over buf[0, total) in LDS: groups of 2^R elements at stride 2^s.
+// The same stages on N float4 at once, stage by stage, with no branch between them: the
+// compiler issues every lane exchange of a stage together and waits once (a per-float4 order
+// leaves a chain of dependent exchanges on the critical path).
+template <int N>
+__device__ __forceinline__ void hadamard_wave_n(float4 (&v)[N], int L, float scale)
+{
+    const unsigned lane = __lane_id();
+    if (L >= 1) {
+#pragma unroll
+        for (int u = 0; u < N; u++) {
+            const float a = v[u].x + v[u].y, b = v[u].x - v[u].y;
+            const float c = v[u].z + v[u].w, d = v[u].z - v[u].w;
+            v[u] = make_float4(a, b, c, d);
+        }
+    }
+    if (L >= 2) {
+#pragma unroll
+        for (int u = 0; u < N; u++) {
+            const float a = v[u].x + v[u].z, c = v[u].x - v[u].z;
+            const float b = v[u].y + v[u].w, d = v[u].y - v[u].w;
+            v[u] = make_float4(a, b, c, d);
+        }
+    }
+#define PN_HX_STAGE(LMIN, MASK)                                                                    \
+    if (L >= LMIN) {                                                                               \
+        _Pragma("unroll") for (int u = 0; u < N; u++) hx_lane_stage<MASK>(v[u], lane & MASK);      \
+    }
+    PN_HX_STAGE(3, 1)
+    PN_HX_STAGE(4, 2)
+    PN_HX_STAGE(5, 4)
+    PN_HX_STAGE(6, 8)
+    PN_HX_STAGE(7, 16)
+    PN_HX_STAGE(8, 32)
+#undef PN_HX_STAGE
+    if (L <= 8) {
+#pragma unroll
+        for (int u = 0; u < N; u++)
+            v[u] = make_float4(v[u].x * scale, v[u].y * scale, v[u].z * scale, v[u].w * scale);
+    }
+}
+
+// R stages s .. s+R-1 over buf[0, total) in LDS: groups of 2^R elements at stride 2^s. A thread
+// takes 2 groups at a time (NT apart): all their reads, then the butterflies, then the writes of
+// the groups that exist (a clamped group past the end is read, never written).
 template <int NT, int R>
 __device__ __forceinline__ void hx_lds_pass(lds_f32 *buf, int total, int s, bool last, float scale)
 {
-    constexpr int E = 1 << R;
+    constexpr int E = 1 << R, G4 = 2;
     const int ng = total >> R;
     const int low = (1 << s) - 1;
-    for (int q = (int)threadIdx.x; q < ng; q += NT) {
-        const int base = ((q >> s) << (s + R)) | (q & low);
-        float v[E];
+    for (int q0 = (int)threadIdx.x; q0 < ng; q0 += G4 * NT) {
+        float v[G4][E];
+        int base[G4];
 #pragma unroll
-        for (int j = 0; j < E; j++)
-            v[j] = buf[base + (j << s)];
-#pragma unroll
-        for (int b = 0; b < R; b++) {
-#pragma unroll
-            for (int j = 0; j < E; j++) {
-                if (!(j & (1 << b))) {
-                    const float lo = v[j], hi = v[j | (1 << b)];
-                    v[j] = lo + hi;
-                    v[j | (1 << b)] = lo - hi;
-                }
-            }
-        }
-        if (last) {
+        for (int g = 0; g < G4; g++) {
+            const int q = min(q0 + g * NT, ng - 1);
+            base[g] = ((q >> s) << (s + R)) | (q & low);
 #pragma unroll
             for (int j = 0; j < E; j++)
-                v[j] *= scale;
+                v[g][j] = buf[base[g] + (j << s)];
         }
 #pragma unroll
-        for (int j = 0; j < E; j++)
-            buf[base + (j << s)] = v[j];
+        for (int g = 0; g < G4; g++) {
+#pragma unroll
+            for (int b = 0; b < R; b++) {
+#pragma unroll
+                for (int j = 0; j < E; j++) {
+                    if (!(j & (1 << b))) {
+                        const float lo = v[g][j], hi = v[g][j | (1 << b)];
+                        v[g][j] = lo + hi;
+                        v[g][j | (1 << b)] = lo - hi;
+                    }
+                }
+            }
+            if (last) {
+#pragma unroll
+                for (int j = 0; j < E; j++)
+                    v[g][j] *= scale;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G4; g++) {
+            if (q0 + g * NT < ng) {
+#pragma unroll
+                for (int j = 0; j < E; j++)
+                    buf[base[g] + (j << s)] = v[g][j];
+            }
+        }
     }
 }
 
@@ -141,14 +229,13 @@ __device__ void hadamard_lds_stages(lds_f32 *buf, int total, int L, float scale)
 {
     int s = 8;
     while (s < L) {  // uniform
-        const int left = L - s, passes = (left + 3) >> 2, r = (left + passes - 1) / passes;
+        const int left = L - s, passes = (left + 2) / 3, r = (left + passes - 1) / passes;
         const bool last = s + r == L;
         __syncthreads();
         switch (r) {
         case 1: hx_lds_pass<NT, 1>(buf, total, s, last, scale); break;
         case 2: hx_lds_pass<NT, 2>(buf, total, s, last, scale); break;
-        case 3: hx_lds_pass<NT, 3>(buf, total, s, last, scale); break;
-        default: hx_lds_pass<NT, 4>(buf, total, s, last, scale); break;
+        default: hx_lds_pass<NT, 3>(buf, total, s, last, scale); break;
         }
         s += r;
     }

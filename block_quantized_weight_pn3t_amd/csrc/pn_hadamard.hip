@@ -8,7 +8,7 @@
 namespace pn {
 
 constexpr int kHxThreads = 256;
-constexpr int kHxChunk = 4096;  // elements per workgroup step when slices exceed one wave's 256
+constexpr int kHxChunk = 1024;  // elements per workgroup step when slices exceed one wave's 256
 
 __device__ __forceinline__ float4 hx_load4(const float *p, int vec4)
 {
