@@ -518,14 +518,22 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     // waiting for x never waits for them.
     const int per_tok = nb * QB;
     const int total = M * per_tok;
-    const int nq = (total + kFlatWaves * 64 - 1) / (kFlatWaves * 64);
+    // ROT: thread (wave w, lane l) takes, for u = 4 g + j, the float4 at
+    // 256 (w + 8 g) + 64 j + l: a wave holds whole 1024-element pieces of x, 4 float4 per lane
+    // 256 elements apart, so the rotation's stages 8-9 stay in registers. Otherwise l + 512 u.
+    const int nq = ROT ? 4 * ((total + 256 * kFlatWaves - 1) / (256 * kFlatWaves))
+                       : (total + kFlatWaves * 64 - 1) / (kFlatWaves * 64);
+    auto qpos = [&](int u) {
+        return ROT ? 256 * (wave + kFlatWaves * (u >> 2)) + 64 * (u & 3) + lane
+                   : (int)threadIdx.x + u * kFlatWaves * 64;
+    };
     // Each workgroup walks x from its own starting block (rotated by the workgroup index) so that
     // the CUs of an XCD do not all request the same lines of x, i.e. the same L2 channel, at once.
-    // (with ROT by whole 256-element pieces, which its waves transform: 64 float4 units, where
+    // (with ROT by whole 1024-element pieces, which its waves transform: 256 float4 units, where
     // x holds a whole number of them)
     const int rot = !ROT ? (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB
-                    : (total & 63) ? 0
-                                   : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(total >> 6)) * 64;
+                    : (total & 255) ? 0
+                                    : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(total >> 8)) * 256;
     auto rotq = [&](int q) { q += rot; return q >= total ? q - total : q; };
     auto token_of = [](int q, int per) {  // q / per for q < M * per, without a division
         int m = 0;
@@ -538,7 +546,7 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
 #pragma unroll
     for (int u = 0; u < QPT; u++) {
         if (u < nq) {
-            const int q = rotq(min((int)threadIdx.x + u * kFlatWaves * 64, total - 1));
+            const int q = rotq(min(qpos(u), total - 1));
             const int m = token_of(q, per_tok);
             const float *src = x + (int64_t)m * K + 4 * (q - m * per_tok);
             xv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
@@ -594,13 +602,16 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
         // four float4 at a time (their lane exchanges in flight together), only as many as hold x
 #pragma unroll
         for (int g0 = 0; g0 < QPT; g0 += 4)
-            if (g0 < nq)  // uniform
-                hadamard_wave_n<4>(*reinterpret_cast<float4(*)[4]>(&xv[g0]), hL, hscale);
-        if (hL > 8) {  // uniform
+            if (g0 < nq) {  // uniform
+                float4(&v4)[4] = *reinterpret_cast<float4(*)[4]>(&xv[g0]);
+                hadamard_wave_n<4>(v4, hL, hscale);
+                hadamard_regs_8_9(v4, hL, hscale);
+            }
+        if (hL > 10) {  // uniform
             lds_f32 *hb = (lds_f32 *)lds;
 #pragma unroll
             for (int u = 0; u < QPT; u++) {
-                const int q0 = (int)threadIdx.x + u * kFlatWaves * 64;
+                const int q0 = qpos(u);
                 if (u < nq && q0 < total) {
                     const int q = rotq(q0);
                     hb[4 * q + 0] = xv[u].x;
@@ -609,10 +620,10 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
                     hb[4 * q + 3] = xv[u].w;
                 }
             }
-            hadamard_lds_stages<kFlatWaves * 64>(hb, 4 * total, hL, hscale);
+            hadamard_lds_stages<kFlatWaves * 64>(hb, 4 * total, hL, hscale, 10);
 #pragma unroll
             for (int u = 0; u < QPT; u++) {
-                const int q = rotq(min((int)threadIdx.x + u * kFlatWaves * 64, total - 1));
+                const int q = rotq(min(qpos(u), total - 1));
                 if (u < nq)
                     xv[u] = make_float4(hb[4 * q], hb[4 * q + 1], hb[4 * q + 2], hb[4 * q + 3]);
             }
@@ -624,7 +635,7 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     // lanes holds one block); pn3t x * 2^(24-p), sums in a second pass.
 #pragma unroll
     for (int u = 0; u < QPT; u++) {
-        const int q0 = (int)threadIdx.x + u * kFlatWaves * 64;
+        const int q0 = qpos(u);
         if (u < nq && q0 < total) {  // pn4t: whole DPP rows are in or out (total and row bases are multiples of 16)
             const int q = rotq(q0);  // a whole-block rotation keeps each DPP row on one block
             const int m = token_of(q, per_tok);
@@ -892,20 +903,23 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
             }
         }
     };
-    // ROT: x as consecutive float4 per lane (a wave holds 256 consecutive elements), at most
-    // 64 blocks of M tokens over 512 lanes
-    constexpr int HQ = ROT ? (M * 64 * F::G / 4 + 511) / 512 : 1;
-    const int total4 = (int)(M * K / 4), nh = (total4 + 511) >> 9;
-    // workgroups start at different 256-element pieces of x (as the plain staging rotates its
+    // ROT: x as float4 per lane, thread (wave w, lane l) taking for u = 4 g + j the float4 at
+    // 256 (w + 8 g) + 64 j + l: a wave holds whole 1024-element pieces, 4 float4 per lane 256
+    // elements apart, so the rotation's stages 0-9 stay in registers (at most 64 blocks of M
+    // tokens over 8 waves)
+    constexpr int HQ = ROT ? 4 * ((M * 64 * F::G / 4 + 2047) / 2048) : 1;
+    const int total4 = (int)(M * K / 4), nh = 4 * ((total4 + 2047) >> 11);
+    auto hpos = [&](int u) { return 256 * (wave + 8 * (u >> 2)) + 64 * (u & 3) + lane; };
+    // workgroups start at different 1024-element pieces of x (as the plain staging rotates its
     // blocks), so that the CUs of an XCD do not request the same lines at once
-    const int hrot = (!ROT || (total4 & 63)) ? 0
-                     : (int)(((uint32_t)blockIdx.x * 5u) % (uint32_t)(total4 >> 6)) * 64;
+    const int hrot = (!ROT || (total4 & 255)) ? 0
+                     : (int)(((uint32_t)blockIdx.x * 5u) % (uint32_t)(total4 >> 8)) * 256;
     auto hq = [&](int q) { q += hrot; return q >= total4 ? q - total4 : q; };
     float4 hv[HQ];
     if constexpr (ROT) {
 #pragma unroll
         for (int u = 0; u < HQ; u++) {
-            const float *src = x + 4 * hq(min((int)threadIdx.x + 512 * u, total4 - 1));
+            const float *src = x + 4 * hq(min(hpos(u), total4 - 1));
             if (u < nh)
                 hv[u] = x_vec4 ? *reinterpret_cast<const float4 *>(src)
                                : make_float4(src[0], src[1], src[2], src[3]);
@@ -927,10 +941,16 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     if constexpr (ROT) {  // the rotation, while the weight loads are in flight
         extern __shared__ float4 hx_dyn[];  // M * K floats
         lds_f32 *hb = (lds_f32 *)(float *)hx_dyn;
-        hadamard_wave_n<HQ>(hv, hL, hscale);
+#pragma unroll
+        for (int g0 = 0; g0 < HQ; g0 += 4)
+            if (g0 < nh) {  // uniform
+                float4(&v4)[4] = *reinterpret_cast<float4(*)[4]>(&hv[g0]);
+                hadamard_wave_n<4>(v4, hL, hscale);
+                hadamard_regs_8_9(v4, hL, hscale);
+            }
 #pragma unroll
         for (int u = 0; u < HQ; u++) {
-            const int q0 = (int)threadIdx.x + 512 * u;
+            const int q0 = hpos(u);
             if (u < nh) {
                 if (q0 < total4) {
                     const int q = hq(q0);
@@ -941,8 +961,8 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
                 }
             }
         }
-        if (hL > 8)
-            hadamard_lds_stages<512>(hb, 4 * total4, hL, hscale);
+        if (hL > 10)
+            hadamard_lds_stages<512>(hb, 4 * total4, hL, hscale, 10);
         else
             __syncthreads();
         load_x((const float *)hx_dyn, 1);

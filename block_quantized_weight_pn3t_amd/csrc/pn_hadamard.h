@@ -72,15 +72,13 @@ __device__ __forceinline__ void hx_lane_stage(float4 &v, bool upper)
         hx_swap_bfly<MASK>(v.x, v.y);
         hx_swap_bfly<MASK>(v.z, v.w);
     } else {
-        float p;
-        p = hx_partner<MASK>(v.x);
-        v.x = upper ? p - v.x : p + v.x;
-        p = hx_partner<MASK>(v.y);
-        v.y = upper ? p - v.y : p + v.y;
-        p = hx_partner<MASK>(v.z);
-        v.z = upper ? p - v.z : p + v.z;
-        p = hx_partner<MASK>(v.w);
-        v.w = upper ? p - v.w : p + v.w;
+        // partner + (+-1) * own: the product is exact, so this is the same rounding as
+        // partner - own / partner + own, and the DPP move can fold into the add
+        const float sgn = upper ? -1.0f : 1.0f;
+        v.x = hx_partner<MASK>(v.x) + sgn * v.x;
+        v.y = hx_partner<MASK>(v.y) + sgn * v.y;
+        v.z = hx_partner<MASK>(v.z) + sgn * v.z;
+        v.w = hx_partner<MASK>(v.w) + sgn * v.w;
     }
 }
 
@@ -172,6 +170,32 @@ __device__ __forceinline__ void hadamard_wave_n(float4 (&v)[N], int L, float sca
     }
 }
 
+// Stages 8 and 9 (where L >= 9, 10) on four float4 of a lane that sit 256 elements apart
+// (v[j] holds elements 4 lane + 256 j .. + 3 of a 1024-element piece of x), then the scaling
+// where L is 9 or 10. Same butterflies, in the same order, as the LDS pass would run.
+__device__ __forceinline__ void hadamard_regs_8_9(float4 (&v)[4], int L, float scale)
+{
+    auto bfly = [](float4 &lo, float4 &hi) {
+        const float4 a = make_float4(lo.x + hi.x, lo.y + hi.y, lo.z + hi.z, lo.w + hi.w);
+        const float4 b = make_float4(lo.x - hi.x, lo.y - hi.y, lo.z - hi.z, lo.w - hi.w);
+        lo = a;
+        hi = b;
+    };
+    if (L >= 9) {
+        bfly(v[0], v[1]);
+        bfly(v[2], v[3]);
+    }
+    if (L >= 10) {
+        bfly(v[0], v[2]);
+        bfly(v[1], v[3]);
+    }
+    if (L == 9 || L == 10) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            v[j] = make_float4(v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale);
+    }
+}
+
 // R stages s .. s+R-1 over buf[0, total) in LDS: groups of 2^R elements at stride 2^s. A thread
 // takes 2 groups at a time (NT apart): all their reads, then the butterflies, then the writes of
 // the groups that exist (a clamped group past the end is read, never written).
@@ -222,12 +246,12 @@ __device__ __forceinline__ void hx_lds_pass(lds_f32 *buf, int total, int s, bool
     }
 }
 
-// Stages 8 .. L-1 (L > 8) over buf[0, total) in LDS, total a multiple of 2^L, then the scaling.
+// Stages s0 .. L-1 (L > s0) over buf[0, total) in LDS, total a multiple of 2^L, then the scaling.
 // Every thread of the workgroup (NT of them) calls it; it starts and ends with a barrier.
 template <int NT>
-__device__ void hadamard_lds_stages(lds_f32 *buf, int total, int L, float scale)
+__device__ void hadamard_lds_stages(lds_f32 *buf, int total, int L, float scale, int s0 = 8)
 {
-    int s = 8;
+    int s = s0;
     while (s < L) {  // uniform
         const int left = L - s, passes = (left + 2) / 3, r = (left + passes - 1) / passes;
         const bool last = s + r == L;
