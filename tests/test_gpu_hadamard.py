@@ -123,7 +123,7 @@ def gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B):
 # kernel; B below 256 rotates in registers only, above it through LDS.
 FUSED = [(PN3T, 300, 64, 1024), (PN3T, 77, 8, 128), (PN3T, 33, 16, 256), (PN4T, 45, 64, 4096),
          (PN4T, 260, 272, 1024), (PN4T, 70, 96, 2048), (PN3T, 41, 80, 256), (PN4T, 19, 130, 64),
-         (PN4T, 9, 256, 16384)]
+         (PN4T, 9, 256, 16384), (PN3T, 25, 8, 4), (PN4T, 31, 130, 8), (PN3T, 13, 64, 512)]
 
 
 @pytest.mark.parametrize("M", [1, 2])
