@@ -232,6 +232,19 @@ __device__ __forceinline__ uint32_t f64_to_e4m3_sat(double v)
 // PN_ERR_DEVICE.
 int check_device();
 
+// Raises kernel KERN's limit of dynamic LDS to `bytes`, once per process: a function-local static
+// (one per kernel) is initialised exactly once even when several host threads launch at once.
+// false if the runtime refused (the caller reports PN_ERR_HIP). The library serves the current
+// device of a single-GPU process; the attribute is not set again per device.
+template <auto KERN>
+inline bool lds_limit_once(int bytes)
+{
+    static const bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               bytes) == hipSuccess;
+    return ok;
+}
+
 // Maps the launch status of the last kernel to PN_OK / PN_ERR_HIP.
 int launch_status();
 

@@ -485,14 +485,9 @@ static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int6
                               const float *x, float *y, hipStream_t s)
 {
     constexpr int R = 2;
-    auto kern = fp8row_gemv_kernel<M, R, D, QX>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kFp8MaxLds) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = fp8row_gemv_kernel<M, R, D, QX>;
+    if (!lds_limit_once<kern>(kFp8MaxLds))
+        return PN_ERR_HIP;
     const int64_t nch = K >> 4;
     // a phase holds at most 512 chunks (8192 weights) and fits LDS at 4 tokens; 16 float4 x loads
     // per thread at most

@@ -1148,14 +1148,9 @@ static int launch_lds(const uint8_t *W, int64_t N, int64_t K, const float *x, fl
     const int per_block = M * F::LDS_STRIDE * (int)sizeof(float);
     const int phase_nb = min(nb, kMaxLds / per_block);
     const size_t lds = (size_t)phase_nb * per_block;
-    auto kern = pn_gemv_kernel<TYPE, M, R, D>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMaxLds) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = pn_gemv_kernel<TYPE, M, R, D>;
+    if (!lds_limit_once<kern>(kMaxLds))
+        return PN_ERR_HIP;
     const LaunchCfg c = choose_cfg(N, R);
     const int grid = (int)std::min<int64_t>(c.grid, (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
@@ -1172,17 +1167,10 @@ static int launch_xreg(const uint8_t *W, int64_t N, int64_t K, const float *x, f
     const int nb = (int)(K / F::G);
     const int grid = (int)std::min<int64_t>(num_cus(), (N + 3) / 4);
     const int vec4 = aligned(x, 16) ? 1 : 0;
-    auto kern = pn_gemv_xreg_kernel<TYPE, M, D, ROT>;
+    constexpr auto kern = pn_gemv_xreg_kernel<TYPE, M, D, ROT>;
     const size_t lds = ROT ? (size_t)M * K * sizeof(float) : 0;  // the rotated x
-    if (ROT) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)((size_t)M * 64 * F::G * sizeof(float))) != hipSuccess)
-                return PN_ERR_HIP;
-            attr_set = true;
-        }
-    }
+    if (ROT && !lds_limit_once<kern>((int)((size_t)M * 64 * F::G * sizeof(float))))
+        return PN_ERR_HIP;
     // 512 threads: the cooperative staging gives each thread one word of one block
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, y, row_split(N, grid), vec4,
@@ -1196,14 +1184,9 @@ template <int TYPE, int M, int QPT, bool ROT>
 static int launch_flat_q(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, float *y,
                          int grid, int64_t NP, size_t lds, hipStream_t s, int hL, float hscale)
 {
-    auto kern = pn_gemv_flat_kernel<TYPE, M, 2, 4, QPT, ROT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMaxLds) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = pn_gemv_flat_kernel<TYPE, M, 2, 4, QPT, ROT>;
+    if (!lds_limit_once<kern>(kMaxLds))
+        return PN_ERR_HIP;
     const int vec4 = aligned(x, 16) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kFlatWaves), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, y, NP / grid, (int)(NP % grid), vec4,

@@ -799,14 +799,9 @@ static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, i
 {
     const size_t lds = std::max<size_t>((size_t)Pb * mfma_block_bytes<TYPE>(M),
                                         (size_t)TG * kMfmaWaves * 64 * 16);
-    auto kern = pn_gemv_mfma_kernel<TYPE, TG>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMfmaLds) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = pn_gemv_mfma_kernel<TYPE, TG>;
+    if (!lds_limit_once<kern>(kMfmaLds))
+        return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaThreads), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, M, y, rq, rr, Pb, nph,
                        aligned(x, 16) ? 1 : 0);
@@ -818,14 +813,9 @@ static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *
                               int M, float *y, int64_t rq, int rr, int grid, int Pb, int nph,
                               size_t lds, hipStream_t s)
 {
-    auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMfmaLds) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC>;
+    if (!lds_limit_once<kern>(kMfmaLds))
+        return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaThreads), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, M, y, rq, rr, Pb, nph,
                        aligned(x, 16) ? 1 : 0);

@@ -142,14 +142,8 @@ extern "C" int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B,
         const int64_t chunks = (total + C - 1) / C;
         const int grid = (int)std::min<int64_t>(chunks, (int64_t)num_cus_hx() * 4);
         const size_t lds = (size_t)C * sizeof(float);
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute((const void *)hadamard_lds_kernel,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)((size_t(1) << kHadamardMaxLog) * sizeof(float))) != hipSuccess)
-                return PN_ERR_HIP;
-            attr_set = true;
-        }
+        if (!lds_limit_once<hadamard_lds_kernel>((int)((size_t(1) << kHadamardMaxLog) * sizeof(float))))
+            return PN_ERR_HIP;
         hipLaunchKernelGGL(hadamard_lds_kernel, dim3((unsigned)grid), dim3(kHxThreads), lds, s, x,
                            out, total, C, L, scale, vin, vout);
     }

@@ -314,14 +314,9 @@ static int launch_nv(const uint8_t *codes, const uint8_t *scales, float g, int64
     const int ngroups = (int)(K >> 4);
     const int per_group = M * kGroupLdsWords * 4;
     const int phase_groups = min(ngroups, kNvLdsBudget / per_group);
-    auto kern = nvfp4_gemv_kernel<M, R>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kNvLdsBudget) != hipSuccess)
-            return PN_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr auto kern = nvfp4_gemv_kernel<M, R>;
+    if (!lds_limit_once<kern>(kNvLdsBudget))
+        return PN_ERR_HIP;
     const int64_t rows_per_wg = 4 * R;
     hipLaunchKernelGGL(kern, dim3((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), dim3(256),
                        (size_t)phase_groups * per_group, s, codes, scales, g, N, K, x, y,
