@@ -5,26 +5,53 @@
 // NVFP4: "Quantisation and profiles", section "NVFP4"; NInfer "tensor formats" section 3.3.
 #include <string.h>
 
+#include <atomic>
+
 #include "pn_common.h"
 
 namespace pn {
 
+// Per-device facts, looked up once per device and kept for the process (atomics: entry points
+// may be called from several host threads, on different devices).
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_dev_status[kMaxDevices];  // 0 unknown, else status + 1000
+static std::atomic<int> g_dev_cus[kMaxDevices];     // 0 unknown
+
 int check_device()
 {
-    static int cached_dev = -1;
-    static int cached_status = PN_ERR_DEVICE;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return PN_ERR_HIP;
-    if (dev == cached_dev)
-        return cached_status;
+    if (dev < kMaxDevices) {
+        const int c = g_dev_status[dev].load(std::memory_order_relaxed);
+        if (c != 0)
+            return c - 1000;
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
         return PN_ERR_HIP;
     const int st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? PN_OK : PN_ERR_DEVICE;
-    cached_dev = dev;
-    cached_status = st;
+    if (dev < kMaxDevices) {
+        g_dev_status[dev].store(st + 1000, std::memory_order_relaxed);
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    }
     return st;
+}
+
+int device_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        const int c = g_dev_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0) {
+            g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+            return prop.multiProcessorCount;
+        }
+    }
+    return 256;  // MI355X; entry points have passed check_device() before they size a grid
 }
 
 int launch_status()

@@ -231,6 +231,8 @@ __device__ __forceinline__ uint32_t f64_to_e4m3_sat(double v)
 // Checks that the current device is gfx950 (cached per device). Returns PN_OK, PN_ERR_HIP or
 // PN_ERR_DEVICE.
 int check_device();
+// Compute units of the current device (cached per device).
+int device_cus();
 
 // Raises kernel KERN's limit of dynamic LDS to `bytes`, once per process: a function-local static
 // (one per kernel) is initialised exactly once even when several host threads launch at once.

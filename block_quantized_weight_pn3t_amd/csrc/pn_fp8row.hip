@@ -467,18 +467,7 @@ static int fp8row_common(const uint8_t *codes, const uint16_t *scales, int64_t N
     return PN_OK;
 }
 
-static int fp8_num_cus()
-{
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return 256;
-        cus = prop.multiProcessorCount;
-    }
-    return cus;
-}
+static int fp8_num_cus() { return device_cus(); }
 
 template <int M, int QX, int D>
 static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,

@@ -1111,18 +1111,7 @@ static int older_share(int dflt)
     return v < 4 ? 4 : v > 15 ? 15 : v;
 }
 
-static int num_cus()
-{
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return 256;
-        cus = prop.multiProcessorCount;
-    }
-    return cus;
-}
+static int num_cus() { return device_cus(); }
 
 // Waves per workgroup (one workgroup per CU): 8 (two per SIMD, so one wave's memory waits overlap
 // the other's arithmetic) unless the rows are too few to give every wave a group of R. Rows are

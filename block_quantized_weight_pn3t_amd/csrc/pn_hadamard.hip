@@ -91,18 +91,7 @@ float hadamard_scale(int L)
     return (float)(1.0 / sqrt((double)(int64_t(1) << L)));
 }
 
-static int num_cus_hx()
-{
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return 256;
-        cus = prop.multiProcessorCount;
-    }
-    return cus;
-}
+static int num_cus_hx() { return device_cus(); }
 
 }  // namespace pn
 

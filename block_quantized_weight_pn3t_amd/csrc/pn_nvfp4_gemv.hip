@@ -288,14 +288,7 @@ template <int M, int GPL>
 static int launch_nv_xreg(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
                           const uint16_t *x, float *y, hipStream_t s)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return PN_ERR_HIP;
-        cus = prop.multiProcessorCount;
-    }
+    const int cus = device_cus();
     const int grid = (int)std::min<int64_t>(cus, (N + 3) / 4);
     const int64_t S = (int64_t)grid * 4;
     // ring of 4 rows at 1-2 tokens, 2 at 3-4 (registers: x takes 8*GPL per token)
