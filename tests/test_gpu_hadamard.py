@@ -191,3 +191,21 @@ def test_gemv_hadamard_rejects_rows_it_cannot_stage(env):
     pn.gemv(typ, Wd, N, K, xr, y)
     torch.cuda.synchronize()
     assert torch.all(y == 0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("typ,N,K,seed,xseed", [(PN3T, 17408, 5120, 301, 304),
+                                                (PN4T, 5120, 17408, 303, 305)])
+def test_gemv_hadamard_full_size(env, typ, N, K, seed, xseed):
+    """The model's gate and down shapes with x rotated in slices of 1024 (the bench's setting),
+    one and two tokens, every row against the oracle."""
+    pn, torch, dev = env
+    _, W = quantized(typ, N, K, seed)
+    Wd = dev_bytes(torch, dev, W)
+    x2 = synth.activations(xseed, 2, K)
+    y_ref, bound, rbound = oracle.gemv_hadamard(typ, W, N, K, x2, 1024)
+    for M in (1, 2):
+        y = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x2[:M], 1024)
+        tol = 1e-5 * bound[:M] + (1 + 1e-5) * gamma(1024) * rbound[:M]
+        err = np.abs(y.astype(np.float64) - y_ref[:M])
+        assert np.all(err <= tol), f"M={M} max |err| / tol = {float(np.max(err / tol)):.3f}"
