@@ -22,7 +22,7 @@ PN4T = 125
 GROUP = {PN3T: 80, PN4T: 64}
 MAX_TOKENS = 4         # NVFP4 and row-scaled E4M3 GEMV
 GEMV_MAX_TOKENS = 16   # PN GEMV
-GEMV_HADAMARD_MAX_TOKENS = 2  # PN GEMV with the rotation fused
+GEMV_HADAMARD_MAX_TOKENS = 4  # PN GEMV with the rotation fused
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpn.so")
@@ -159,7 +159,7 @@ def hadamard_rows(x, B, out, M=None, K=None, stream=None):
 
 
 def gemv_hadamard(type_, W, N, K, x, B, y, M=None, stream=None):
-    """y[M, N] <- W[N, K] . (H x)[M, K]^T, the rotation fused into the GEMV (M <= 2)."""
+    """y[M, N] <- W[N, K] . (H x)[M, K]^T, the rotation fused into the GEMV (M <= 4)."""
     import torch
     _dev(x, "x", torch.float32)
     _dev(y, "y", torch.float32)

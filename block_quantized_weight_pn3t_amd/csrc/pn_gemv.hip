@@ -1305,9 +1305,18 @@ extern "C" int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, c
         return st;
     hipStream_t s = (hipStream_t)stream;
     const float hs = hadamard_scale(L);
-    if (type == PN_TYPE_PN3T)
-        return dispatch_hadamard<PN_TYPE_PN3T>((const uint8_t *)W, N, K, x, M, y, L, hs, s);
-    return dispatch_hadamard<PN_TYPE_PN4T>((const uint8_t *)W, N, K, x, M, y, L, hs, s);
+    // tokens two at a time (the fused staging serves one or two; 3-4 tokens read W once per pair)
+    for (int64_t m0 = 0; m0 < M; m0 += 2) {
+        const int64_t mc = std::min<int64_t>(2, M - m0);
+        st = type == PN_TYPE_PN3T
+                 ? dispatch_hadamard<PN_TYPE_PN3T>((const uint8_t *)W, N, K, x + m0 * K, mc,
+                                                   y + m0 * N, L, hs, s)
+                 : dispatch_hadamard<PN_TYPE_PN4T>((const uint8_t *)W, N, K, x + m0 * K, mc,
+                                                   y + m0 * N, L, hs, s);
+        if (st != PN_OK)
+            return st;
+    }
+    return PN_OK;
 }
 
 extern "C" int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,

@@ -57,7 +57,7 @@ enum {
 /* Maximum tokens per GEMV call. */
 #define PN_MAX_TOKENS 4        /* NVFP4 and row-scaled E4M3 GEMV */
 #define PN_GEMV_MAX_TOKENS 16  /* PN GEMV */
-#define PN_GEMV_HADAMARD_MAX_TOKENS 2  /* PN GEMV with the rotation fused */
+#define PN_GEMV_HADAMARD_MAX_TOKENS 4  /* PN GEMV with the rotation fused */
 
 /* Bytes of one PN row of K weights: 34*K/80 (pn3t) or 34*K/64 (pn4t); 0 if K is not a positive
  * multiple of the block size or type is unknown. Host-only, no device work. */
@@ -126,15 +126,17 @@ int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64
  * (PN_ERR_SHAPE). out may equal x (in place); otherwise they must not overlap. */
 int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out, void *stream);
 
-/* y = W x' for M = 1..2 tokens: the PN GEMV (pn_gemv) over the rotated x, the rotation fused into
+/* y = W x' for M = 1..4 tokens: the PN GEMV (pn_gemv) over the rotated x, the rotation fused into
  * the kernels' x staging (each workgroup rotates x in its registers and LDS while its first
  * weight loads are in flight; x itself is not modified). Arguments as pn_gemv, plus B as in
- * pn_hadamard_rows. M outside 0..2 gives PN_ERR_TOKENS. The fused staging takes rows of at most
- * 64 blocks, and longer rows whose x (M * K floats) fits the long-row kernel's LDS area (K up to
- * about 34,000 at one token, 17,000 at two); other shapes give PN_ERR_SHAPE: rotate with
- * pn_hadamard_rows, then call pn_gemv. Gives the same bits as pn_hadamard_rows followed by pn_gemv
- * on the same shape (the same transform, then the same kernel), so the accuracy of pn_gemv
- * applies to the rotated x, plus the rotation's own error above. */
+ * pn_hadamard_rows. M outside 0..4 gives PN_ERR_TOKENS. Tokens are served two at a time, one
+ * launch per pair (at 3-4 tokens W is read twice). The fused staging takes rows of at most 64
+ * blocks, and longer rows whose x (2 * K floats for a pair) fits the long-row kernel's LDS area
+ * (K up to about 34,000 at one token, 17,000 at two); other shapes give PN_ERR_SHAPE: rotate with
+ * pn_hadamard_rows, then call pn_gemv. At 1-2 tokens it gives the same bits as pn_hadamard_rows
+ * followed by pn_gemv on the same shape (the same transform, then the same kernel); at every M
+ * the accuracy of the one- and two-token pn_gemv applies to the rotated x, plus the rotation's
+ * own error above. */
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 

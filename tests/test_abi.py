@@ -77,7 +77,7 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_hadamard_rows(fake, 0, 640, 64, fake, None) == 0       # M = 0: no-op
     assert L.pn_hadamard_rows(None, 1, 640, 64, fake, None) == -4
     assert L.pn_hadamard_rows(fake, 1, 640, 64, P(0x1002), None) == -5
-    assert L.pn_gemv_hadamard(124, fake, 4, 640, fake, 3, 64, fake, None) == -3  # M above 2
+    assert L.pn_gemv_hadamard(124, fake, 4, 640, fake, 5, 64, fake, None) == -3  # M above 4
     assert L.pn_gemv_hadamard(124, fake, 4, 640, fake, 1, 256, fake, None) == -8
     assert L.pn_gemv_hadamard(124, fake, 4, 650, fake, 1, 64, fake, None) == -2
     assert L.pn_gemv_hadamard(7, fake, 4, 640, fake, 1, 64, fake, None) == -1

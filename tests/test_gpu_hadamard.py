@@ -126,7 +126,7 @@ FUSED = [(PN3T, 300, 64, 1024), (PN3T, 77, 8, 128), (PN3T, 33, 16, 256), (PN4T, 
          (PN4T, 9, 256, 16384), (PN3T, 25, 8, 4), (PN4T, 31, 130, 8), (PN3T, 13, 64, 512)]
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("typ,N,nb,B", FUSED)
 def test_gemv_hadamard_matches_oracle(env, typ, N, nb, B, M):
     pn, torch, dev = env
@@ -198,13 +198,13 @@ def test_gemv_hadamard_rejects_rows_it_cannot_stage(env):
                                                 (PN4T, 5120, 17408, 303, 305)])
 def test_gemv_hadamard_full_size(env, typ, N, K, seed, xseed):
     """The model's gate and down shapes with x rotated in slices of 1024 (the bench's setting),
-    one and two tokens, every row against the oracle."""
+    one to four tokens, every row against the oracle."""
     pn, torch, dev = env
     _, W = quantized(typ, N, K, seed)
     Wd = dev_bytes(torch, dev, W)
-    x2 = synth.activations(xseed, 2, K)
+    x2 = synth.activations(xseed, 4, K)
     y_ref, bound, rbound = oracle.gemv_hadamard(typ, W, N, K, x2, 1024)
-    for M in (1, 2):
+    for M in (1, 2, 3, 4):
         y = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x2[:M], 1024)
         tol = 1e-5 * bound[:M] + (1 + 1e-5) * gamma(1024) * rbound[:M]
         err = np.abs(y.astype(np.float64) - y_ref[:M])
