@@ -192,10 +192,11 @@ def extra_workloads(pn, torch, dev, reps, warmup):
                                    "per_matrix_us": {k: v["us"] for k, v in per.items()}}
     log("[bench] extra: layer set done")
 
-    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1, 2, on the same
-    # layer set, against the plain launches above; and the rotation on its own
+    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1..4 (3-4 as two
+    # launches of a token pair), on the same layer set, against the plain launches above; and the
+    # rotation on its own
     xr = torch.empty((4, 17408), dtype=torch.float32, device=dev)
-    for M in (1, 2):
+    for M in (1, 2, 3, 4):
         per, tot_b, tot_us, tot_plain = {}, 0, 0.0, 0.0
         for name, typ, N, K, Ws in mats:
             us = time_launches(torch, stream, lambda c: check(pn.gemv_hadamard_ptr(
@@ -302,7 +303,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0 = skip)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured configurations (pn4t 5120x6144, layer set at "
-                         "M=1..4, the layer set with Hadamard-rotated x at M=1,2, NVFP4 at M=1..4, "
+                         "M=1..4, the layer set with Hadamard-rotated x at M=1..4, NVFP4 at M=1..4, "
                          "row-scaled E4M3 head at M=1..4)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
