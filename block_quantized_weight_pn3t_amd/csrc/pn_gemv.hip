@@ -1204,6 +1204,8 @@ static int launch_flat(const uint8_t *W, int64_t N, int64_t K, const float *x, f
         return launch_flat_q<TYPE, M, 8, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
     if (need <= 16)
         return launch_flat_q<TYPE, M, 16, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
+    if (need <= 24)  // two tokens of down (17 per thread): fewer registers than 32
+        return launch_flat_q<TYPE, M, 24, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
     return launch_flat_q<TYPE, M, 32, ROT>(W, N, (int)nb, x, K, y, grid, NP, lds, s, hL, hscale);
 }
 
