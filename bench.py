@@ -192,9 +192,11 @@ def extra_workloads(pn, torch, dev, reps, warmup):
                                    "per_matrix_us": {k: v["us"] for k, v in per.items()}}
     log("[bench] extra: layer set done")
 
-    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1..4 (3-4 as two
-    # launches of a token pair), on the same layer set, against the plain launches above; and the
-    # rotation on its own
+    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1..4 (3-4 in one
+    # matrix-core launch where it stages x in one pass, else as two launches of a token pair), on
+    # the same layer set, against the plain launches above; the rotation on its own; and the
+    # layer set with each distinct input rotated once and shared (q, k, v; gate and up; o; down;
+    # the 6144-wide matrix) ahead of plain launches
     xr = torch.empty((4, 17408), dtype=torch.float32, device=dev)
     for M in (1, 2, 3, 4):
         per, tot_b, tot_us, tot_plain = {}, 0, 0.0, 0.0
@@ -209,10 +211,19 @@ def extra_workloads(pn, torch, dev, reps, warmup):
         out[f"hadamard1024_layer_set_M{M}"] = {
             "GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
             "plain_us": round(tot_plain, 2), "per_matrix_us": per}
-    for M, K in ((1, 5120), (1, 17408), (2, 17408), (4, 17408)):
-        us = time_launches(torch, stream, lambda c: check(pn.lib().pn_hadamard_rows(
-            xs[K].data_ptr(), M, K, 1024, xr.data_ptr(), sh), "pn_hadamard_rows"), 1, reps, warmup)
-        out[f"hadamard_rows_1024_M{M}_K{K}_us"] = round(us, 3)
+    rot = {}
+    for M in (1, 2, 3, 4):
+        for K in (5120, 6144, 17408):
+            rot[M, K] = time_launches(torch, stream, lambda c: check(pn.lib().pn_hadamard_rows(
+                xs[K].data_ptr(), M, K, 1024, xr.data_ptr(), sh), "pn_hadamard_rows"), 1, reps,
+                warmup)
+    out["hadamard_rows_1024_us"] = {f"M{M}_K{K}": round(v, 3) for (M, K), v in rot.items()}
+    for M in (1, 2, 3, 4):
+        plain = out[f"layer_set_M{M}"]
+        rot_us = 3 * rot[M, 5120] + rot[M, 6144] + rot[M, 17408]
+        out[f"hadamard1024_layer_set_rotate_once_M{M}"] = {
+            "GBs": round(sum(Ws[0].numel() for *_, Ws in mats) / (plain["us"] + rot_us) / 1e3, 1),
+            "us": round(plain["us"] + rot_us, 2), "rotations_us": round(rot_us, 2)}
     del mats
     log("[bench] extra: Hadamard done")
 

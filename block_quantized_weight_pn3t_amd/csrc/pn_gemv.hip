@@ -1279,6 +1279,8 @@ static int dispatch_hadamard(const uint8_t *W, int64_t N, int64_t K, const float
 
 int hadamard_log(int64_t B, int64_t K);
 float hadamard_scale(int L);
+int launch_mfma_hadamard(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
+                         float *y, int cus, int hL, float hscale, hipStream_t s);
 
 }  // namespace pn
 
@@ -1307,7 +1309,11 @@ extern "C" int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, c
         return st;
     hipStream_t s = (hipStream_t)stream;
     const float hs = hadamard_scale(L);
-    // tokens two at a time (the fused staging serves one or two; 3-4 tokens read W once per pair)
+    // three or four tokens: one launch of the matrix-core kernel where it stages x in one pass
+    if (M >= 3 && (st = launch_mfma_hadamard(type, (const uint8_t *)W, N, K, x, (int)M, y,
+                                             num_cus(), L, hs, s)) != 1)
+        return st;
+    // else tokens two at a time (the fused staging serves one or two; W read once per pair)
     for (int64_t m0 = 0; m0 < M; m0 += 2) {
         const int64_t mc = std::min<int64_t>(2, M - m0);
         st = type == PN_TYPE_PN3T

@@ -39,6 +39,7 @@
 // (W 4-byte aligned, rows of a multiple of 4 blocks), the other reads each lane's bytes directly
 // (any 2-byte aligned W and block count).
 #include "pn_common.h"
+#include "pn_hadamard.h"
 
 namespace pn {
 
@@ -369,7 +370,9 @@ __device__ __forceinline__ void mfma_read_a(MfmaA &a, const uint8_t *blk, int g,
 // per k-step covers both; K-split (up to 16 tokens): hi and lo are two A operands on the same
 // codes. `after_loads` runs once the first x loads are issued (a caller's weight prefetch: loads
 // retire in order, so waiting for x then leaves the prefetch in flight).
-template <int TYPE, bool SLOT, int EG, class F>
+// LX: x comes from LDS instead (fp32 [M][K] at the start of the x area, the rotated x): every
+// unit is read before the area is overwritten (one chunk of units; the caller ensures it).
+template <int TYPE, bool SLOT, int EG, class F, bool LX = false>
 __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t K, int M,
                                            int ML, int pb0, int npb, int xvec4, F after_loads)
 {
@@ -386,7 +389,8 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
         m = w % M;
         brel = EG * (w / M) + bi;
     };
-    __syncthreads();  // earlier readers of the x area are done
+    if constexpr (!LX)
+        __syncthreads();  // earlier readers of the x area are done (LX: the caller synchronised)
     // x is a restrict kernel argument, so its loads may otherwise move past the prefetch below;
     // through an opaque copy of the address they stay in program order
     uint64_t xaddr = reinterpret_cast<uint64_t>(x);
@@ -401,7 +405,21 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
             const int u = min((c * kMfmaUnits + ub) * kMfmaThreads + tid, U - 1);
             int gg, m, brel;
             unit_coords(u, gg, m, brel);
-            mfma_load_unit<TYPE>(xg, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4, xr[ub]);
+            if constexpr (LX) {
+                typedef __attribute__((address_space(3))) const mf_f4 lds_f4_t;
+                lds_f4_t *src = reinterpret_cast<lds_f4_t *>(
+                    (const lds_f32 *)(const float *)xa +
+                    ((int64_t)m * K + (int64_t)(pb0 + brel) * T::G + PERG * gg));
+#pragma unroll
+                for (int q = 0; q < PERG / 4; q++) {
+                    const mf_f4 f = src[q];
+                    xr[ub][4 * q] = f.x; xr[ub][4 * q + 1] = f.y;
+                    xr[ub][4 * q + 2] = f.z; xr[ub][4 * q + 3] = f.w;
+                }
+            } else {
+                mfma_load_unit<TYPE>(xg, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4,
+                                     xr[ub]);
+            }
         }
     };
     auto convert = [&](int c) {
@@ -460,13 +478,20 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
             }
     };
     load(0);
-    asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
-    after_loads();
-    asm volatile("" ::: "memory");
-    convert(0);
-    for (int c = 1; c < nch; c++) {
-        load(c);
-        convert(c);
+    if constexpr (LX) {
+        // every read of the fp32 x is done before any thread overwrites the area (a barrier on
+        // LDS traffic only: the weight copies in flight need not land)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        convert(0);
+    } else {
+        asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
+        after_loads();
+        asm volatile("" ::: "memory");
+        convert(0);
+        for (int c = 1; c < nch; c++) {
+            load(c);
+            convert(c);
+        }
     }
     const int used = SLOT ? 2 * M : M;
     for (int i = tid; i < npb * 16; i += kMfmaThreads)
@@ -613,11 +638,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // MC: the token capacity of the x layout (4, 8 or 16; M <= MC), so that every LDS offset of
 // the loop is a constant. Up to 8, hi and lo are token slots.
-template <int TYPE, int TG, int MC>
+// ROT (3-4 tokens, one phase of x, one chunk of staging units, slices of at most 1024): x is
+// first rotated, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the Hadamard rotation of
+// "Files that use PN", as read in pn_hadamard.h), in registers while the first weight copies are
+// in flight, and written as fp32 to the x area, which the staging then reads.
+template <int TYPE, int TG, int MC, bool ROT = false>
 __global__ void __launch_bounds__(kMfmaThreads)
 pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
                         const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
-                        int64_t rq, int rr, int Pb, int nph, int xvec4)
+                        int64_t rq, int rr, int Pb, int nph, int xvec4, int hL, float hscale)
 {
     constexpr bool SLOT = MC <= 8;
     constexpr int ACC = SLOT ? 2 : 4;       // tokens per lane
@@ -691,11 +720,72 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
                 }
                 ++pf;
             };
-            mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
+            if constexpr (ROT) {
+                // x of the M tokens as float4 per lane: thread (wave w, lane l) takes, for
+                // u = 4 g + j, the float4 at 256 (w + 8 g) + 64 j + l, so a wave holds whole
+                // 1024-element pieces and stages 0-9 of the rotation stay in registers
+                constexpr int HQ = 12;  // M K <= 24576 elements (checked on the host)
+                const int total4 = (int)(M * K / 4), nh = 4 * ((total4 + 2047) >> 11);
+                auto hpos = [&](int u) { return 256 * (wave + 8 * (u >> 2)) + 64 * (u & 3) + lane; };
+                // the previous group's partial sums (which alias the x area and may reach into
+                // the slots) are read; no weight copy is in flight here
+                __syncthreads();
+                // through an opaque copy of the address the x loads stay before the prefetch
+                uint64_t xaddr = reinterpret_cast<uint64_t>(x);
+                asm volatile("" : "+s"(xaddr));
+                typedef __attribute__((address_space(1))) const mf_f4 g_f4_t;
+                gfloat_t *xg = reinterpret_cast<gfloat_t *>(xaddr);
+                // every load unconditional (past the end: the last float4 again, never written
+                // back), one branch on the alignment around them all: loads in branches of their
+                // own get waited for one by one where the branches join
+                float4 hv[HQ];
+                if (xvec4) {
+#pragma unroll
+                    for (int u = 0; u < HQ; u++) {
+                        const mf_f4 f = reinterpret_cast<g_f4_t *>(xg)[min(hpos(u), total4 - 1)];
+                        hv[u] = make_float4(f.x, f.y, f.z, f.w);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < HQ; u++) {
+                        const int q = min(hpos(u), total4 - 1);
+                        hv[u] = make_float4(xg[4 * q], xg[4 * q + 1], xg[4 * q + 2], xg[4 * q + 3]);
+                    }
+                }
+                asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
                 issue_next();
                 issue_next();
                 issue_next();
-            });
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int g0 = 0; g0 < HQ; g0 += 4)
+                    if (g0 < nh) {  // uniform
+                        float4(&v4)[4] = *reinterpret_cast<float4(*)[4]>(&hv[g0]);
+                        hadamard_wave_n<4>(v4, hL, hscale);
+                        hadamard_regs_8_9(v4, hL, hscale);
+                    }
+                lds_f32 *xf = (lds_f32 *)(float *)xa;
+#pragma unroll
+                for (int u = 0; u < HQ; u++) {
+                    const int q = hpos(u);
+                    if (u < nh && q < total4) {
+                        xf[4 * q + 0] = hv[u].x;
+                        xf[4 * q + 1] = hv[u].y;
+                        xf[4 * q + 2] = hv[u].z;
+                        xf[4 * q + 3] = hv[u].w;
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                auto none = [] {};
+                mfma_stage<TYPE, SLOT, kChunkBlocks, decltype(none), true>(xa, x, K, M, MC, pb0,
+                                                                           npb, xvec4, none);
+            } else {
+                mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
+                    issue_next();
+                    issue_next();
+                    issue_next();
+                });
+            }
 #pragma unroll
             for (int t = 0; t < TG; t++) {
                 const int lo = max(i0, t * n4), hi = min(i1, (t + 1) * n4);
@@ -808,23 +898,24 @@ static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, i
     return launch_status();
 }
 
-template <int TYPE, int TG, int MC>
+template <int TYPE, int TG, int MC, bool ROT = false>
 static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K,
                               int M, float *y, int64_t rq, int rr, int grid, int Pb, int nph,
-                              size_t lds, hipStream_t s)
+                              size_t lds, hipStream_t s, int hL = 0, float hscale = 1.0f)
 {
-    constexpr auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC>;
+    constexpr auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC, ROT>;
     if (!lds_limit_once<kern>(kMfmaLds))
         return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaThreads), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, M, y, rq, rr, Pb, nph,
-                       aligned(x, 16) ? 1 : 0);
+                       aligned(x, 16) ? 1 : 0, hL, hscale);
     return launch_status();
 }
 
-template <int TYPE, int MC>
+template <int TYPE, int MC, bool ROT = false>
 static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, int M,
-                             float *y, int grid, int64_t rq, int rr, hipStream_t s)
+                             float *y, int grid, int64_t rq, int rr, hipStream_t s, int hL = 0,
+                             float hscale = 1.0f)
 {
     // tiles of 16 rows per group
     constexpr int max_tg = kMfmaMaxTG;
@@ -842,8 +933,8 @@ static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x
 #define PN_MFMA_CASE(tg)                                                                           \
     case tg:                                                                                       \
         if constexpr (tg <= max_tg)                                                                \
-            return launch_mfma_lds_tg<TYPE, tg, MC>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,       \
-                                                      nph, lds, s);                                \
+            return launch_mfma_lds_tg<TYPE, tg, MC, ROT>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,  \
+                                                           nph, lds, s, hL, hscale);               \
         else                                                                                       \
             return PN_ERR_SHAPE;
     PN_MFMA_CASE(1) PN_MFMA_CASE(2) PN_MFMA_CASE(3) PN_MFMA_CASE(4) PN_MFMA_CASE(5)
@@ -900,6 +991,37 @@ int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x
     if (type == PN_TYPE_PN3T)
         return launch_mfma_t<PN_TYPE_PN3T>(W, N, K, x, M, y, cus, s);
     return launch_mfma_t<PN_TYPE_PN4T>(W, N, K, x, M, y, cus, s);
+}
+
+// The GEMV over Hadamard-rotated x at 3-4 tokens in one launch of the weight-staging kernel:
+// W as mfma_stages_weights takes it, slices of at most 1024 elements, and the x of the call
+// staged in one phase and one pass of units (at most 256 blocks over the tokens; every shape
+// within this fits the fp32 x in the x area: M G floats per block <= the block's operands).
+// Same grid and tiles as launch_mfma, so the result has the bits of the rotation followed by
+// pn_gemv. Returns 1 where the shape is not taken (PN_GEMV_HADAMARD_PAIRS: never, for timing).
+template <int TYPE>
+static int launch_mfma_hadamard_t(const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
+                                  float *y, int cus, int hL, float hscale, hipStream_t s)
+{
+    using T = MTile<TYPE>;
+    const int64_t nb = K / T::G;
+    const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
+    const int pb_max = ((kMfmaLds - ring) / mfma_block_bytes<TYPE>(4)) & ~(kChunkBlocks - 1);
+    if (M < 3 || M > 4 || hL > 10 || !mfma_stages_weights(TYPE, W, N, K) || nb > pb_max ||
+        nb * M * 4 > kMfmaThreads * kMfmaUnits || M * K > 24576 || getenv("PN_GEMV_HADAMARD_PAIRS"))
+        return 1;
+    const int grid = (int)std::min<int64_t>(cus, (N + 15) / 16);
+    const int64_t rq = N / grid;
+    const int rr = (int)(N % grid);
+    return launch_mfma_lds_t<TYPE, 4, true>(W, N, (int)nb, x, K, M, y, grid, rq, rr, s, hL, hscale);
+}
+
+int launch_mfma_hadamard(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
+                         float *y, int cus, int hL, float hscale, hipStream_t s)
+{
+    if (type == PN_TYPE_PN3T)
+        return launch_mfma_hadamard_t<PN_TYPE_PN3T>(W, N, K, x, M, y, cus, hL, hscale, s);
+    return launch_mfma_hadamard_t<PN_TYPE_PN4T>(W, N, K, x, M, y, cus, hL, hscale, s);
 }
 
 }  // namespace pn

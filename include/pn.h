@@ -129,14 +129,20 @@ int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out
 /* y = W x' for M = 1..4 tokens: the PN GEMV (pn_gemv) over the rotated x, the rotation fused into
  * the kernels' x staging (each workgroup rotates x in its registers and LDS while its first
  * weight loads are in flight; x itself is not modified). Arguments as pn_gemv, plus B as in
- * pn_hadamard_rows. M outside 0..4 gives PN_ERR_TOKENS. Tokens are served two at a time, one
- * launch per pair (at 3-4 tokens W is read twice). The fused staging takes rows of at most 64
- * blocks, and longer rows whose x (2 * K floats for a pair) fits the long-row kernel's LDS area
- * (K up to about 34,000 at one token, 17,000 at two); other shapes give PN_ERR_SHAPE: rotate with
- * pn_hadamard_rows, then call pn_gemv. At 1-2 tokens it gives the same bits as pn_hadamard_rows
- * followed by pn_gemv on the same shape (the same transform, then the same kernel); at every M
- * the accuracy of the one- and two-token pn_gemv applies to the rotated x, plus the rotation's
- * own error above. */
+ * pn_hadamard_rows. M outside 0..4 gives PN_ERR_TOKENS.
+ * At 3-4 tokens one launch of the matrix-core kernel serves the call where W is 4-byte aligned,
+ * rows hold a multiple of 4 blocks (M * blocks <= 256, and at most 64 blocks for pn3t, 80 for
+ * pn4t), B <= 1024 and the offsets fit 31 bits; it gives the same bits, and the same accuracy, as
+ * pn_hadamard_rows followed by pn_gemv on the same shape. Otherwise tokens are served two at a
+ * time, one launch per pair (W read twice at 3-4 tokens), with the one- and two-token fused
+ * staging: rows of at most 64 blocks, and longer rows whose x (2 * K floats for a pair) fits the
+ * long-row kernel's LDS area (K up to about 34,000 at one token, 17,000 at two); other shapes
+ * give PN_ERR_SHAPE: rotate with pn_hadamard_rows, then call pn_gemv. At 1-2 tokens it gives the
+ * same bits as pn_hadamard_rows followed by pn_gemv on the same shape (the same transform, then
+ * the same kernel), and pairs the accuracy of the one- and two-token pn_gemv on the rotated x;
+ * the rotation's own error above adds to either. Every workgroup rotates the whole x of the
+ * call, so where one x feeds several calls (gate and up), rotating it once with pn_hadamard_rows
+ * and calling pn_gemv is cheaper. */
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 

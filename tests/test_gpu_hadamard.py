@@ -108,8 +108,8 @@ def test_rotation_exact_inputs(env, B):
         assert np.array_equal(rotate(pn, torch, dev, x1, B).astype(np.float64), ref), j
 
 
-def gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B):
-    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+def gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B, x_offset=0):
+    _, xd = dev_f32(torch, dev, x, x_offset)
     x_before = xd.clone()
     M = x.shape[0]
     yd = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
@@ -123,7 +123,8 @@ def gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B):
 # kernel; B below 256 rotates in registers only, above it through LDS.
 FUSED = [(PN3T, 300, 64, 1024), (PN3T, 77, 8, 128), (PN3T, 33, 16, 256), (PN4T, 45, 64, 4096),
          (PN4T, 260, 272, 1024), (PN4T, 70, 96, 2048), (PN3T, 41, 80, 256), (PN4T, 19, 130, 64),
-         (PN4T, 9, 256, 16384), (PN3T, 25, 8, 4), (PN4T, 31, 130, 8), (PN3T, 13, 64, 512)]
+         (PN4T, 9, 256, 16384), (PN3T, 25, 8, 4), (PN4T, 31, 130, 8), (PN3T, 13, 64, 512),
+         (PN4T, 50, 76, 256)]
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
@@ -159,6 +160,38 @@ def test_gemv_hadamard_equals_rotate_then_gemv(env, typ, N, nb, B, M):
     xr = rotate(pn, torch, dev, x, B)
     two = run_gemv(pn, torch, dev, typ, Wd, N, K, xr)
     assert np.array_equal(fused.view(np.uint32), two.view(np.uint32))
+
+
+# Three and four tokens in one launch of the matrix-core kernel (W 4-byte aligned, rows of a
+# multiple of 4 blocks, slices of at most 1024, the x of the call staged in one pass): (type, N,
+# nb, B, M). 40000 rows give workgroups two groups of tiles. pn4t with 76 blocks is taken at
+# three tokens only: four need two passes of units and go by pairs (in FUSED).
+MFMA_ROT = [(PN3T, 300, 64, 1024, 3), (PN3T, 300, 64, 1024, 4), (PN4T, 50, 76, 256, 3),
+            (PN3T, 25, 8, 4, 3), (PN3T, 25, 8, 4, 4), (PN3T, 40000, 8, 64, 3),
+            (PN3T, 40000, 8, 64, 4), (PN4T, 70, 64, 512, 3), (PN4T, 70, 64, 512, 4),
+            (PN3T, 16, 4, 2, 4)]
+
+
+@pytest.mark.parametrize("typ,N,nb,B,M", MFMA_ROT)
+@pytest.mark.parametrize("x_offset", [0, 1])
+def test_gemv_hadamard_mfma_equals_rotate_then_gemv(env, typ, N, nb, B, M, x_offset):
+    """At three and four tokens the single launch stages the rotated x exactly as the matrix-core
+    GEMV stages a given x: its bits equal pn_hadamard_rows followed by pn_gemv, and both are
+    within the oracle's tolerance. x 16-byte aligned or not (offset by one float)."""
+    pn, torch, dev = env
+    G = oracle.PARAMS[typ][1]
+    K = nb * G
+    _, W = quantized(typ, N, K, 5900 + nb)
+    Wd = dev_bytes(torch, dev, W)
+    x = synth.activations(5950 + nb + M, M, K)
+    fused = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B, x_offset)
+    xr = rotate(pn, torch, dev, x, B)
+    two = run_gemv(pn, torch, dev, typ, Wd, N, K, xr)
+    assert np.array_equal(fused.view(np.uint32), two.view(np.uint32))
+    y_ref, bound, rbound = oracle.gemv_hadamard(typ, W, N, K, x, B)
+    tol = 1e-5 * bound + (1 + 1e-5) * gamma(B) * rbound
+    err = np.abs(fused.astype(np.float64) - y_ref)
+    assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
 
 
 def test_gemv_hadamard_one_hot_column(env):
