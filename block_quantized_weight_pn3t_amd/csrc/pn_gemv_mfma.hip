@@ -370,8 +370,9 @@ __device__ __forceinline__ void mfma_read_a(MfmaA &a, const uint8_t *blk, int g,
 // per k-step covers both; K-split (up to 16 tokens): hi and lo are two A operands on the same
 // codes. `after_loads` runs once the first x loads are issued (a caller's weight prefetch: loads
 // retire in order, so waiting for x then leaves the prefetch in flight).
-// LX: x comes from LDS instead (fp32 [M][K] at the start of the x area, the rotated x): every
-// unit is read before the area is overwritten (one chunk of units; the caller ensures it).
+// LX: x comes from LDS instead (fp32 [M][K] at the start of the x area, the rotated x), 4 units
+// per thread: every unit is read before the area is overwritten (one pass of at most 2048 units;
+// the caller ensures it).
 template <int TYPE, bool SLOT, int EG, class F, bool LX = false>
 __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t K, int M,
                                            int ML, int pb0, int npb, int xvec4, F after_loads)
@@ -380,8 +381,9 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
     constexpr int PERG = T::PERG;
     const int tid = threadIdx.x;
     const int per_block = mfma_block_bytes<TYPE>(ML), e_off = mfma_a_bytes<TYPE>(ML);
+    constexpr int UNITS = LX ? 4 : kMfmaUnits;  // units per thread and pass
     const int U = npb * M * 4;
-    const int nch = (U + kMfmaThreads * kMfmaUnits - 1) / (kMfmaThreads * kMfmaUnits);
+    const int nch = (U + kMfmaThreads * UNITS - 1) / (kMfmaThreads * UNITS);
     // unit u: k-group u % 4, then the block within its group of EG, then the token, then the group
     auto unit_coords = [&](int u, int &gg, int &m, int &brel) {
         gg = u & 3;
@@ -396,13 +398,13 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
     uint64_t xaddr = reinterpret_cast<uint64_t>(x);
     asm volatile("" : "+s"(xaddr));
     gfloat_t *xg = reinterpret_cast<gfloat_t *>(xaddr);
-    float xr[kMfmaUnits][PERG];
+    float xr[UNITS][PERG];
     // loads outside any branch (a unit past the end loads the last one again), so the waits for
     // them can leave the weight prefetch issued after them in flight
     auto load = [&](int c) {
 #pragma unroll
-        for (int ub = 0; ub < kMfmaUnits; ub++) {
-            const int u = min((c * kMfmaUnits + ub) * kMfmaThreads + tid, U - 1);
+        for (int ub = 0; ub < UNITS; ub++) {
+            const int u = min((c * UNITS + ub) * kMfmaThreads + tid, U - 1);
             int gg, m, brel;
             unit_coords(u, gg, m, brel);
             if constexpr (LX) {
@@ -424,8 +426,8 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
     };
     auto convert = [&](int c) {
     #pragma unroll
-            for (int ub = 0; ub < kMfmaUnits; ub++) {
-                const int u = (c * kMfmaUnits + ub) * kMfmaThreads + tid;
+            for (int ub = 0; ub < UNITS; ub++) {
+                const int u = (c * UNITS + ub) * kMfmaThreads + tid;
                 if (u < U) {  // U is a multiple of 4 EG: whole lane groups take this branch
                     int gg, m, brel;
                     unit_coords(u, gg, m, brel);
@@ -995,7 +997,7 @@ int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x
 
 // The GEMV over Hadamard-rotated x at 3-4 tokens in one launch of the weight-staging kernel:
 // W as mfma_stages_weights takes it, slices of at most 1024 elements, and the x of the call
-// staged in one phase and one pass of units (at most 256 blocks over the tokens; every shape
+// staged in one phase and one pass of units (at most 512 blocks over the tokens; every shape
 // within this fits the fp32 x in the x area: M G floats per block <= the block's operands).
 // Same grid and tiles as launch_mfma, so the result has the bits of the rotation followed by
 // pn_gemv. Returns 1 where the shape is not taken (PN_GEMV_HADAMARD_PAIRS: never, for timing).
@@ -1008,7 +1010,7 @@ static int launch_mfma_hadamard_t(const uint8_t *W, int64_t N, int64_t K, const 
     const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
     const int pb_max = ((kMfmaLds - ring) / mfma_block_bytes<TYPE>(4)) & ~(kChunkBlocks - 1);
     if (M < 3 || M > 4 || hL > 10 || !mfma_stages_weights(TYPE, W, N, K) || nb > pb_max ||
-        nb * M * 4 > kMfmaThreads * kMfmaUnits || M * K > 24576 || getenv("PN_GEMV_HADAMARD_PAIRS"))
+        nb * M * 4 > kMfmaThreads * 4 || M * K > 24576 || getenv("PN_GEMV_HADAMARD_PAIRS"))
         return 1;
     const int grid = (int)std::min<int64_t>(cus, (N + 15) / 16);
     const int64_t rq = N / grid;

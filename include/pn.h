@@ -131,9 +131,9 @@ int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out
  * weight loads are in flight; x itself is not modified). Arguments as pn_gemv, plus B as in
  * pn_hadamard_rows. M outside 0..4 gives PN_ERR_TOKENS.
  * At 3-4 tokens one launch of the matrix-core kernel serves the call where W is 4-byte aligned,
- * rows hold a multiple of 4 blocks (M * blocks <= 256, and at most 64 blocks for pn3t, 80 for
- * pn4t), B <= 1024 and the offsets fit 31 bits; it gives the same bits, and the same accuracy, as
- * pn_hadamard_rows followed by pn_gemv on the same shape. Otherwise tokens are served two at a
+ * rows hold a multiple of 4 blocks (at most 64 for pn3t, 80 for pn4t), B <= 1024 and the
+ * offsets fit 31 bits; it gives the same bits, and the same accuracy, as pn_hadamard_rows
+ * followed by pn_gemv on the same shape. Otherwise tokens are served two at a
  * time, one launch per pair (W read twice at 3-4 tokens), with the one- and two-token fused
  * staging: rows of at most 64 blocks, and longer rows whose x (2 * K floats for a pair) fits the
  * long-row kernel's LDS area (K up to about 34,000 at one token, 17,000 at two); other shapes

@@ -164,9 +164,10 @@ def test_gemv_hadamard_equals_rotate_then_gemv(env, typ, N, nb, B, M):
 
 # Three and four tokens in one launch of the matrix-core kernel (W 4-byte aligned, rows of a
 # multiple of 4 blocks, slices of at most 1024, the x of the call staged in one pass): (type, N,
-# nb, B, M). 40000 rows give workgroups two groups of tiles. pn4t with 76 blocks is taken at
-# three tokens only: four need two passes of units and go by pairs (in FUSED).
+# nb, B, M). 40000 rows give workgroups two groups of tiles; pn4t with 80 blocks is the longest
+# row it takes (FUSED has longer rows and larger slices, which go by pairs).
 MFMA_ROT = [(PN3T, 300, 64, 1024, 3), (PN3T, 300, 64, 1024, 4), (PN4T, 50, 76, 256, 3),
+            (PN4T, 50, 76, 256, 4), (PN4T, 33, 80, 1024, 4),
             (PN3T, 25, 8, 4, 3), (PN3T, 25, 8, 4, 4), (PN3T, 40000, 8, 64, 3),
             (PN3T, 40000, 8, 64, 4), (PN4T, 70, 64, 512, 3), (PN4T, 70, 64, 512, 4),
             (PN3T, 16, 4, 2, 4)]
