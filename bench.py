@@ -276,6 +276,50 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     return out
 
 
+def shard_shapes(pn, torch, dev, mats, reps, warmup):
+    """One GPU's share of the MLP step at M = 1 when G = 2, 4, 8 GPUs share it: gate+up split by
+    rows (G slices of N/G rows of the stacked 34816x5120 pn3t; no reduction), down split along K
+    at block boundaries (5120 x 17408/G pn4t, a partial y per GPU for one all-reduce). Every
+    slice of every rotated copy is its own buffer (> 256 MB in rotation). Launch-to-launch µs of
+    the two launches and of each alone; the collective and the x broadcast are not part of it."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    gu, dn = mats
+    out = {}
+    for G in (2, 4, 8):
+        n_gu = gu["N"] // G
+        nb_dn = dn["K"] // 64 // G
+        k_dn = nb_dn * 64
+        gu_sh = [W[g * n_gu:(g + 1) * n_gu] for W in gu["Ws"] for g in range(G)]
+        dn_sh = [W.view(dn["N"], -1, 34)[:, g * nb_dn:(g + 1) * nb_dn].contiguous()
+                 for W in dn["Ws"] for g in range(G)]
+        x_dn = dn["x"][:, :k_dn].contiguous()
+        b_gu, b_dn = gu_sh[0].numel(), dn_sh[0].numel()
+
+        def l_gu(c):
+            check(pn.gemv_ptr(124, gu_sh[c].data_ptr(), n_gu, gu["K"], gu["x"].data_ptr(), 1,
+                              gu["y"].data_ptr(), sh), "pn_gemv")
+
+        def l_dn(c):
+            check(pn.gemv_ptr(125, dn_sh[c].data_ptr(), dn["N"], k_dn, x_dn.data_ptr(), 1,
+                              dn["y"].data_ptr(), sh), "pn_gemv")
+
+        def step(c):
+            l_gu(c)
+            l_dn(c)
+        n = len(gu_sh)
+        us = time_launches(torch, stream, step, n, reps, warmup)
+        us_gu = time_launches(torch, stream, l_gu, n, reps, warmup)
+        us_dn = time_launches(torch, stream, l_dn, n, reps, warmup)
+        out[f"G{G}"] = {"gate_up": f"{n_gu}x{gu['K']} pn3t", "down": f"{dn['N']}x{k_dn} pn4t",
+                        "step_us": round(us, 3), "GBs": round((b_gu + b_dn) / us / 1e3, 1),
+                        "gate_up_us": round(us_gu, 3), "gate_up_GBs": round(b_gu / us_gu / 1e3, 1),
+                        "down_us": round(us_dn, 3), "down_GBs": round(b_dn / us_dn / 1e3, 1)}
+        del gu_sh, dn_sh
+    log("[bench] extra: shard shapes done")
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle's GEMV timed on the host cores: a bounded sample (1/16 of the rows of each MLP
     matrix, quantized by the oracle), repeated to ~`seconds` of work."""
@@ -427,6 +471,8 @@ def main():
     }
     if not args.no_extra:
         result["extra"] = extra_workloads(pn, torch, dev, args.steps, args.warmup)
+        result["extra"]["mlp_shard_M1"] = shard_shapes(pn, torch, dev, mats, args.steps,
+                                                       args.warmup)
     if args.copy_mb > 0:
         copy_calibration(torch, dev, args.copy_mb)
     if args.cpu_seconds > 0:
