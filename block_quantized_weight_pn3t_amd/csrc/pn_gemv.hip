@@ -1239,6 +1239,12 @@ static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, in
     case 2:
         if (short_rows)
             return launch_xreg<TYPE, 2, 2>(W, N, K, x, y, s);
+        // rows of 65-128 blocks: the matrix cores, where they stage the weights, beat the
+        // long-row kernel at two tokens (0.3-2 us per launch at 5120 rows); longer rows and
+        // one token stay on the vector units (PN_GEMV_NO_MFMA keeps them there)
+        if (K / Fmt<TYPE>::G > 64 && K / Fmt<TYPE>::G <= 128 && !getenv("PN_GEMV_NO_MFMA") &&
+            mfma_stages_weights(TYPE, W, N, K))
+            return launch_mfma(TYPE, W, N, K, x, 2, y, num_cus(), s);
         if (flat && (st = launch_flat<TYPE, 2>(W, N, K, x, y, s)) != kNotApplicable)
             return st;
         return launch_lds<TYPE, 2, 2, 2>(W, N, K, x, y, s);

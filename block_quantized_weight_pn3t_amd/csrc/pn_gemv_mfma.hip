@@ -638,7 +638,7 @@ constexpr int kStepLoads = 9;                                  // buffer loads p
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// MC: the token capacity of the x layout (4, 8 or 16; M <= MC), so that every LDS offset of
+// MC: the token capacity of the x layout (2, 4, 8 or 16; M <= MC), so that every LDS offset of
 // the loop is a constant. Up to 8, hi and lo are token slots.
 // ROT (3-4 tokens, one phase of x, one chunk of staging units, slices of at most 1024): x is
 // first rotated, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the Hadamard rotation of
@@ -961,7 +961,8 @@ static int launch_mfma_t(const uint8_t *W, int64_t N, int64_t K, const float *x,
     // weights staged through LDS (4-byte aligned W, rows of a multiple of 4 blocks);
     // PN_GEMV_MFMA_DIRECT keeps the direct-load kernel (tests, timing)
     if (mfma_stages_weights(TYPE, W, N, K))
-        return M <= 4   ? launch_mfma_lds_t<TYPE, 4>(W, N, nb, x, K, M, y, grid, rq, rr, s)
+        return M == 2   ? launch_mfma_lds_t<TYPE, 2>(W, N, nb, x, K, M, y, grid, rq, rr, s)
+               : M <= 4 ? launch_mfma_lds_t<TYPE, 4>(W, N, nb, x, K, M, y, grid, rq, rr, s)
                : M <= 8 ? launch_mfma_lds_t<TYPE, 8>(W, N, nb, x, K, M, y, grid, rq, rr, s)
                         : launch_mfma_lds_t<TYPE, 16>(W, N, nb, x, K, M, y, grid, rq, rr, s);
     const int per_block = mfma_block_bytes<TYPE>(M);

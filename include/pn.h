@@ -96,14 +96,14 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
  *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
  *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
- *  - M >= 3 on the matrix cores (3 and 4 tokens when W is 4-byte aligned and rows hold a
- *    multiple of 4 blocks; every shape from 5 tokens): the zero point is taken off each code
- *    exactly (no fold), and each x is carried as an fp16 (hi, lo) pair with one exponent per
- *    token and group of blocks (4 consecutive blocks where W is staged through LDS, one block
- *    where it is read directly): exact to 2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the
- *    largest |x| in its group, whichever is larger -- every x that meets a nonzero weight must
- *    be within about 2^14 of the largest |x| of its group, or the group's other terms must
- *    dominate.
+ *  - On the matrix cores (every shape from 5 tokens; at 3 and 4 tokens when W is 4-byte aligned
+ *    and rows hold a multiple of 4 blocks; at 2 tokens when, in addition, rows hold 65 to 128
+ *    blocks): the zero point is taken off each code exactly (no fold), and each x is carried as
+ *    an fp16 (hi, lo) pair with one exponent per token and group of blocks (4 consecutive
+ *    blocks where W is staged through LDS, one block where it is read directly): exact to
+ *    2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the largest |x| in its group, whichever
+ *    is larger -- every x that meets a nonzero weight must be within about 2^14 of the largest
+ *    |x| of its group, or the group's other terms must dominate.
  *    Every other path uses x exactly (scaled by powers of two). Rows are not
  * validated here (validate at load); an invalid row gives an unspecified value but no
  * out-of-bounds access. Deterministic: the same inputs and launch give the same bits on every

@@ -1,5 +1,7 @@
-"""GPU parity of the PN GEMV at 3..16 tokens (the matrix-core path from 5 tokens, and at 3-4 when forced) through the C ABI against the
-CPU oracle ("PN weight format", "Block layout" and "Value"; the sum y = W x itself).
+"""GPU parity of the PN GEMV on the matrix-core path (every shape from 5 tokens; at 3-4 tokens on
+stageable weights or when forced; at 2 tokens on stageable rows of 65-128 blocks) and of the
+vector-unit kernels where forced, through the C ABI against the CPU oracle ("PN weight format",
+"Block layout" and "Value"; the sum y = W x itself).
 
 Tolerance as for every PN GEMV: |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output. The cases cover
 ragged row counts (a last tile of 16 rows partly empty), both alignment parities of the weights,
@@ -171,10 +173,39 @@ def test_gemv_direct_weight_loads_forced(env, monkeypatch, typ, N, nb, M):
     assert_within(y, y_ref, bound)
 
 
-@pytest.mark.parametrize("M", [3, 4])
-@pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 45, 128)])
+@pytest.mark.parametrize("typ,N,nb", [(PN4T, 300, 80), (PN4T, 1024, 80), (PN4T, 77, 96),
+                                      (PN3T, 37, 68), (PN3T, 515, 128), (PN4T, 9, 100)])
+def test_gemv_two_tokens_matrix_cores(env, typ, N, nb):
+    """Two tokens on rows of 65-128 blocks (W 4-byte aligned, a multiple of 4 blocks) run on the
+    matrix cores with a two-token x layout; with W at +2 bytes the long-row kernel serves them."""
+    pn, torch, dev = env
+    K, W = case(typ, N, nb, 9400 + nb)
+    x = synth.activations(9500 + nb, 2, K)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    for offset in (0, 2):
+        y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
+        assert_within(y, y_ref, bound)
+
+
+def test_gemv_two_tokens_matrix_cores_x_phases(env):
+    """Two tokens whose magnitudes ramp over 2^24 along K: each group of 4 blocks takes its own
+    exponent, within the documented range."""
+    pn, torch, dev = env
+    typ, N, nb = PN4T, 130, 96
+    K, W = case(typ, N, nb, 9450)
+    x = synth.activations(9451, 2, K).astype(np.float64)
+    ramp = np.linspace(-12.0, 12.0, K)
+    x[0] *= 2.0 ** ramp
+    x[1] *= 2.0 ** ramp[::-1]
+    x = x.astype(np.float32)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    assert_within(run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x), y_ref, bound)
+
+
+@pytest.mark.parametrize("M,typ,N,nb", [(3, PN3T, 37, 64), (3, PN4T, 45, 128), (4, PN3T, 37, 64),
+                                        (4, PN4T, 45, 128), (2, PN4T, 45, 128), (2, PN3T, 33, 80)])
 def test_gemv_vector_kernel_forced(env, monkeypatch, typ, N, nb, M):
-    """The vector-unit kernel at 3-4 tokens on shapes the matrix cores take by default."""
+    """The vector-unit kernels at 2-4 tokens on shapes the matrix cores take by default."""
     pn, torch, dev = env
     monkeypatch.setenv("PN_GEMV_NO_MFMA", "1")
     K, W = case(typ, N, nb, 9950 + nb)
