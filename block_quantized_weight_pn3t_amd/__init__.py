@@ -11,7 +11,7 @@ import ctypes as C
 import os
 
 __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
-           "dequantize_rows", "dequantize_row", "gemv", "quantize_rows", "hadamard_rows",
+           "dequantize_rows", "dequantize_row", "gemv", "gemv_group", "quantize_rows", "hadamard_rows",
            "gemv_hadamard", "nvfp4_validate_rows",
            "nvfp4_dequantize_rows", "gemv_nvfp4", "nvfp4_global_scale", "nvfp4_quantize_rows",
            "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row", "fp8row_quantize_rows",
@@ -23,6 +23,7 @@ GROUP = {PN3T: 80, PN4T: 64}
 MAX_TOKENS = 4         # NVFP4 and row-scaled E4M3 GEMV
 GEMV_MAX_TOKENS = 16   # PN GEMV
 GEMV_HADAMARD_MAX_TOKENS = 4  # PN GEMV with the rotation fused
+GEMV_GROUP_MAX_PARTS = 4  # matrices per pn_gemv_group call
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpn.so")
@@ -32,6 +33,13 @@ if not os.path.exists(library_path):
 
 _lib = C.CDLL(library_path)
 _P, _I64, _I32, _F = C.c_void_p, C.c_int64, C.c_int, C.c_float
+
+
+class GemvPart(C.Structure):
+    """pn_gemv_part of include/pn.h: one matrix of a pn_gemv_group call."""
+    _fields_ = [("type", C.c_int), ("W", C.c_void_p), ("N", C.c_int64), ("y", C.c_void_p)]
+
+
 _SIGS = {
     "pn_row_bytes": (_I64, [_I32, _I64]),
     "pn_status_string": (C.c_char_p, [_I32]),
@@ -40,6 +48,7 @@ _SIGS = {
     "pn_dequantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P]),
     "pn_dequantize_row": (_I32, [_I32, _P, _I64, _P, _P]),
     "pn_gemv": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "pn_gemv_group": (_I32, [C.POINTER(GemvPart), _I32, _I64, _P, _I64, _P]),
     "pn_quantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
     "pn_hadamard_rows": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "pn_gemv_hadamard": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
@@ -139,6 +148,32 @@ def gemv(type_, W, N, K, x, y, M=None, stream=None):
     if M is None:
         M = 1 if x.dim() == 1 else x.shape[0]
     _check(_lib.pn_gemv(type_, _ptr(W), N, K, _ptr(x), M, _ptr(y), _stream(stream)), "pn_gemv")
+
+
+def gemv_group(parts, K, x, M=None, stream=None):
+    """Several PN GEMVs that share x: parts is a sequence of (type, W, N, y) with W raw PN bytes
+    and y fp32[M, N] on the device; every y[M, N] <- W[N, K] . x[M, K]^T, in one launch where the
+    shapes allow (pn_gemv_group)."""
+    import torch
+    _dev(x, "x", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    arr = (GemvPart * len(parts))()
+    for i, (type_, W, N, y) in enumerate(parts):
+        _dev(y, "y", torch.float32)
+        arr[i] = GemvPart(type_, _ptr(W), N, _ptr(y))
+    _check(_lib.pn_gemv_group(arr, len(parts), K, _ptr(x), M, _stream(stream)), "pn_gemv_group")
+
+
+def gemv_group_ptr(parts, K, x_ptr, M, stream_handle):
+    """Raw-pointer form for timing loops: parts is a sequence of (type, W_ptr, N, y_ptr) or a
+    prepared GemvPart array; returns the status instead of raising."""
+    if not isinstance(parts, C.Array):
+        arr = (GemvPart * len(parts))()
+        for i, (type_, W, N, y) in enumerate(parts):
+            arr[i] = GemvPart(type_, W, N, y)
+        parts = arr
+    return _lib.pn_gemv_group(parts, len(parts), K, x_ptr, M, stream_handle)
 
 
 def gemv_ptr(type_, W_ptr, N, K, x_ptr, M, y_ptr, stream_handle):

@@ -165,10 +165,11 @@ struct RowSplit {
     int rr;      // N % (gridDim.x * 4)
 };
 
+// (blk: the workgroup's index among those that share the rows)
 __device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int nwaves, int fnum,
-                                          int64_t &begin, int &count)
+                                          int64_t &begin, int &count, int blk)
 {
-    const int slot = blockIdx.x * 4 + (wave & 3);
+    const int slot = blk * 4 + (wave & 3);
     const int h = wave >> 2;
     const int64_t s0 = (int64_t)slot * sp.rq + min(slot, sp.rr);
     const int64_t cnt = sp.rq + (slot < sp.rr ? 1 : 0);
@@ -179,6 +180,11 @@ __device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int 
     count = (int)(b1 - b0);
     // an empty range may start at N; its (unused, clamped) prefetch must still address a real row
     begin = min(s0 + b0, N - 1);
+}
+__device__ __forceinline__ void wave_rows(int64_t N, RowSplit sp, int wave, int nwaves, int fnum,
+                                          int64_t &begin, int &count)
+{
+    wave_rows(N, sp, wave, nwaves, fnum, begin, count, (int)blockIdx.x);
 }
 
 inline RowSplit row_split(int64_t N, int grid)

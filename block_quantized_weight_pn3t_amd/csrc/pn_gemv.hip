@@ -478,12 +478,12 @@ constexpr int kFlatWaves = 8;  // waves per workgroup of the flat kernel (two pe
 // rotation of "Files that use PN", as read in pn_hadamard.h), in the registers that hold it
 // (stages 0-7) and through the x area of LDS (stages 8 and up), before it is staged.
 template <int TYPE, int M, int R, int D, int QPT, bool ROT>
-__global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__restrict__ W, int64_t N,
+__device__ __forceinline__ void flat_body(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
                                                             const float *__restrict__ x, int64_t K,
                                                             float *__restrict__ y, int64_t gq,
                                                             int gr, int x_vec4, int fnum, int hL,
-                                                            float hscale)
+                                                            float hscale, int blk_id)
 {
     using F = Fmt<TYPE>;
     constexpr int V = ((M * R + 3) / 4) * 4;
@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
 
     // this workgroup's groups [P0, P1) and this wave's piece [F0, F1) of its (group, block) pairs
     // (gq, gr: quotient and remainder of the group count by the grid, from the host)
-    const int blk = blockIdx.x;
+    const int blk = blk_id;
     const int64_t P0 = (int64_t)blk * gq + min(blk, gr);
     const int T = (int)(gq + (blk < gr ? 1 : 0)) * nb;  // < 2^30 (checked on the host)
     // SIMD j = wave & 3 takes the quarter [q0, q1) of the range; its older wave (h = 0) the first
@@ -531,9 +531,9 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
     // the CUs of an XCD do not all request the same lines of x, i.e. the same L2 channel, at once.
     // (with ROT by whole 1024-element pieces, which its waves transform: 256 float4 units, where
     // x holds a whole number of them)
-    const int rot = !ROT ? (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(M * nb)) * QB
+    const int rot = !ROT ? (int)(((uint32_t)blk_id * 17u) % (uint32_t)(M * nb)) * QB
                     : (total & 255) ? 0
-                                    : (int)(((uint32_t)blockIdx.x * 17u) % (uint32_t)(total >> 8)) * 256;
+                                    : (int)(((uint32_t)blk_id * 17u) % (uint32_t)(total >> 8)) * 256;
     auto rotq = [&](int q) { q += rot; return q >= total ? q - total : q; };
     auto token_of = [](int q, int per) {  // q / per for q < M * per, without a division
         int m = 0;
@@ -853,6 +853,17 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
         }
     }
 }
+template <int TYPE, int M, int R, int D, int QPT, bool ROT>
+__global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__restrict__ W, int64_t N,
+                                                            int nb, int64_t row_bytes,
+                                                            const float *__restrict__ x, int64_t K,
+                                                            float *__restrict__ y, int64_t gq,
+                                                            int gr, int x_vec4, int fnum, int hL,
+                                                            float hscale)
+{
+    flat_body<TYPE, M, R, D, QPT, ROT>(W, N, nb, row_bytes, x, K, y, gq, gr, x_vec4, fnum, hL,
+                                       hscale, (int)blockIdx.x);
+}
 
 // ---- short rows: staged x in registers ----------------------------------------------------------
 
@@ -864,12 +875,12 @@ __global__ void __launch_bounds__(512) pn_gemv_flat_kernel(const uint8_t *__rest
 // ROT: x is first rotated into LDS, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the
 // Hadamard rotation of "Files that use PN", as read in pn_hadamard.h); the staging then reads x'.
 template <int TYPE, int M, int D, bool ROT>
-__global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__restrict__ W, int64_t N,
+__device__ __forceinline__ void xreg_body(const uint8_t *__restrict__ W, int64_t N,
                                                             int nb, int64_t row_bytes,
                                                             const float *__restrict__ x, int64_t K,
                                                             float *__restrict__ y, RowSplit sp,
                                                             int x_vec4, int fnum, int hL,
-                                                            float hscale)
+                                                            float hscale, int blk_id)
 {
     using F = Fmt<TYPE>;
     constexpr int RPR = 4 / M;  // rows per reduction
@@ -878,7 +889,7 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t r_begin;
     int nrows;
-    wave_rows(N, sp, wave, nwaves, fnum, r_begin, nrows);
+    wave_rows(N, sp, wave, nwaves, fnum, r_begin, nrows, blk_id);
     const bool active = lane < nb;
     const int b = min(lane, nb - 1);
     const uint8_t *wbase = W + r_begin * row_bytes + (int64_t)kBlockBytes * b;
@@ -887,7 +898,7 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     // The x loads are issued before the first weight loads, so waiting for x never waits for
     // weights (the memory counter retires loads in order).
     // (blocks taken in an order rotated by the workgroup index, as in the long-row kernel)
-    const int bb = ((threadIdx.x >> 3) + blockIdx.x * 5) & 63, i = threadIdx.x & 7;
+    const int bb = ((threadIdx.x >> 3) + blk_id * 5) & 63, i = threadIdx.x & 7;
     const bool have = bb < nb;
     float xv[M][F::CPW];
     auto load_x = [&](const float *xs, int vec) {
@@ -913,7 +924,7 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
     // workgroups start at different 1024-element pieces of x (as the plain staging rotates its
     // blocks), so that the CUs of an XCD do not request the same lines at once
     const int hrot = (!ROT || (total4 & 255)) ? 0
-                     : (int)(((uint32_t)blockIdx.x * 5u) % (uint32_t)(total4 >> 8)) * 256;
+                     : (int)(((uint32_t)blk_id * 5u) % (uint32_t)(total4 >> 8)) * 256;
     auto hq = [&](int q) { q += hrot; return q >= total4 ? q - total4 : q; };
     float4 hv[HQ];
     if constexpr (ROT) {
@@ -1091,6 +1102,17 @@ __global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__rest
             }
         }
     }
+}
+template <int TYPE, int M, int D, bool ROT>
+__global__ void __launch_bounds__(512) pn_gemv_xreg_kernel(const uint8_t *__restrict__ W, int64_t N,
+                                                            int nb, int64_t row_bytes,
+                                                            const float *__restrict__ x, int64_t K,
+                                                            float *__restrict__ y, RowSplit sp,
+                                                            int x_vec4, int fnum, int hL,
+                                                            float hscale)
+{
+    xreg_body<TYPE, M, D, ROT>(W, N, nb, row_bytes, x, K, y, sp, x_vec4, fnum, hL, hscale,
+                               (int)blockIdx.x);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
@@ -1283,6 +1305,168 @@ static int dispatch_hadamard(const uint8_t *W, int64_t N, int64_t K, const float
     return PN_ERR_SHAPE;
 }
 
+// ---- several GEMVs that share x, in one launch -----------------------------------------------
+// One grid serves up to 4 matrices (parts) that read the same x: part i owns the workgroups
+// [start_i, start_{i+1}), and within them runs the register kernel's body (rows of at most 64
+// blocks) or the long-row kernel's body (longer rows whose x fits, 8 float4 of x per thread),
+// exactly as its own launch of that many workgroups would. The parts' fixed costs (x staging,
+// the first weight latency, drain) then run side by side instead of one launch after another.
+constexpr int kGroupMax = 4;
+enum { kGroupXreg3 = 0, kGroupXreg4 = 1, kGroupFlat3 = 2, kGroupFlat4 = 3 };
+
+struct GroupPart {
+    const uint8_t *W;
+    float *y;
+    int64_t N, row_bytes, gq;
+    RowSplit sp;
+    int nb, kind, start, gr, fnum;
+};
+
+struct GroupArgs {
+    GroupPart p[kGroupMax];
+    const float *x;
+    int64_t K;
+    int count, x_vec4;
+};
+
+template <int M>
+__global__ void __launch_bounds__(512) pn_gemv_group_kernel(GroupArgs ga)
+{
+    constexpr int D = M == 1 ? 4 : 2;  // the register kernel's ring, as its own launch uses
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kGroupMax; j++)
+        if (j < ga.count && (int)blockIdx.x >= ga.p[j].start)
+            i = j;
+    const GroupPart &p = ga.p[i];
+    const int blk = (int)blockIdx.x - p.start;
+    switch (p.kind) {
+    case kGroupXreg3:
+        xreg_body<PN_TYPE_PN3T, M, D, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
+                                             ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        break;
+    case kGroupXreg4:
+        xreg_body<PN_TYPE_PN4T, M, D, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
+                                             ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        break;
+    case kGroupFlat3:
+        flat_body<PN_TYPE_PN3T, M, 2, 4, 8, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
+                                                   p.gq, p.gr, ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        break;
+    default:
+        flat_body<PN_TYPE_PN4T, M, 2, 4, 8, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
+                                                   p.gq, p.gr, ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        break;
+    }
+}
+
+// Static LDS of the group kernel: the register kernel's staging area for both types.
+template <int M> constexpr int group_static_lds()
+{
+    return M * 64 * (Fmt<PN_TYPE_PN3T>::LDS_STRIDE + Fmt<PN_TYPE_PN4T>::LDS_STRIDE) * 4;
+}
+
+// The part's kind and its dynamic LDS need, or -1 where neither body takes the shape.
+template <int M>
+static int group_kind(int type, int64_t N, int64_t K, int grid_max, size_t &lds)
+{
+    const int G = type == PN_TYPE_PN3T ? Fmt<PN_TYPE_PN3T>::G : Fmt<PN_TYPE_PN4T>::G;
+    const int stride =
+        type == PN_TYPE_PN3T ? Fmt<PN_TYPE_PN3T>::LDS_STRIDE : Fmt<PN_TYPE_PN4T>::LDS_STRIDE;
+    const int64_t nb = K / G;
+    lds = 0;
+    if (nb <= 64)
+        return type == PN_TYPE_PN3T ? kGroupXreg3 : kGroupXreg4;
+    constexpr int V = ((M * 2 + 3) / 4) * 4;
+    lds = (size_t)M * nb * stride * sizeof(float) + (size_t)kFlatWaves * 2 * V * sizeof(float) +
+          kFlatWaves * 4 * sizeof(int);
+    const int64_t need = (M * nb * (G / 4) + 64 * kFlatWaves - 1) / (64 * kFlatWaves);
+    const int64_t NP = (N + 1) / 2;
+    if (need > 8 || lds + group_static_lds<M>() > (size_t)kMaxLds ||
+        ((NP + grid_max - 1) / grid_max) * nb >= (int64_t(1) << 30))
+        return -1;
+    return type == PN_TYPE_PN3T ? kGroupFlat3 : kGroupFlat4;
+}
+
+// Launches the group, or returns kNotApplicable where a part's shape is not taken.
+template <int M>
+static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const float *x,
+                        hipStream_t s)
+{
+    const int cus = num_cus();
+    GroupArgs ga{};
+    int idx[kGroupMax], n = 0;
+    size_t lds = 0;
+    double bytes[kGroupMax], total = 0.0;
+    int cap[kGroupMax];
+    for (int i = 0; i < count; i++) {
+        if (parts[i].N == 0)
+            continue;
+        size_t l = 0;
+        const int kind = group_kind<M>(parts[i].type, parts[i].N, K, cus, l);
+        if (kind < 0)
+            return kNotApplicable;
+        GroupPart &g = ga.p[n];
+        g.W = (const uint8_t *)parts[i].W;
+        g.y = parts[i].y;
+        g.N = parts[i].N;
+        g.row_bytes = pn_row_bytes(parts[i].type, K);
+        g.nb = (int)(g.row_bytes / kBlockBytes);
+        g.kind = kind;
+        g.fnum = kind <= kGroupXreg4 ? older_share(12) : older_share(10);
+        bytes[n] = (double)g.N * (double)g.row_bytes;
+        total += bytes[n];
+        // workgroups beyond these would get no rows (register body: 4 rows per workgroup at
+        // least; long-row body: one row pair)
+        cap[n] = (int)std::min<int64_t>(cus, kind <= kGroupXreg4 ? (g.N + 3) / 4 : (g.N + 1) / 2);
+        lds = std::max(lds, l);
+        idx[n++] = i;
+    }
+    if (n == 0)
+        return PN_OK;
+    // workgroups in proportion to bytes (at least one each), the rest to the most loaded part
+    int grid[kGroupMax], used = 0;
+    for (int j = 0; j < n; j++) {
+        grid[j] = std::max(1, std::min(cap[j], (int)(cus * bytes[j] / total)));
+        used += grid[j];
+    }
+    while (used < cus) {
+        int best = -1;
+        double load = 0.0;
+        for (int j = 0; j < n; j++)
+            if (grid[j] < cap[j] && bytes[j] / grid[j] > load) {
+                load = bytes[j] / grid[j];
+                best = j;
+            }
+        if (best < 0)
+            break;
+        grid[best]++;
+        used++;
+    }
+    int start = 0;
+    for (int j = 0; j < n; j++) {
+        GroupPart &g = ga.p[j];
+        g.start = start;
+        start += grid[j];
+        g.sp = row_split(g.N, grid[j]);
+        const int64_t NP = (g.N + 1) / 2;
+        g.gq = NP / grid[j];
+        g.gr = (int)(NP % grid[j]);
+        if (g.kind >= kGroupFlat3 && (g.gq + 1) * g.nb >= (int64_t(1) << 30))
+            return kNotApplicable;  // the long-row body's (row pair, block) index must fit 30 bits
+    }
+    (void)idx;
+    ga.count = n;
+    ga.x = x;
+    ga.K = K;
+    ga.x_vec4 = aligned(x, 16) ? 1 : 0;
+    constexpr auto kern = pn_gemv_group_kernel<M>;
+    if (!lds_limit_once<kern>(kMaxLds - group_static_lds<M>()))
+        return PN_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3((unsigned)start), dim3(512), lds, s, ga);
+    return launch_status();
+}
+
 int hadamard_log(int64_t B, int64_t K);
 float hadamard_scale(int L);
 int launch_mfma_hadamard(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
@@ -1327,6 +1511,64 @@ extern "C" int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, c
                                                    y + m0 * N, L, hs, s)
                  : dispatch_hadamard<PN_TYPE_PN4T>((const uint8_t *)W, N, K, x + m0 * K, mc,
                                                    y + m0 * N, L, hs, s);
+        if (st != PN_OK)
+            return st;
+    }
+    return PN_OK;
+}
+
+extern "C" int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, const float *x,
+                             int64_t M, void *stream)
+{
+    if (count < 1 || count > PN_GEMV_GROUP_MAX_PARTS)
+        return PN_ERR_SHAPE;
+    if (!parts)
+        return PN_ERR_NULL;
+    if (M < 0 || M > PN_GEMV_MAX_TOKENS)
+        return PN_ERR_TOKENS;
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &p = parts[i];
+        if (p.type != PN_TYPE_PN3T && p.type != PN_TYPE_PN4T)
+            return PN_ERR_TYPE;
+        if (p.N < 0 || pn_row_bytes(p.type, K) == 0)
+            return PN_ERR_SHAPE;
+    }
+    if (M == 0)
+        return PN_OK;
+    bool any = false;
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &p = parts[i];
+        if (p.N == 0)
+            continue;
+        any = true;
+        if (!p.W || !p.y)
+            return PN_ERR_NULL;
+        if (!aligned(p.W, 2) || !aligned(p.y, 4))
+            return PN_ERR_ALIGN;
+    }
+    if (!any)
+        return PN_OK;
+    if (!x)
+        return PN_ERR_NULL;
+    if (!aligned(x, 4))
+        return PN_ERR_ALIGN;
+    int st = check_device();
+    if (st != PN_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (count > 1 && M <= 2 && !getenv("PN_GEMV_NO_GROUP")) {
+        st = M == 1 ? launch_group<1>(parts, count, K, x, s) : launch_group<2>(parts, count, K, x, s);
+        if (st != kNotApplicable)
+            return st;
+    }
+    // one launch per part (three or more tokens, or a shape the group does not take)
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &p = parts[i];
+        if (p.N == 0)
+            continue;
+        st = p.type == PN_TYPE_PN3T
+                 ? dispatch_m<PN_TYPE_PN3T>((const uint8_t *)p.W, p.N, K, x, M, p.y, s)
+                 : dispatch_m<PN_TYPE_PN4T>((const uint8_t *)p.W, p.N, K, x, M, p.y, s);
         if (st != PN_OK)
             return st;
     }

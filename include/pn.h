@@ -57,6 +57,7 @@ enum {
 /* Maximum tokens per GEMV call. */
 #define PN_MAX_TOKENS 4        /* NVFP4 and row-scaled E4M3 GEMV */
 #define PN_GEMV_MAX_TOKENS 16  /* PN GEMV */
+#define PN_GEMV_GROUP_MAX_PARTS 4  /* matrices per pn_gemv_group call */
 #define PN_GEMV_HADAMARD_MAX_TOKENS 4  /* PN GEMV with the rotation fused */
 
 /* Bytes of one PN row of K weights: 34*K/80 (pn3t) or 34*K/64 (pn4t); 0 if K is not a positive
@@ -110,6 +111,27 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  * call. */
 int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
             void *stream);
+
+/* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up), as pn_gemv of each
+ * part: parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], same accuracy contract and
+ * determinism as pn_gemv. 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part
+ * has its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument
+ * errors as pn_gemv, for the first part that has one; parts with N = 0 are skipped. At 1-2
+ * tokens, where every part's rows hold at most 64 blocks, or longer rows whose x fits the
+ * long-row kernel with 8 float4 of x per thread, one launch serves all parts: the workgroups are
+ * shared among them in proportion to their bytes, so their fixed costs (x staging, the first
+ * weight latency, drain) overlap. Otherwise (or with PN_GEMV_NO_GROUP set) each part is its own
+ * pn_gemv launch. Results may differ from separate pn_gemv calls in the last bits (rows are
+ * summed in a different partition), never beyond the accuracy contract. The parts' y must not
+ * overlap each other or x. */
+typedef struct pn_gemv_part {
+    int type;       /* PN_TYPE_PN3T or PN_TYPE_PN4T */
+    const void *W;  /* N rows of pn_row_bytes(type, K) bytes, 2-byte aligned */
+    int64_t N;      /* rows (outputs per token) */
+    float *y;       /* fp32[M, N], 4-byte aligned */
+} pn_gemv_part;
+int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int64_t M,
+                  void *stream);
 
 /* ---- Hadamard-rotated activations ("PN weight format", "Files that use PN") ----------------
  * The page states that the model rotates the activations that reach the PN weights with a

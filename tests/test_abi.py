@@ -83,5 +83,28 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_gemv_hadamard(7, fake, 4, 640, fake, 1, 64, fake, None) == -1
     assert L.pn_gemv_hadamard(124, fake, 0, 640, fake, 1, 64, fake, None) == 0
     assert L.pn_gemv_hadamard(124, None, 4, 640, fake, 1, 64, fake, None) == -4
+    # several GEMVs that share x
+    Part = pn.GemvPart
+
+    def group(parts, K=640, x=fake, M=1, count=None):
+        arr = (Part * max(len(parts), 1))(*parts)
+        return L.pn_gemv_group(arr if parts else None, len(parts) if count is None else count,
+                               K, x, M, None)
+    ok = Part(124, 0x1000, 4, 0x2000)
+    assert group([ok], count=0) == -2                                  # no parts
+    assert group([ok] * 5) == -2                                       # above the maximum
+    assert group([]) == -2
+    assert L.pn_gemv_group(None, 2, 640, fake, 1, None) == -4           # NULL parts
+    assert group([ok, Part(7, 0x1000, 4, 0x2000)]) == -1               # a bad type
+    assert group([ok, Part(125, 0x1000, 4, 0x2000)], K=560) == -2      # K not whole pn4t blocks
+    assert group([ok, Part(124, 0x1000, -1, 0x2000)]) == -2            # negative N
+    assert group([ok], M=17) == -3
+    assert group([ok], M=0) == 0                                       # M = 0: no-op
+    assert group([Part(124, 0, 0, 0), Part(125, 0, 0, 0)], K=320) == 0  # every N = 0: no-op
+    assert group([ok, Part(124, 0, 4, 0x2000)]) == -4                  # NULL W
+    assert group([ok, Part(124, 0x1001, 4, 0x2000)]) == -5             # W odd address
+    assert group([ok, Part(124, 0x1000, 4, 0x2002)]) == -5             # y not 4-aligned
+    assert group([ok], x=P(0x1002)) == -5                              # x not 4-aligned
+    assert group([ok], x=None) == -4
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert isinstance(pn.status_string(s), str)

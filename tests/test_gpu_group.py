@@ -1,0 +1,109 @@
+"""Several PN GEMVs that share x in one launch (pn_gemv_group) through the C ABI against the CPU
+oracle ("PN weight format", "Value"; each part's sum y = W x itself): every part within
+1e-5 * sum_k |w x| per output, the same bits on every call, the parts' outputs independent of one
+another. The cases reach each body of the group kernel (the register kernel's for rows of at most
+64 blocks, the long-row kernel's for longer rows, both types), tiny and empty parts, x off
+16-byte alignment, and the fallback to one launch per part (three tokens)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_cases import LAYER_SET, PN3T, PN4T, quantized
+from test_gpu_pn import assert_within, dev_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_weight_pn3t_amd as pn
+    return pn, torch, torch.device("cuda:0")
+
+
+def run_group(pn, torch, dev, K, parts, x, x_offset=0):
+    """parts: [(type, W bytes, N)] -> list of y (numpy), one pn_gemv_group call."""
+    M = x.shape[0]
+    buf = torch.zeros(M * K + x_offset, dtype=torch.float32, device=dev)
+    xd = buf[x_offset:x_offset + M * K].view(M, K)
+    xd.copy_(torch.from_numpy(np.ascontiguousarray(x, np.float32)))
+    ys, args = [], []
+    for typ, W, N in parts:
+        yd = torch.full((M, max(N, 1)), float("nan"), dtype=torch.float32, device=dev)
+        Wd = dev_bytes(torch, dev, W) if N else torch.zeros(1, dtype=torch.uint8, device=dev)
+        ys.append(yd)
+        args.append((typ, Wd, N, yd))
+    pn.gemv_group(args, K, xd, M=M)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy()[:, :N] for y, (_, _, N) in zip(ys, parts)]
+
+
+# (K, [(type, N)]): the body each part takes is fixed by K
+CASES = [
+    (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # register pn3t + long-row pn4t (q, k, v)
+    (5120, [(PN3T, 1000), (PN3T, 777)]),                        # two register pn3t parts (gate, up)
+    (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # register bodies of both types, tiny parts
+    (6400, [(PN3T, 140), (PN4T, 301)]),                         # long-row bodies of both types
+    (5120, [(PN3T, 0), (PN4T, 50), (PN3T, 9)]),                 # an empty part
+]
+
+
+def parts_for(K, spec, seed):
+    out = []
+    for j, (typ, N) in enumerate(spec):
+        W = quantized(typ, N, K, seed + 17 * j)[1] if N else np.zeros((0,), np.uint8)
+        out.append((typ, W, N))
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_group_matches_oracle(env, case, M):
+    pn, torch, dev = env
+    K, spec = CASES[case]
+    parts = parts_for(K, spec, 13000 + 100 * case)
+    x = synth.activations(13500 + case + M, M, K)
+    ys = run_group(pn, torch, dev, K, parts, x)
+    again = run_group(pn, torch, dev, K, parts, x)
+    for (typ, W, N), y, y2 in zip(parts, ys, again):
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+        if N:
+            y_ref, bound = oracle.gemv(typ, W, N, K, x)
+            assert_within(y, y_ref, bound)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
+    """x one float off 16-byte alignment gives the bits of aligned x; with the group switched
+    off (one launch per part) every part is still within the bound."""
+    pn, torch, dev = env
+    K, spec = CASES[0]
+    parts = parts_for(K, spec, 13000)
+    x = synth.activations(13600 + M, M, K)
+    a = run_group(pn, torch, dev, K, parts, x)
+    b = run_group(pn, torch, dev, K, parts, x, x_offset=1)
+    for ya, yb in zip(a, b):
+        assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    monkeypatch.setenv("PN_GEMV_NO_GROUP", "1")
+    c = run_group(pn, torch, dev, K, parts, x)
+    for (typ, W, N), y in zip(parts, c):
+        y_ref, bound = oracle.gemv(typ, W, N, K, x)
+        assert_within(y, y_ref, bound)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1, 2])
+def test_group_layer_q_k_v(env, M):
+    """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one launch, every row."""
+    pn, torch, dev = env
+    K = 5120
+    spec = [(typ, N, seed) for N, KK, typ, seed in LAYER_SET if KK == K and N in (6144, 1024)]
+    parts = [(typ, quantized(typ, N, K, seed)[1], N) for typ, N, seed in spec]
+    assert len(parts) == 3
+    x = synth.activations(13700 + M, M, K)
+    for (typ, W, N), y in zip(parts, run_group(pn, torch, dev, K, parts, x)):
+        y_ref, bound = oracle.gemv(typ, W, N, K, x)
+        assert_within(y, y_ref, bound)
