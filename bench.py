@@ -170,61 +170,89 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     del Ws, W0
     log("[bench] extra: pn4t 5120x6144 done")
 
-    # decoder-layer set at M = 1..4, 4 copies (679.6 MB)
+    # decoder-layer set at M = 1..4, 4 copies (679.6 MB). Every layer figure is one layer's launches
+    # issued back to back with copy c of every matrix at layer c, so consecutive layers rotate over
+    # the whole 680 MB, past the 256 MB Infinity Cache. per_matrix_us times each matrix alone over
+    # its own 4 copies, for reference: the small ones then fit the Infinity Cache.
     layer = [("gate", 124, 17408, 5120, 401), ("up", 124, 17408, 5120, 402), ("q", 124, 6144, 5120, 403),
              ("o", 124, 5120, 5120, 404), ("k", 125, 1024, 5120, 405), ("v", 125, 1024, 5120, 406),
              ("p6144", 125, 5120, 6144, 407), ("down", 125, 5120, 17408, 408)]
+    C = 4
     mats = []
     for name, typ, N, K, seed in layer:
         W0 = quantize_pn(pn, torch, dev, typ, synth.gaussian_weights(seed, N, K, 0.02))
-        mats.append((name, typ, N, K, [W0] + [W0.clone() for _ in range(3)]))
+        mats.append((name, typ, N, K, [W0] + [W0.clone() for _ in range(C - 1)]))
     xs = {K: torch.from_numpy(np.ascontiguousarray(synth.activations(409, 4, K))).to(dev)
           for K in (5120, 6144, 17408)}
-    y = torch.empty((4, 17408), dtype=torch.float32, device=dev)
+    xr = {K: torch.empty((4, K), dtype=torch.float32, device=dev) for K in xs}
+    byname = {m[0]: m for m in mats}
+    ys = {m[0]: torch.empty((4, m[2]), dtype=torch.float32, device=dev) for m in mats}
+    set_bytes = sum(m[4][0].numel() for m in mats)
+    order = ["q", "k", "v", "o", "gate", "up", "down", "p6144"]
+    # the matrices that read one input (in the model: q, k, v; o; gate, up; down; the 6144-wide one)
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",), ("p6144",)]
+    garr = {g: [(pn.GemvPart * len(g))(*[pn.GemvPart(byname[n][1], byname[n][4][c].data_ptr(),
+                                                      byname[n][2], ys[n].data_ptr()) for n in g])
+                for c in range(C)] for g in groups if len(g) > 1}
+
+    def plain(n, c, M, xsrc=None):
+        _, typ, N, K, Ws = byname[n]
+        check(pn.gemv_ptr(typ, Ws[c].data_ptr(), N, K, (xs[K] if xsrc is None else xsrc).data_ptr(),
+                          M, ys[n].data_ptr(), sh), "pn_gemv")
+
+    def layer_plain(c, M):
+        for n in order:
+            plain(n, c, M)
+
+    def layer_grouped(c, M):
+        for g in groups:
+            if len(g) == 1:
+                plain(g[0], c, M)
+            else:
+                K = byname[g[0]][3]
+                check(pn.gemv_group_ptr(garr[g][c], K, xs[K].data_ptr(), M, sh), "pn_gemv_group")
+
+    def layer_fused(c, M):
+        for n in order:
+            _, typ, N, K, Ws = byname[n]
+            check(pn.gemv_hadamard_ptr(typ, Ws[c].data_ptr(), N, K, xs[K].data_ptr(), M, 1024,
+                                       ys[n].data_ptr(), sh), "pn_gemv_hadamard")
+
+    def layer_rotate_once(c, M):
+        for g in groups:
+            K = byname[g[0]][3]
+            check(pn.lib().pn_hadamard_rows(xs[K].data_ptr(), M, K, 1024, xr[K].data_ptr(), sh),
+                  "pn_hadamard_rows")
+            if len(g) == 1:
+                plain(g[0], c, M, xr[K])
+            else:
+                check(pn.gemv_group_ptr(garr[g][c], K, xr[K].data_ptr(), M, sh), "pn_gemv_group")
+
+    def layer_entry(fn, M, **kw):
+        us = time_launches(torch, stream, lambda c: fn(c, M), C, reps, warmup)
+        return {"GBs": round(set_bytes / us / 1e3, 1), "us": round(us, 2), **kw}
+
     for M in (1, 2, 3, 4):
-        per, tot_b, tot_us = {}, 0, 0.0
-        for name, typ, N, K, Ws in mats:
-            e = pn_entry(typ, N, K, Ws, M, xs[K], y)
-            per[name] = e
-            tot_b += Ws[0].numel()
-            tot_us += e["us"]
-        out[f"layer_set_M{M}"] = {"GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
-                                   "per_matrix_us": {k: v["us"] for k, v in per.items()}}
+        per = {n: pn_entry(byname[n][1], byname[n][2], byname[n][3], byname[n][4], M,
+                           xs[byname[n][3]], ys[n])["us"] for n in order}
+        out[f"layer_set_M{M}"] = layer_entry(layer_plain, M, per_matrix_us=per)
+        out[f"layer_set_grouped_M{M}"] = layer_entry(layer_grouped, M)
     log("[bench] extra: layer set done")
 
-    # Hadamard-rotated activations (slices of 1024) fused into the GEMV at M = 1..4 (3-4 in one
-    # matrix-core launch where it stages x in one pass, else as two launches of a token pair), on
-    # the same layer set, against the plain launches above; the rotation on its own; and the
-    # layer set with each distinct input rotated once and shared (q, k, v; gate and up; o; down;
-    # the 6144-wide matrix) ahead of plain launches
-    xr = torch.empty((4, 17408), dtype=torch.float32, device=dev)
+    # Hadamard-rotated activations (slices of 1024): every matrix through pn_gemv_hadamard (the
+    # rotation fused into each launch); and each distinct input rotated once with
+    # pn_hadamard_rows and shared by the grouped launches; and the rotation on its own
     for M in (1, 2, 3, 4):
-        per, tot_b, tot_us, tot_plain = {}, 0, 0.0, 0.0
-        for name, typ, N, K, Ws in mats:
-            us = time_launches(torch, stream, lambda c: check(pn.gemv_hadamard_ptr(
-                typ, Ws[c].data_ptr(), N, K, xs[K].data_ptr(), M, 1024, y.data_ptr(), sh),
-                "pn_gemv_hadamard"), len(Ws), reps, warmup)
-            per[name] = round(us, 3)
-            tot_b += Ws[0].numel()
-            tot_us += us
-            tot_plain += out[f"layer_set_M{M}"]["per_matrix_us"][name]
-        out[f"hadamard1024_layer_set_M{M}"] = {
-            "GBs": round(tot_b / tot_us / 1e3, 1), "us": round(tot_us, 2),
-            "plain_us": round(tot_plain, 2), "per_matrix_us": per}
+        out[f"hadamard1024_layer_set_M{M}"] = layer_entry(layer_fused, M)
+        out[f"hadamard1024_layer_set_rotate_once_M{M}"] = layer_entry(layer_rotate_once, M)
     rot = {}
     for M in (1, 2, 3, 4):
         for K in (5120, 6144, 17408):
             rot[M, K] = time_launches(torch, stream, lambda c: check(pn.lib().pn_hadamard_rows(
-                xs[K].data_ptr(), M, K, 1024, xr.data_ptr(), sh), "pn_hadamard_rows"), 1, reps,
+                xs[K].data_ptr(), M, K, 1024, xr[K].data_ptr(), sh), "pn_hadamard_rows"), 1, reps,
                 warmup)
     out["hadamard_rows_1024_us"] = {f"M{M}_K{K}": round(v, 3) for (M, K), v in rot.items()}
-    for M in (1, 2, 3, 4):
-        plain = out[f"layer_set_M{M}"]
-        rot_us = 3 * rot[M, 5120] + rot[M, 6144] + rot[M, 17408]
-        out[f"hadamard1024_layer_set_rotate_once_M{M}"] = {
-            "GBs": round(sum(Ws[0].numel() for *_, Ws in mats) / (plain["us"] + rot_us) / 1e3, 1),
-            "us": round(plain["us"] + rot_us, 2), "rotations_us": round(rot_us, 2)}
-    del mats
+    del mats, garr, ys
     log("[bench] extra: Hadamard done")
 
     # NVFP4 17408 x 5120, clip-search quantized on the GPU, x bf16, M = 1..4, 11 copies

@@ -1242,6 +1242,8 @@ static int ring_depth()
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
                 int cus, hipStream_t s);
 bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K);
+int launch_mfma_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int M,
+                      int cus, hipStream_t s);
 
 template <int TYPE>
 static int dispatch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
@@ -1556,8 +1558,10 @@ extern "C" int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, co
     if (st != PN_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    if (count > 1 && M <= 2 && !getenv("PN_GEMV_NO_GROUP")) {
-        st = M == 1 ? launch_group<1>(parts, count, K, x, s) : launch_group<2>(parts, count, K, x, s);
+    if (count > 1 && M <= 4 && !getenv("PN_GEMV_NO_GROUP")) {
+        st = M == 1   ? launch_group<1>(parts, count, K, x, s)
+             : M == 2 ? launch_group<2>(parts, count, K, x, s)
+                      : launch_mfma_group(parts, count, K, x, (int)M, num_cus(), s);
         if (st != kNotApplicable)
             return st;
     }

@@ -644,12 +644,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // first rotated, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the Hadamard rotation of
 // "Files that use PN", as read in pn_hadamard.h), in registers while the first weight copies are
 // in flight, and written as fp32 to the x area, which the staging then reads.
-template <int TYPE, int TG, int MC, bool ROT = false>
-__global__ void __launch_bounds__(kMfmaThreads)
-pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
-                        const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
-                        int64_t rq, int rr, int Pb, int nph, int xvec4, int hL, float hscale)
-{
+template <int TYPE, int TG, int MC, bool ROT>
+__device__ __forceinline__ void
+mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
+              const float *__restrict__ x, int64_t K, int M, float *__restrict__ y, int64_t rq,
+              int rr, int Pb, int nph, int xvec4, int hL, float hscale, int blk_id){
     constexpr bool SLOT = MC <= 8;
     constexpr int ACC = SLOT ? 2 : 4;       // tokens per lane
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -664,7 +663,7 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
     uint8_t *const xa = lds;
     uint8_t *const ring = lds + Pb * per_block + wave * kLdsRing * kChunkBytes;
 
-    const int64_t wg = blockIdx.x;
+    const int64_t wg = blk_id;
     const int64_t r0 = wg * rq + (wg < rr ? wg : rr);
     const int64_t r1 = r0 + rq + (wg < rr ? 1 : 0);
     const int ntiles = (int)((r1 - r0 + 15) >> 4);
@@ -881,6 +880,15 @@ pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_
         }
     }
 }
+template <int TYPE, int TG, int MC, bool ROT = false>
+__global__ void __launch_bounds__(kMfmaThreads)
+pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
+                        const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
+                        int64_t rq, int rr, int Pb, int nph, int xvec4, int hL, float hscale)
+{
+    mfma_lds_body<TYPE, TG, MC, ROT>(W, N, nb, row_bytes, x, K, M, y, rq, rr, Pb, nph, xvec4, hL,
+                                     hscale, (int)blockIdx.x);
+}
 
 // LDS for the x of a phase and, aliased, the 8 waves' partial sums (8 KB per tile of the group).
 constexpr int kMfmaLds = 160 * 1024 - 1024;
@@ -986,6 +994,120 @@ bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K)
     const int64_t nb = K / (type == PN_TYPE_PN3T ? 80 : 64);
     return aligned(W, 4) && nb % kChunkBlocks == 0 && (N + 16) * nb * kBlockBytes < (int64_t(1) << 31) &&
            !getenv("PN_GEMV_MFMA_DIRECT");
+}
+
+// ---- several GEMVs that share x, 3-4 tokens, in one launch ---------------------------------
+// Part i owns the workgroups [start_i, start_{i+1}) and runs the LDS-staged kernel's body there
+// with its own phases and row split, as its own launch of that many workgroups would. Tiles go in
+// groups of up to 9 (the largest group a launch uses): a workgroup of at most 9 tiles takes them in
+// one group, the same order as its own launch.
+struct MfmaGroupPart {
+    const uint8_t *W;
+    float *y;
+    int64_t N, rq;
+    int nb, type, start, rr, Pb, nph;
+};
+
+struct MfmaGroupArgs {
+    MfmaGroupPart p[4];
+    const float *x;
+    int64_t K;
+    int count, M, xvec4;
+};
+
+__global__ void __launch_bounds__(kMfmaThreads) pn_gemv_mfma_group_kernel(MfmaGroupArgs ga)
+{
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < 4; j++)
+        if (j < ga.count && (int)blockIdx.x >= ga.p[j].start)
+            i = j;
+    const MfmaGroupPart &p = ga.p[i];
+    const int blk = (int)blockIdx.x - p.start;
+    if (p.type == PN_TYPE_PN3T)
+        mfma_lds_body<PN_TYPE_PN3T, kMfmaMaxTG, 4, false>(
+            p.W, p.N, p.nb, (int64_t)p.nb * kBlockBytes, ga.x, ga.K, ga.M, p.y, p.rq, p.rr, p.Pb,
+            p.nph, ga.xvec4, 0, 1.0f, blk);
+    else
+        mfma_lds_body<PN_TYPE_PN4T, kMfmaMaxTG, 4, false>(
+            p.W, p.N, p.nb, (int64_t)p.nb * kBlockBytes, ga.x, ga.K, ga.M, p.y, p.rq, p.rr, p.Pb,
+            p.nph, ga.xvec4, 0, 1.0f, blk);
+}
+
+// Launches the group at M = 3, 4 (parts with N = 0 skipped); returns 1 where a part's weights
+// are not staged through LDS (the caller then launches the parts one by one).
+int launch_mfma_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int M,
+                      int cus, hipStream_t s)
+{
+    if (M < 3 || M > 4 || count > 4)
+        return 1;
+    MfmaGroupArgs ga{};
+    double bytes[4], total = 0.0;
+    int cap[4], n = 0;
+    size_t lds = 0;
+    const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &q = parts[i];
+        if (q.N == 0)
+            continue;
+        if (!mfma_stages_weights(q.type, q.W, q.N, K))
+            return 1;
+        MfmaGroupPart &g = ga.p[n];
+        g.W = (const uint8_t *)q.W;
+        g.y = q.y;
+        g.N = q.N;
+        g.type = q.type;
+        g.nb = (int)(K / (q.type == PN_TYPE_PN3T ? 80 : 64));
+        const int per_block = q.type == PN_TYPE_PN3T ? mfma_block_bytes<PN_TYPE_PN3T>(4)
+                                                      : mfma_block_bytes<PN_TYPE_PN4T>(4);
+        const int pb_max = ((kMfmaLds - ring) / per_block) & ~(kChunkBlocks - 1);
+        g.nph = (g.nb + pb_max - 1) / pb_max;
+        g.Pb = ((g.nb + g.nph - 1) / g.nph + kChunkBlocks - 1) & ~(kChunkBlocks - 1);
+        lds = std::max(lds, std::max<size_t>((size_t)g.Pb * per_block + ring,
+                                             (size_t)kMfmaMaxTG * 8192));
+        bytes[n] = (double)q.N * g.nb * kBlockBytes;
+        total += bytes[n];
+        cap[n] = (int)std::min<int64_t>(cus, (q.N + 15) / 16);
+        n++;
+    }
+    if (n == 0)
+        return PN_OK;
+    int grid[4], used = 0;
+    for (int j = 0; j < n; j++) {
+        grid[j] = std::max(1, std::min(cap[j], (int)(cus * bytes[j] / total)));
+        used += grid[j];
+    }
+    while (used < cus) {
+        int best = -1;
+        double load = 0.0;
+        for (int j = 0; j < n; j++)
+            if (grid[j] < cap[j] && bytes[j] / grid[j] > load) {
+                load = bytes[j] / grid[j];
+                best = j;
+            }
+        if (best < 0)
+            break;
+        grid[best]++;
+        used++;
+    }
+    int start = 0;
+    for (int j = 0; j < n; j++) {
+        MfmaGroupPart &g = ga.p[j];
+        g.start = start;
+        start += grid[j];
+        g.rq = g.N / grid[j];
+        g.rr = (int)(g.N % grid[j]);
+    }
+    ga.count = n;
+    ga.x = x;
+    ga.K = K;
+    ga.M = M;
+    ga.xvec4 = aligned(x, 16) ? 1 : 0;
+    constexpr auto kern = pn_gemv_mfma_group_kernel;
+    if (!lds_limit_once<kern>(kMfmaLds))
+        return PN_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3((unsigned)start), dim3(kMfmaThreads), lds, s, ga);
+    return launch_status();
 }
 
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,

@@ -1,9 +1,10 @@
 """Several PN GEMVs that share x in one launch (pn_gemv_group) through the C ABI against the CPU
 oracle ("PN weight format", "Value"; each part's sum y = W x itself): every part within
 1e-5 * sum_k |w x| per output, the same bits on every call, the parts' outputs independent of one
-another. The cases reach each body of the group kernel (the register kernel's for rows of at most
-64 blocks, the long-row kernel's for longer rows, both types), tiny and empty parts, x off
-16-byte alignment, and the fallback to one launch per part (three tokens)."""
+another. The cases reach each body of the group kernels (at 1-2 tokens the register kernel's for
+rows of at most 64 blocks and the long-row kernel's for longer rows, at 3-4 tokens the
+LDS-staged matrix-core kernel's, both types), tiny and empty parts, x off 16-byte alignment, and
+the fallback to one launch per part (rows the matrix cores cannot stage, at 3-4 tokens)."""
 import numpy as np
 import pytest
 
@@ -45,7 +46,8 @@ def run_group(pn, torch, dev, K, parts, x, x_offset=0):
 CASES = [
     (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # register pn3t + long-row pn4t (q, k, v)
     (5120, [(PN3T, 1000), (PN3T, 777)]),                        # two register pn3t parts (gate, up)
-    (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # register bodies of both types, tiny parts
+    (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # register bodies of both types, tiny
+                                                                # parts; 50 pn4t blocks: separate at 3-4
     (6400, [(PN3T, 140), (PN4T, 301)]),                         # long-row bodies of both types
     (5120, [(PN3T, 0), (PN4T, 50), (PN3T, 9)]),                 # an empty part
 ]
@@ -59,7 +61,7 @@ def parts_for(K, spec, seed):
     return out
 
 
-@pytest.mark.parametrize("M", [1, 2, 3])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_group_matches_oracle(env, case, M):
     pn, torch, dev = env
@@ -75,7 +77,7 @@ def test_group_matches_oracle(env, case, M):
             assert_within(y, y_ref, bound)
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3])
 def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
     """x one float off 16-byte alignment gives the bits of aligned x; with the group switched
     off (one launch per part) every part is still within the bound."""
@@ -95,7 +97,7 @@ def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_group_layer_q_k_v(env, M):
     """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one launch, every row."""
     pn, torch, dev = env
