@@ -1397,7 +1397,7 @@ static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const f
 {
     const int cus = num_cus();
     GroupArgs ga{};
-    int idx[kGroupMax], n = 0;
+    int n = 0;
     size_t lds = 0;
     double bytes[kGroupMax], total = 0.0;
     int cap[kGroupMax];
@@ -1422,7 +1422,7 @@ static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const f
         // least; long-row body: one row pair)
         cap[n] = (int)std::min<int64_t>(cus, kind <= kGroupXreg4 ? (g.N + 3) / 4 : (g.N + 1) / 2);
         lds = std::max(lds, l);
-        idx[n++] = i;
+        n++;
     }
     if (n == 0)
         return PN_OK;
@@ -1457,7 +1457,6 @@ static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const f
         if (g.kind >= kGroupFlat3 && (g.gq + 1) * g.nb >= (int64_t(1) << 30))
             return kNotApplicable;  // the long-row body's (row pair, block) index must fit 30 bits
     }
-    (void)idx;
     ga.count = n;
     ga.x = x;
     ga.K = K;
