@@ -116,12 +116,13 @@ int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64
  * part: parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], same accuracy contract and
  * determinism as pn_gemv. 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part
  * has its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument
- * errors as pn_gemv, for the first part that has one; parts with N = 0 are skipped. At 1-2
- * tokens, where every part's rows hold at most 64 blocks, or longer rows whose x fits the
- * long-row kernel with 8 float4 of x per thread, one launch serves all parts: the workgroups are
- * shared among them in proportion to their bytes, so their fixed costs (x staging, the first
- * weight latency, drain) overlap. Otherwise (or with PN_GEMV_NO_GROUP set) each part is its own
- * pn_gemv launch. Results may differ from separate pn_gemv calls in the last bits (rows are
+ * errors as pn_gemv, for the first part that has one; parts with N = 0 are skipped. One launch
+ * serves all parts where every part qualifies -- at 1-2 tokens, rows of at most 64 blocks, or
+ * longer rows whose x fits the long-row kernel with 8 float4 of x per thread; at 3-4 tokens,
+ * weights the matrix cores stage through LDS (4-byte aligned W, rows of a multiple of 4
+ * blocks) -- with the workgroups shared among the parts in proportion to their bytes, so that
+ * their fixed costs (x staging, the first weight latency, drain) overlap. Otherwise (or with
+ * PN_GEMV_NO_GROUP set) each part is its own pn_gemv launch. Results may differ from separate pn_gemv calls in the last bits (rows are
  * summed in a different partition), never beyond the accuracy contract. The parts' y must not
  * overlap each other or x. */
 typedef struct pn_gemv_part {
