@@ -393,7 +393,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: run with --gpus 1 "
+        print(json.dumps({"error": "this bench measures one GPU only: run with --gpus 1 "
                           "(the GEMV shards by rows, with no new kernels; several GPUs are not measured)"}))
         sys.exit(2)
 

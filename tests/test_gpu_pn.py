@@ -2,8 +2,8 @@
 
 Decode and validation must be bit-exact (NaN outputs compared by class: a NaN or infinite d only
 occurs in invalid rows, whose decode the pages leave open; the IEEE product is the reading). The
-GEMV must satisfy |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output (the tolerance the task states;
-the pages' P4 post reports ~1e-6 agreement for its packed kernel). The quantizer must be bit-exact.
+GEMV must satisfy |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output (the accuracy contract of
+pn_gemv in include/pn.h; the packed-BF16 post reports about 1e-6 agreement for its own kernel). The quantizer must be bit-exact.
 """
 import numpy as np
 import pytest

@@ -3,7 +3,7 @@
 Sources: "Quantisation and profiles", sections "NVFP4" (w = e2m1 * weight_scale[n, k/16] *
 weight_scale_2, 0.5625 B/weight, the MLP byte counts) and "The clip search" (five multipliers);
 NInfer "tensor formats" section 3.3 (E2M1/E4M3FN words, scale validity). The quantizer's base
-scale formulas are this build's reading (the pages give only the multipliers): parity with the
+scale formulas are this library's reading (the pages give only the multipliers): parity with the
 engine's own quantizer is unpinned; what is pinned is validity, the grid, and that the kept
 multiplier is the brute-force minimum of the five.
 """
