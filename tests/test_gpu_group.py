@@ -50,6 +50,8 @@ CASES = [
                                                                 # parts; 50 pn4t blocks: separate at 3-4
     (6400, [(PN3T, 140), (PN4T, 301)]),                         # long-row bodies of both types
     (5120, [(PN3T, 0), (PN4T, 50), (PN3T, 9)]),                 # an empty part
+    (5120, [(PN3T, 200), (PN4T, 64), (PN3T, 17), (PN4T, 300)]),  # four parts, all on the matrix
+                                                                # cores at 3-4 tokens
 ]
 
 
