@@ -12,7 +12,7 @@ import os
 
 __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
            "dequantize_rows", "dequantize_row", "gemv", "gemv_group", "quantize_rows", "hadamard_rows",
-           "gemv_hadamard", "nvfp4_validate_rows",
+           "gemv_hadamard", "gemv_group_hadamard", "nvfp4_validate_rows",
            "nvfp4_dequantize_rows", "gemv_nvfp4", "nvfp4_global_scale", "nvfp4_quantize_rows",
            "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row", "fp8row_quantize_rows",
            "library_path", "status_string", "lib"]
@@ -49,6 +49,7 @@ _SIGS = {
     "pn_dequantize_row": (_I32, [_I32, _P, _I64, _P, _P]),
     "pn_gemv": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _P]),
     "pn_gemv_group": (_I32, [C.POINTER(GemvPart), _I32, _I64, _P, _I64, _P]),
+    "pn_gemv_group_hadamard": (_I32, [C.POINTER(GemvPart), _I32, _I64, _P, _I64, _I64, _P]),
     "pn_quantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
     "pn_hadamard_rows": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "pn_gemv_hadamard": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
@@ -163,6 +164,25 @@ def gemv_group(parts, K, x, M=None, stream=None):
         _dev(y, "y", torch.float32)
         arr[i] = GemvPart(type_, _ptr(W), N, _ptr(y))
     _check(_lib.pn_gemv_group(arr, len(parts), K, _ptr(x), M, _stream(stream)), "pn_gemv_group")
+
+
+def gemv_group_hadamard(parts, K, x, B, M=None, stream=None):
+    """gemv_group over x rotated in slices of B (pn_gemv_group_hadamard); x is not modified."""
+    import torch
+    _dev(x, "x", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    arr = (GemvPart * len(parts))()
+    for i, (type_, W, N, y) in enumerate(parts):
+        _dev(y, "y", torch.float32)
+        arr[i] = GemvPart(type_, _ptr(W), N, _ptr(y))
+    _check(_lib.pn_gemv_group_hadamard(arr, len(parts), K, _ptr(x), M, B, _stream(stream)),
+           "pn_gemv_group_hadamard")
+
+
+def gemv_group_hadamard_ptr(parts, K, x_ptr, M, B, stream_handle):
+    """Raw-pointer form: parts a prepared GemvPart array; returns the status."""
+    return _lib.pn_gemv_group_hadamard(parts, len(parts), K, x_ptr, M, B, stream_handle)
 
 
 def gemv_group_ptr(parts, K, x_ptr, M, stream_handle):

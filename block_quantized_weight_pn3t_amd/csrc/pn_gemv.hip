@@ -1328,10 +1328,12 @@ struct GroupArgs {
     GroupPart p[kGroupMax];
     const float *x;
     int64_t K;
-    int count, x_vec4;
+    int count, x_vec4, hL;
+    float hscale;
 };
 
-template <int M>
+// ROT: every part reads x rotated in slices of 2^hL (the fused staging of the two bodies).
+template <int M, bool ROT>
 __global__ void __launch_bounds__(512) pn_gemv_group_kernel(GroupArgs ga)
 {
     constexpr int D = M == 1 ? 4 : 2;  // the register kernel's ring, as its own launch uses
@@ -1344,20 +1346,22 @@ __global__ void __launch_bounds__(512) pn_gemv_group_kernel(GroupArgs ga)
     const int blk = (int)blockIdx.x - p.start;
     switch (p.kind) {
     case kGroupXreg3:
-        xreg_body<PN_TYPE_PN3T, M, D, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
-                                             ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        xreg_body<PN_TYPE_PN3T, M, D, ROT>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
+                                           ga.x_vec4, p.fnum, ga.hL, ga.hscale, blk);
         break;
     case kGroupXreg4:
-        xreg_body<PN_TYPE_PN4T, M, D, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
-                                             ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        xreg_body<PN_TYPE_PN4T, M, D, ROT>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y, p.sp,
+                                           ga.x_vec4, p.fnum, ga.hL, ga.hscale, blk);
         break;
     case kGroupFlat3:
-        flat_body<PN_TYPE_PN3T, M, 2, 4, 8, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
-                                                   p.gq, p.gr, ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        flat_body<PN_TYPE_PN3T, M, 2, 4, 8, ROT>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
+                                                 p.gq, p.gr, ga.x_vec4, p.fnum, ga.hL, ga.hscale,
+                                                 blk);
         break;
     default:
-        flat_body<PN_TYPE_PN4T, M, 2, 4, 8, false>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
-                                                   p.gq, p.gr, ga.x_vec4, p.fnum, 0, 1.0f, blk);
+        flat_body<PN_TYPE_PN4T, M, 2, 4, 8, ROT>(p.W, p.N, p.nb, p.row_bytes, ga.x, ga.K, p.y,
+                                                 p.gq, p.gr, ga.x_vec4, p.fnum, ga.hL, ga.hscale,
+                                                 blk);
         break;
     }
 }
@@ -1369,14 +1373,14 @@ template <int M> constexpr int group_static_lds()
 }
 
 // The part's kind and its dynamic LDS need, or -1 where neither body takes the shape.
-template <int M>
+template <int M, bool ROT>
 static int group_kind(int type, int64_t N, int64_t K, int grid_max, size_t &lds)
 {
     const int G = type == PN_TYPE_PN3T ? Fmt<PN_TYPE_PN3T>::G : Fmt<PN_TYPE_PN4T>::G;
     const int stride =
         type == PN_TYPE_PN3T ? Fmt<PN_TYPE_PN3T>::LDS_STRIDE : Fmt<PN_TYPE_PN4T>::LDS_STRIDE;
     const int64_t nb = K / G;
-    lds = 0;
+    lds = ROT ? (size_t)M * K * sizeof(float) : 0;  // the register body's rotated x
     if (nb <= 64)
         return type == PN_TYPE_PN3T ? kGroupXreg3 : kGroupXreg4;
     constexpr int V = ((M * 2 + 3) / 4) * 4;
@@ -1384,16 +1388,17 @@ static int group_kind(int type, int64_t N, int64_t K, int grid_max, size_t &lds)
           kFlatWaves * 4 * sizeof(int);
     const int64_t need = (M * nb * (G / 4) + 64 * kFlatWaves - 1) / (64 * kFlatWaves);
     const int64_t NP = (N + 1) / 2;
-    if (need > 8 || lds + group_static_lds<M>() > (size_t)kMaxLds ||
+    const int64_t nq_rot = 4 * ((M * nb * (G / 4) + 256 * kFlatWaves - 1) / (256 * kFlatWaves));
+    if (need > 8 || (ROT && nq_rot > 8) || lds + group_static_lds<M>() > (size_t)kMaxLds ||
         ((NP + grid_max - 1) / grid_max) * nb >= (int64_t(1) << 30))
         return -1;
     return type == PN_TYPE_PN3T ? kGroupFlat3 : kGroupFlat4;
 }
 
 // Launches the group, or returns kNotApplicable where a part's shape is not taken.
-template <int M>
+template <int M, bool ROT = false>
 static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const float *x,
-                        hipStream_t s)
+                        hipStream_t s, int hL = 0, float hscale = 1.0f)
 {
     const int cus = num_cus();
     GroupArgs ga{};
@@ -1405,7 +1410,7 @@ static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const f
         if (parts[i].N == 0)
             continue;
         size_t l = 0;
-        const int kind = group_kind<M>(parts[i].type, parts[i].N, K, cus, l);
+        const int kind = group_kind<M, ROT>(parts[i].type, parts[i].N, K, cus, l);
         if (kind < 0)
             return kNotApplicable;
         GroupPart &g = ga.p[n];
@@ -1461,7 +1466,11 @@ static int launch_group(const pn_gemv_part *parts, int count, int64_t K, const f
     ga.x = x;
     ga.K = K;
     ga.x_vec4 = aligned(x, 16) ? 1 : 0;
-    constexpr auto kern = pn_gemv_group_kernel<M>;
+    ga.hL = hL;
+    ga.hscale = hscale;
+    if (lds + group_static_lds<M>() > (size_t)kMaxLds)
+        return kNotApplicable;
+    constexpr auto kern = pn_gemv_group_kernel<M, ROT>;
     if (!lds_limit_once<kern>(kMaxLds - group_static_lds<M>()))
         return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)start), dim3(512), lds, s, ga);
@@ -1572,6 +1581,66 @@ extern "C" int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, co
         st = p.type == PN_TYPE_PN3T
                  ? dispatch_m<PN_TYPE_PN3T>((const uint8_t *)p.W, p.N, K, x, M, p.y, s)
                  : dispatch_m<PN_TYPE_PN4T>((const uint8_t *)p.W, p.N, K, x, M, p.y, s);
+        if (st != PN_OK)
+            return st;
+    }
+    return PN_OK;
+}
+
+extern "C" int pn_gemv_group_hadamard(const pn_gemv_part *parts, int count, int64_t K,
+                                      const float *x, int64_t M, int64_t B, void *stream)
+{
+    if (count < 1 || count > PN_GEMV_GROUP_MAX_PARTS)
+        return PN_ERR_SHAPE;
+    if (!parts)
+        return PN_ERR_NULL;
+    if (M < 0 || M > PN_GEMV_HADAMARD_MAX_TOKENS)
+        return PN_ERR_TOKENS;
+    for (int i = 0; i < count; i++) {
+        if (parts[i].type != PN_TYPE_PN3T && parts[i].type != PN_TYPE_PN4T)
+            return PN_ERR_TYPE;
+        if (parts[i].N < 0 || pn_row_bytes(parts[i].type, K) == 0)
+            return PN_ERR_SHAPE;
+    }
+    const int L = hadamard_log(B, K);
+    if (L < 0)
+        return PN_ERR_HADAMARD;
+    if (M == 0)
+        return PN_OK;
+    bool any = false;
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &p = parts[i];
+        if (p.N == 0)
+            continue;
+        any = true;
+        if (!p.W || !p.y)
+            return PN_ERR_NULL;
+        if (!aligned(p.W, 2) || !aligned(p.y, 4))
+            return PN_ERR_ALIGN;
+    }
+    if (!any)
+        return PN_OK;
+    if (!x)
+        return PN_ERR_NULL;
+    if (!aligned(x, 4))
+        return PN_ERR_ALIGN;
+    int st = check_device();
+    if (st != PN_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (count > 1 && M <= 2 && !getenv("PN_GEMV_NO_GROUP")) {
+        const float hs = hadamard_scale(L);
+        st = M == 1 ? launch_group<1, true>(parts, count, K, x, s, L, hs)
+                    : launch_group<2, true>(parts, count, K, x, s, L, hs);
+        if (st != kNotApplicable)
+            return st;
+    }
+    // one fused launch per part (three or four tokens, or a shape the group does not take)
+    for (int i = 0; i < count; i++) {
+        const pn_gemv_part &p = parts[i];
+        if (p.N == 0)
+            continue;
+        st = pn_gemv_hadamard(p.type, p.W, p.N, K, x, M, B, p.y, stream);
         if (st != PN_OK)
             return st;
     }

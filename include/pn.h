@@ -169,6 +169,18 @@ int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 
+/* Several GEMVs that share x, over the rotated x: parts[i].y = W_i x' for each part, x' the
+ * rotation above (B as in pn_hadamard_rows), 0 <= M <= 4 (else PN_ERR_TOKENS), parts and errors
+ * as pn_gemv_group. At 1-2 tokens, where every part takes the one- and two-token fused staging
+ * with at most 8 float4 of x per thread (rows of at most 64 blocks; longer rows of up to 4096
+ * float4 of x over the tokens), one launch serves all parts: every workgroup rotates x once for
+ * its part, as the fused call does, and the parts share the grid in proportion to their bytes.
+ * Otherwise (or with PN_GEMV_NO_GROUP set) each part is its own pn_gemv_hadamard call, with that
+ * call's shapes and errors. Accuracy as pn_gemv_hadamard; results may differ from separate calls
+ * in the last bits, never beyond it. */
+int pn_gemv_group_hadamard(const pn_gemv_part *parts, int count, int64_t K, const float *x,
+                           int64_t M, int64_t B, void *stream);
+
 /* ---- PN reference quantizer ("PN weight format", "Reference quantizer") ---------------------
  * Quantizes fp32 w[nrows, K] (row-major) into PN rows W (nrows * pn_row_bytes bytes), one group of
  * 80 or 64 weights per block: 36 candidate scales s = fp16(sigma * m * amax / z),

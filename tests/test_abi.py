@@ -106,5 +106,13 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert group([ok, Part(124, 0x1000, 4, 0x2002)]) == -5             # y not 4-aligned
     assert group([ok], x=P(0x1002)) == -5                              # x not 4-aligned
     assert group([ok], x=None) == -4
+    hg = lambda parts, B=64, M=1, K=640: L.pn_gemv_group_hadamard(
+        (Part * len(parts))(*parts), len(parts), K, fake, M, B, None)
+    assert hg([ok], B=3) == -8                                         # B not a power of two
+    assert hg([ok], B=256) == -8                                       # B does not divide K
+    assert hg([ok], M=5) == -3                                         # above 4 tokens
+    assert hg([ok, Part(7, 0x1000, 4, 0x2000)]) == -1
+    assert hg([ok], M=0) == 0
+    assert L.pn_gemv_group_hadamard(None, 1, 640, fake, 1, 64, None) == -4
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert isinstance(pn.status_string(s), str)

@@ -111,3 +111,47 @@ def test_group_layer_q_k_v(env, M):
     for (typ, W, N), y in zip(parts, run_group(pn, torch, dev, K, parts, x)):
         y_ref, bound = oracle.gemv(typ, W, N, K, x)
         assert_within(y, y_ref, bound)
+
+
+def run_group_hadamard(pn, torch, dev, K, parts, x, B):
+    M = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    x_before = xd.clone()
+    ys, args = [], []
+    for typ, W, N in parts:
+        yd = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+        ys.append(yd)
+        args.append((typ, dev_bytes(torch, dev, W), N, yd))
+    pn.gemv_group_hadamard(args, K, xd, B, M=M)
+    torch.cuda.synchronize()
+    assert torch.equal(xd, x_before), "the call modified x"
+    return [y.cpu().numpy() for y in ys]
+
+
+# (K, B, [(type, N)]): x rotated in slices of B ("Files that use PN"; the reading of pn_hadamard.h)
+ROT_CASES = [
+    (5120, 1024, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),   # register pn3t + long-row pn4t
+    (5120, 256, [(PN3T, 300), (PN3T, 77)]),                  # two register parts
+    (3200, 64, [(PN3T, 333), (PN4T, 65), (PN4T, 7)]),        # register bodies of both types
+    (6400, 256, [(PN3T, 140), (PN4T, 301)]),                 # long-row bodies of both types
+    (17408, 1024, [(PN4T, 37), (PN4T, 20)]),                 # too long for the group: one call each
+]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("case", range(len(ROT_CASES)))
+def test_group_hadamard_matches_oracle(env, case, M):
+    from test_gpu_hadamard import gamma
+    pn, torch, dev = env
+    K, B, spec = ROT_CASES[case]
+    parts = [(typ, quantized(typ, N, K, 14000 + 100 * case + 17 * j)[1], N)
+             for j, (typ, N) in enumerate(spec)]
+    x = synth.activations(14500 + case + M, M, K)
+    ys = run_group_hadamard(pn, torch, dev, K, parts, x, B)
+    again = run_group_hadamard(pn, torch, dev, K, parts, x, B)
+    for (typ, W, N), y, y2 in zip(parts, ys, again):
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+        y_ref, bound, rbound = oracle.gemv_hadamard(typ, W, N, K, x, B)
+        tol = 1e-5 * bound + (1 + 1e-5) * gamma(B) * rbound
+        err = np.abs(y.astype(np.float64) - y_ref)
+        assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
