@@ -218,6 +218,18 @@ def extra_workloads(pn, torch, dev, reps, warmup):
             check(pn.gemv_hadamard_ptr(typ, Ws[c].data_ptr(), N, K, xs[K].data_ptr(), M, 1024,
                                        ys[n].data_ptr(), sh), "pn_gemv_hadamard")
 
+    def layer_fused_grouped(c, M):
+        for g in groups:
+            K = byname[g[0]][3]
+            if len(g) == 1:
+                n = g[0]
+                check(pn.gemv_hadamard_ptr(byname[n][1], byname[n][4][c].data_ptr(), byname[n][2],
+                                           K, xs[K].data_ptr(), M, 1024, ys[n].data_ptr(), sh),
+                      "pn_gemv_hadamard")
+            else:
+                check(pn.gemv_group_hadamard_ptr(garr[g][c], K, xs[K].data_ptr(), M, 1024, sh),
+                      "pn_gemv_group_hadamard")
+
     def layer_rotate_once(c, M):
         for g in groups:
             K = byname[g[0]][3]
@@ -240,10 +252,12 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     log("[bench] extra: layer set done")
 
     # Hadamard-rotated activations (slices of 1024): every matrix through pn_gemv_hadamard (the
-    # rotation fused into each launch); and each distinct input rotated once with
-    # pn_hadamard_rows and shared by the grouped launches; and the rotation on its own
+    # rotation fused into each launch); the matrices that share an input through
+    # pn_gemv_group_hadamard (one launch, the rotation fused); each distinct input rotated once
+    # with pn_hadamard_rows and shared by the grouped launches; and the rotation on its own
     for M in (1, 2, 3, 4):
         out[f"hadamard1024_layer_set_M{M}"] = layer_entry(layer_fused, M)
+        out[f"hadamard1024_layer_set_fused_grouped_M{M}"] = layer_entry(layer_fused_grouped, M)
         out[f"hadamard1024_layer_set_rotate_once_M{M}"] = layer_entry(layer_rotate_once, M)
     rot = {}
     for M in (1, 2, 3, 4):
