@@ -100,13 +100,15 @@ def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-def test_group_layer_q_k_v(env, M):
-    """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one launch, every row."""
+@pytest.mark.parametrize("rows", [(6144, 1024), (17408,)])
+def test_group_layer_q_k_v(env, M, rows):
+    """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one launch, and its gate and
+    up (pn3t 17408x5120 each) in one launch, every row."""
     pn, torch, dev = env
     K = 5120
-    spec = [(typ, N, seed) for N, KK, typ, seed in LAYER_SET if KK == K and N in (6144, 1024)]
+    spec = [(typ, N, seed) for N, KK, typ, seed in LAYER_SET if KK == K and N in rows]
     parts = [(typ, quantized(typ, N, K, seed)[1], N) for typ, N, seed in spec]
-    assert len(parts) == 3
+    assert len(parts) == (3 if rows == (6144, 1024) else 2)
     x = synth.activations(13700 + M, M, K)
     for (typ, W, N), y in zip(parts, run_group(pn, torch, dev, K, parts, x)):
         y_ref, bound = oracle.gemv(typ, W, N, K, x)
