@@ -157,3 +157,20 @@ def test_group_hadamard_matches_oracle(env, case, M):
         tol = 1e-5 * bound + (1 + 1e-5) * gamma(B) * rbound
         err = np.abs(y.astype(np.float64) - y_ref)
         assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_group_hadamard_layer_q_k_v(env, M):
+    """The model's q, k and v over x rotated in slices of 1024, one call, every row."""
+    from test_gpu_hadamard import gamma
+    pn, torch, dev = env
+    K, B = 5120, 1024
+    spec = [(typ, N, seed) for N, KK, typ, seed in LAYER_SET if KK == K and N in (6144, 1024)]
+    parts = [(typ, quantized(typ, N, K, seed)[1], N) for typ, N, seed in spec]
+    x = synth.activations(14800 + M, M, K)
+    for (typ, W, N), y in zip(parts, run_group_hadamard(pn, torch, dev, K, parts, x, B)):
+        y_ref, bound, rbound = oracle.gemv_hadamard(typ, W, N, K, x, B)
+        tol = 1e-5 * bound + (1 + 1e-5) * gamma(B) * rbound
+        err = np.abs(y.astype(np.float64) - y_ref)
+        assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
