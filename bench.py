@@ -376,19 +376,31 @@ def cpu_baseline(seconds: float):
             w = synth.gaussian_weights(wseed, N, K, 0.02)[:n]
             W, _ = oracle.quantize_rows(typ, w, threads=threads)
             samples.append((typ, n, K, W, synth.activations(xseed, 1, K), W.nbytes))
-    total_bytes, reps, t0 = 0, 0, time.perf_counter()
-    while True:
-        for typ, n, K, W, x, nbytes in samples:
-            oracle.gemv(typ, W, n, K, x, threads=threads)
-            total_bytes += nbytes
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+    def rate(nthreads, budget):
+        total_bytes, reps, t0 = 0, 0, time.perf_counter()
+        while True:
+            for typ, n, K, W, x, nbytes in samples:
+                oracle.gemv(typ, W, n, K, x, threads=nthreads)
+                total_bytes += nbytes
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 1000:
+                return total_bytes / el / 1e9, reps, el
+
+    value, reps, el = rate(threads, seconds)
+    one, reps1, el1 = rate(1, max(1.0, seconds / 6))  # the same sample on one thread
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..N/16 of each of gate, up, down (M=1), {reps} passes, {el:.1f} s, "
-                      f"fp64 accumulation, {threads} host threads"}
+                      f"fp64 accumulation, {threads} host threads",
+            "value_one_thread": round(one, 4),
+            "sample_one_thread": f"the same sample, {reps1} passes, {el1:.1f} s, 1 host thread",
+            "host": f"{cpu}; {os.cpu_count()} logical CPUs"}
 
 
 def main():
