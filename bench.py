@@ -37,6 +37,14 @@ MLP = [("gate_up", 124, [(17408, 301), (17408, 302)], 5120, 304),
        ("down", 125, [(5120, 303)], 17408, 305)]
 
 
+def host_threads() -> int:
+    """Host threads for the oracle legs: the CPUs this process may run on."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -269,17 +277,16 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     del mats, garr, ys
     log("[bench] extra: Hadamard done")
 
-    # NVFP4 17408 x 5120, clip-search quantized on the GPU, x bf16, M = 1..4, 11 copies
+    # NVFP4 17408 x 5120, clip-search quantized by the oracle (host threads), x bf16, M = 1..4,
+    # 11 copies
+    import oracle
     N, K = 17408, 5120
-    w = torch.from_numpy(synth.gaussian_weights(501, N, K, 0.02)).to(dev)
-    g = torch.zeros(1, dtype=torch.float32, device=dev)
-    pn.nvfp4_global_scale(w, g)
-    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
-    pn.nvfp4_quantize_rows(w, g, codes, scales)
-    torch.cuda.synchronize()
-    del w
-    gv = float(g.item())
+    w_np = synth.gaussian_weights(501, N, K, 0.02)
+    gv = oracle.nvfp4_global_scale(w_np)
+    c_np, s_np = oracle.nvfp4_quantize_rows(w_np, gv, threads=host_threads())
+    del w_np
+    codes = torch.from_numpy(c_np).to(dev)
+    scales = torch.from_numpy(s_np).to(dev)
     C = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(10)]
     xb = torch.from_numpy(np.ascontiguousarray(synth.activations_bf16(502, 4, K)).view(np.int16)).to(dev)
     nbytes = codes.numel() + scales.numel() + 4
@@ -291,20 +298,17 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     log("[bench] extra: nvfp4 done")
     del C, codes, scales
 
-    # row-scaled E4M3 head, 248,320 x 5,120 (1.27 GB of codes per copy), quantized on the GPU from
-    # seeded N(0, 0.02) weights (every 7th row x20), 2 copies, M = 1..4
+    # row-scaled E4M3 head, 248,320 x 5,120 (1.27 GB of codes per copy): seeded valid E4M3FN words
+    # and positive bf16 multipliers, 2 copies, M = 1..4
     N, K = 248320, 5120
     hc = torch.empty((N, K), dtype=torch.uint8, device=dev)
     hs = torch.empty(N, dtype=torch.int16, device=dev)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(601)
-    for r0 in range(0, N, 8192):
-        n = min(8192, N - r0)
-        w = torch.randn((n, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
-        w[::7] *= 20.0
-        pn.fp8row_quantize_rows(w, hc[r0:r0 + n], hs[r0:r0 + n])
+    for r0 in range(0, N, 16384):
+        n = min(16384, N - r0)
+        c_np, s_np = synth.e4m3_row_words(601 + r0, n, K)
+        hc[r0:r0 + n] = torch.from_numpy(c_np).to(dev)
+        hs[r0:r0 + n] = torch.from_numpy(s_np.view(np.int16)).to(dev)
     torch.cuda.synchronize()
-    del w
     H = [(hc, hs), (hc.clone(), hs.clone())]
     xh = torch.from_numpy(np.ascontiguousarray(synth.activations(602, 4, K))).to(dev)
     yh = torch.empty((4, N), dtype=torch.float32, device=dev)

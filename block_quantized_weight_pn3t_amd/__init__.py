@@ -13,8 +13,7 @@ import os
 __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
            "dequantize_rows", "dequantize_row", "gemv", "gemv_group", "quantize_rows", "hadamard_rows",
            "gemv_hadamard", "gemv_group_hadamard", "nvfp4_validate_rows",
-           "nvfp4_dequantize_rows", "gemv_nvfp4", "nvfp4_global_scale", "nvfp4_quantize_rows",
-           "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row", "fp8row_quantize_rows",
+           "nvfp4_dequantize_rows", "gemv_nvfp4", "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row",
            "library_path", "status_string", "lib"]
 
 PN3T = 124
@@ -56,12 +55,9 @@ _SIGS = {
     "pn_nvfp4_validate_rows": (_I32, [_P, _F, _I64, _I64, _P, _P]),
     "pn_nvfp4_dequantize_rows": (_I32, [_P, _P, _F, _I64, _I64, _P, _P]),
     "pn_gemv_nvfp4": (_I32, [_P, _P, _F, _I64, _I64, _P, _I64, _P, _P]),
-    "pn_nvfp4_global_scale": (_I32, [_P, _I64, _P, _P]),
-    "pn_nvfp4_quantize_rows": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
     "pn_fp8row_validate_rows": (_I32, [_P, _P, _I64, _I64, _P, _P]),
     "pn_fp8row_dequantize_rows": (_I32, [_P, _P, _I64, _I64, _P, _P]),
     "pn_gemv_fp8row": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P]),
-    "pn_fp8row_quantize_rows": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -262,17 +258,6 @@ def gemv_nvfp4_ptr(codes_ptr, scales_ptr, g, N, K, x_ptr, M, y_ptr, stream_handl
     return _lib.pn_gemv_nvfp4(codes_ptr, scales_ptr, g, N, K, x_ptr, M, y_ptr, stream_handle)
 
 
-def nvfp4_global_scale(w, g_out, stream=None):
-    _check(_lib.pn_nvfp4_global_scale(_ptr(w), w.numel(), _ptr(g_out), _stream(stream)),
-           "pn_nvfp4_global_scale")
-
-
-def nvfp4_quantize_rows(w, g_dev, codes, scales, stream=None):
-    N, K = w.shape
-    _check(_lib.pn_nvfp4_quantize_rows(_ptr(w), N, K, _ptr(g_dev), _ptr(codes), _ptr(scales),
-                                       _stream(stream)), "pn_nvfp4_quantize_rows")
-
-
 # ---- row-scaled E4M3FN (FP8_E4M3FN_ROW_BF16S) ----------------------------------------------------
 
 def fp8row_validate_rows(codes, scales, N, K, verdict, stream=None):
@@ -297,7 +282,3 @@ def gemv_fp8row_ptr(codes_ptr, scales_ptr, N, K, x_ptr, M, y_ptr, stream_handle)
     return _lib.pn_gemv_fp8row(codes_ptr, scales_ptr, N, K, x_ptr, M, y_ptr, stream_handle)
 
 
-def fp8row_quantize_rows(w, codes, scales, status=None, stream=None):
-    N, K = w.shape
-    _check(_lib.pn_fp8row_quantize_rows(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(status),
-                                        _stream(stream)), "pn_fp8row_quantize_rows")

@@ -337,123 +337,6 @@ __global__ void __launch_bounds__(512) fp8row_gemv_xreg_kernel(const uint8_t *__
     }
 }
 
-// ---- the FP8-head quantizer: one wave per row --------------------------------------------------
-
-// Double -> bfloat16 word, one rounding to nearest, ties to even (8 significant bits, binary32's
-// exponent range, subnormals down to 2^-133), +-inf past the largest finite value.
-__device__ __forceinline__ uint32_t f64_to_bf16(double v)
-{
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-    const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
-    if (a > 0x7FF0000000000000ull)
-        return 0x7FC0u;
-    if (a == 0x7FF0000000000000ull)
-        return sign | 0x7F80u;
-    const int e = (int)(a >> 52) - 1023;  // double subnormals are far below bfloat16's range
-    if (a == 0 || e < -134)
-        return sign;
-    const uint64_t mant = (a & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-    const int shift = e >= -126 ? 45 : 45 + (-126 - e);  // keep 8 bits, or the 2^-133 quantum
-    uint64_t kept = mant >> shift;
-    const uint64_t rem = mant & ((1ull << shift) - 1), half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (kept & 1)))
-        kept++;
-    if (e < -126)
-        return sign | (uint32_t)kept;  // kept = 128 is the smallest normal, word 0x0080
-    int E = e;
-    if (kept == 256) {
-        kept = 128;
-        E++;
-    }
-    if (E > 127)
-        return sign | 0x7F80u;
-    return sign | (uint32_t)((E + 127) << 7) | (uint32_t)(kept - 128);
-}
-
-__device__ __forceinline__ uint32_t head_code(double q)
-{
-    return (__builtin_signbit(q) ? 0x80u : 0u) | f64_to_e4m3_sat(__builtin_fabs(q));
-}
-
-// Per row: amax; for c = 1.0, 0.95, 0.90 the multiplier word bf16(c * amax / 448) (skipped if zero
-// or not finite), codes the nearest E4M3FN words of w / s (ties to even, saturating at 448, sign
-// kept), squared error of the fp32 decode in double: lane l sums k = l, l + 64, ... in order, then
-// the 64 partials are added in lane order; the smallest error wins, ties keep the earlier
-// multiplier. All-zero rows (or all candidates skipped) are multiplier +0 with codes 0x00;
-// status[row] = 1 and the zero row for a NaN or infinity.
-__global__ void __launch_bounds__(256) fp8row_quantize_kernel(const float *__restrict__ w,
-                                                              int64_t N, int64_t K,
-                                                              uint8_t *__restrict__ codes,
-                                                              uint16_t *__restrict__ scales,
-                                                              int32_t *__restrict__ status)
-{
-    __shared__ double parts[4][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-    if (row >= N)
-        return;  // the whole wave
-    const float *wr = w + row * K;
-    uint8_t *cr = codes + row * K;
-    double amax = 0.0;
-    bool bad = false;
-    for (int64_t k = lane; k < K; k += 64) {
-        const double a = __builtin_fabs((double)wr[k]);
-        if (!__builtin_isfinite(a))
-            bad = true;
-        else
-            amax = a > amax ? a : amax;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const double t = __shfl_xor(amax, o, 64);
-        amax = t > amax ? t : amax;
-    }
-    bad = __any(bad);
-    uint32_t best_sw = 0;
-    bool found = false;
-    if (!bad && amax > 0.0) {
-        const double mult[3] = {1.0, 0.95, 0.90};
-        double best = __builtin_inf();
-        for (int i = 0; i < 3; i++) {
-            const uint32_t sw = f64_to_bf16(mult[i] * amax / 448.0);
-            const double sd = (double)bf16_bits_to_f32(sw);
-            if (sd == 0.0 || !__builtin_isfinite(sd))
-                continue;
-            const float s32 = (float)sd;
-            double part = 0.0;
-            for (int64_t k = lane; k < K; k += 64) {
-                const double q = (double)wr[k] / sd;
-                const float dq = (float)e4m3_f64(head_code(q)) * s32;
-                const double e = (double)wr[k] - (double)dq;
-                part += e * e;
-            }
-            parts[wv][lane] = part;
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            double err = 0.0;
-            for (int l = 0; l < 64; l++)  // every lane adds the partials in lane order
-                err += parts[wv][l];
-            __builtin_amdgcn_wave_barrier();
-            if (err < best) {
-                best = err;
-                best_sw = sw;
-                found = true;
-            }
-        }
-    }
-    if (!found)
-        best_sw = 0;
-    const double sd = (double)bf16_bits_to_f32(best_sw);
-    for (int64_t k = lane; k < K; k += 64)
-        cr[k] = found ? (uint8_t)head_code((double)wr[k] / sd) : (uint8_t)0;
-    if (lane == 0) {
-        scales[row] = (uint16_t)best_sw;
-        if (status)
-            status[row] = bad ? 1 : 0;
-    }
-}
-
 // ---- host ---------------------------------------------------------------------------------------
 
 static int fp8row_common(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K)
@@ -579,21 +462,4 @@ extern "C" int pn_gemv_fp8row(const uint8_t *codes, const uint16_t *scales, int6
     case 3: return launch_fp8row_gemv<3, 12, 4>(codes, scales, N, K, x, y, s);
     default: return launch_fp8row_gemv<4, 16, 4>(codes, scales, N, K, x, y, s);
     }
-}
-
-extern "C" int pn_fp8row_quantize_rows(const float *w, int64_t N, int64_t K, uint8_t *codes,
-                                       uint16_t *scales, int32_t *status, void *stream)
-{
-    int st = fp8row_common(codes, scales, N, K);
-    if (st != PN_OK || N == 0)
-        return st;
-    if (!w)
-        return PN_ERR_NULL;
-    if (!aligned(w, 4) || (status && !aligned(status, 4)))
-        return PN_ERR_ALIGN;
-    if ((st = check_device()) != PN_OK)
-        return st;
-    hipLaunchKernelGGL(fp8row_quantize_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0,
-                       (hipStream_t)stream, w, N, K, codes, scales, status);
-    return launch_status();
 }

@@ -167,114 +167,6 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
         p[i] = v;
 }
 
-// ---- NVFP4 ------------------------------------------------------------------------------------
-
-__device__ __forceinline__ float e2m1_f32(uint32_t c)
-{
-    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-    const uint32_t bits = (e == 0) ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
-    return __builtin_bit_cast(float, bits | ((c & 8u) << 28));
-}
-
-// double -> E2M1 word: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa bit,
-// saturating at 6, sign bit kept for negative inputs
-__device__ __forceinline__ uint32_t f64_to_e2m1_sat(double v)
-{
-    const uint32_t sign = __builtin_signbit(v) ? 8u : 0u;
-    const double a = __builtin_fabs(v);
-    uint32_t c;
-    if (a <= 0.25) c = 0;
-    else if (a < 0.75) c = 1;
-    else if (a <= 1.25) c = 2;
-    else if (a < 1.75) c = 3;
-    else if (a <= 2.5) c = 4;
-    else if (a < 3.5) c = 5;
-    else if (a <= 5.0) c = 6;
-    else c = 7;
-    return sign | c;
-}
-
-__global__ void zero_u32_kernel(uint32_t *p) { *p = 0u; }
-
-__global__ void __launch_bounds__(256) nvfp4_amax_kernel(const float *__restrict__ w, int64_t count,
-                                                         uint32_t *__restrict__ amax_bits)
-{
-    uint32_t local = 0;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t a = __builtin_bit_cast(uint32_t, w[i]) & 0x7FFFFFFFu;  // |w| bits: ordered
-        local = a > local ? a : local;
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t other = (uint32_t)__shfl_xor((int)local, o, 64);
-        local = other > local ? other : local;
-    }
-    if ((threadIdx.x & 63) == 0 && local)
-        atomicMax(amax_bits, local);
-}
-
-// g = fp32(amax / (6 * 448)), 1 for an all-zero tensor, NaN when amax is not finite
-__global__ void nvfp4_global_kernel(float *g)
-{
-    const uint32_t bits = __builtin_bit_cast(uint32_t, *g);
-    float out;
-    if (bits >= 0x7F800000u)
-        out = __builtin_nanf("");
-    else if (bits == 0)
-        out = 1.0f;
-    else
-        out = (float)((double)__builtin_bit_cast(float, bits) / (6.0 * 448.0));
-    *g = out;
-}
-
-__global__ void __launch_bounds__(256) nvfp4_quantize_kernel(const float *__restrict__ w, int64_t N,
-                                                             int64_t K, const float *__restrict__ gp,
-                                                             uint8_t *__restrict__ codes,
-                                                             uint8_t *__restrict__ scales)
-{
-    const int64_t groups = K >> 4;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= N * groups)
-        return;
-    const int64_t row = q / groups, j = q - row * groups;
-    const float *wg = w + row * K + j * 16;
-    const float g = *gp;
-    double amax = 0.0;
-    for (int k = 0; k < 16; k++) {
-        const double a = __builtin_fabs((double)wg[k]);
-        amax = a > amax ? a : amax;
-    }
-    const double mult[5] = {1.00, 0.95, 0.90, 0.85, 0.80};
-    double best = __builtin_inf();
-    uint32_t best_s = 0;
-    uint32_t best_c[16];
-    for (int k = 0; k < 16; k++)
-        best_c[k] = 0;
-    for (int i = 0; i < 5; i++) {
-        const uint32_t sw = f64_to_e4m3_sat(mult[i] * amax / (6.0 * (double)g));
-        const double S = e4m3_f64(sw);
-        double err = 0.0;
-        uint32_t trial[16];
-        for (int k = 0; k < 16; k++) {
-            trial[k] = (S == 0.0) ? 0u : f64_to_e2m1_sat((double)wg[k] / (S * (double)g));
-            const float p = e2m1_f32(trial[k]) * (float)S;
-            const float dq = p * g;
-            const double e = (double)wg[k] - (double)dq;
-            err += e * e;
-        }
-        if (err < best) {
-            best = err;
-            best_s = sw;
-            for (int k = 0; k < 16; k++)
-                best_c[k] = trial[k];
-        }
-    }
-    scales[q] = (uint8_t)best_s;
-    uint8_t *c = codes + row * (K >> 1) + j * 8;
-    for (int k = 0; k < 16; k += 2)
-        c[k >> 1] = (uint8_t)(best_c[k] | (best_c[k + 1] << 4));
-}
-
 }  // namespace pn
 
 using namespace pn;
@@ -313,49 +205,6 @@ int pn_quantize_rows(int type, const float *w, int64_t nrows, int64_t K, void *W
     else
         hipLaunchKernelGGL(pn_quantize_kernel<PN_TYPE_PN4T>, grid, block, 0, s, w, nrows, nb, K,
                            (uint8_t *)W, status);
-    return launch_status();
-}
-
-int pn_nvfp4_global_scale(const float *w, int64_t count, float *g_out, void *stream)
-{
-    if (count < 0)
-        return PN_ERR_SHAPE;
-    if (!g_out || (count > 0 && !w))
-        return PN_ERR_NULL;
-    if (!aligned(g_out, 4) || (w && !aligned(w, 4)))
-        return PN_ERR_ALIGN;
-    int st = check_device();
-    if (st != PN_OK)
-        return st;
-    hipStream_t s = (hipStream_t)stream;
-    uint32_t *bits = reinterpret_cast<uint32_t *>(g_out);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, bits);
-    if (count > 0) {
-        const int64_t blocks = std::min<int64_t>((count + 255) / 256, 2048);
-        hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, count,
-                           bits);
-    }
-    hipLaunchKernelGGL(nvfp4_global_kernel, dim3(1), dim3(1), 0, s, g_out);
-    return launch_status();
-}
-
-int pn_nvfp4_quantize_rows(const float *w, int64_t N, int64_t K, const float *g_dev,
-                           uint8_t *codes, uint8_t *scales, void *stream)
-{
-    if (N < 0 || K <= 0 || K % 16)
-        return PN_ERR_SHAPE;
-    if (N == 0)
-        return PN_OK;
-    if (!w || !g_dev || !codes || !scales)
-        return PN_ERR_NULL;
-    if (!aligned(w, 4) || !aligned(g_dev, 4))
-        return PN_ERR_ALIGN;
-    int st = check_device();
-    if (st != PN_OK)
-        return st;
-    const int64_t total = N * (K / 16);
-    hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       (hipStream_t)stream, w, N, K, g_dev, codes, scales);
     return launch_status();
 }
 

@@ -214,19 +214,6 @@ int pn_nvfp4_dequantize_rows(const uint8_t *codes, const uint8_t *scales, float 
 int pn_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int64_t N, int64_t K,
                   const uint16_t *x_bf16, int64_t M, float *y, void *stream);
 
-/* g_out (one device float) = fp32(amax(|w|) / (6 * 448)) over count fp32 values, 1.0 for an
- * all-zero tensor, NaN if w holds a NaN or infinity. */
-int pn_nvfp4_global_scale(const float *w, int64_t count, float *g_out, void *stream);
-
-/* Clip-search quantizer ("The clip search", uniform channel weights): per group of 16, multipliers
- * 1.00, 0.95, 0.90, 0.85, 0.80 on the scale e4m3(c * amax_group / (6 g)) (nearest, ties to even,
- * saturating at 448), codes the nearest E2M1 word of w / (S g) (ties to even, saturating at 6, sign
- * kept), squared error of the decoded weights in double, ties keep the earlier multiplier.
- * g is read from device memory (g_dev, e.g. written by pn_nvfp4_global_scale). Every step runs in
- * fp64 in the order stated, so these rules fix every output bit. */
-int pn_nvfp4_quantize_rows(const float *w, int64_t N, int64_t K, const float *g_dev,
-                           uint8_t *codes, uint8_t *scales, void *stream);
-
 /* ---- Row-scaled E4M3FN (FP8_E4M3FN_ROW_BF16S) -----------------------------------------------
  * NInfer "tensor formats", section 3.4: codes uint8[N, K] E4M3FN words (section 3.3), row-major;
  * one bfloat16 multiplier word per row, scales uint16[N]; w = binary32(e4m3(c) * bf16(s)).
@@ -249,17 +236,6 @@ int pn_fp8row_dequantize_rows(const uint8_t *codes, const uint16_t *scales, int6
  * Deterministic. */
 int pn_gemv_fp8row(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                    const float *x, int64_t M, float *y, void *stream);
-
-/* FP8-head quantizer, per row of fp32 w[N, K]: for c = 1.0, 0.95, 0.90 the multiplier word
- * bf16(c * amax / 448) (nearest, ties to even; skipped when zero or not finite), codes the
- * nearest E4M3FN words of w / s (ties to the even fraction, saturating at 448, sign kept), the
- * squared error of the fp32 decode in double -- summed as 64 partials over k = l (mod 64) in
- * increasing k, then the partials in increasing l -- smallest error wins, ties keep the earlier
- * multiplier. An all-zero row (or one whose candidates are all skipped) is multiplier +0 with
- * codes 0x00. status (int32[N], optional) = 1 for a row holding a NaN or infinity (written as the
- * zero row). Every step runs in fp64 in the order stated, so these rules fix every output bit. */
-int pn_fp8row_quantize_rows(const float *w, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,
-                            int32_t *status, void *stream);
 
 #ifdef __cplusplus
 }

@@ -719,9 +719,8 @@ void or_fp8row_validate_rows(const uint8_t *codes, const uint16_t *scales, int64
  * row and each multiplier c in 1.0, 0.95, 0.90, the scale word is bf16(c * amax / 448) (skipped when
  * it is zero or not finite); each code is the E4M3FN word nearest to w / s, ties to the even
  * fraction, saturating at 448, sign kept (also when the magnitude rounds to zero); the error is the
- * squared difference between w and the fp32 decode, in double, summed in a fixed order that the
- * pages leave open: 64 partial sums, partial l over k = l, l + 64, l + 128, ... in increasing k,
- * then the partials added in increasing l; the smallest error wins, a tie keeping the earlier
+ * squared difference between w and the fp32 decode, summed in double over k in increasing order
+ * (the plain sum; the pages do not say more); the smallest error wins, a tie keeping the earlier
  * multiplier. An all-zero row, or one whose candidates are
  * all skipped, is scale +0 with codes 0x00. status[n] = 1 when the row holds a NaN or infinity
  * (the row is then written as the zero row). */
@@ -754,16 +753,12 @@ void or_fp8row_quantize_rows(const float *w, int64_t N, int64_t K, uint8_t *code
                 continue;
             float s32 = (float)sd;
             double err = 0.0;
-            for (int l = 0; l < 64; l++) {
-                double part = 0.0;
-                for (int64_t k = l; k < K; k += 64) {
-                    double q = (double)wr[k] / sd;
-                    uint8_t c = (uint8_t)((signbit(q) ? 0x80 : 0) | or_double_to_e4m3_sat(fabs(q)));
-                    float dq = (float)or_e4m3_to_double(c) * s32;
-                    double e = (double)wr[k] - (double)dq;
-                    part += e * e;
-                }
-                err += part;
+            for (int64_t k = 0; k < K; k++) {
+                double q = (double)wr[k] / sd;
+                uint8_t c = (uint8_t)((signbit(q) ? 0x80 : 0) | or_double_to_e4m3_sat(fabs(q)));
+                float dq = (float)or_e4m3_to_double(c) * s32;
+                double e = (double)wr[k] - (double)dq;
+                err += e * e;
             }
             if (err < best) {
                 best = err;

@@ -108,3 +108,17 @@ def random_bytes(seed: int, count: int) -> np.ndarray:
     """Uniform random bytes (for fuzzing block payloads)."""
     words = splitmix64(seed, 0, (count + 7) // 8)
     return words.view(np.uint8)[:count].copy()
+
+
+def e4m3_row_words(seed: int, n: int, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded row-scaled E4M3FN words: codes uint8[n, k] drawn uniformly, with the two NaN words
+    (0x7F, 0xFF) moved to their neighbours 0x7E / 0xFE; one bfloat16 multiplier word per row,
+    positive and normal, exponent field 120..135 (about 2^-7 .. 2^8), random fraction."""
+    codes = random_bytes(seed, n * k).reshape(n, k)
+    nan = (codes & 0x7F) == 0x7F
+    codes[nan] ^= 1
+    h = splitmix64(seed + 1, 0, n)
+    e = (h % np.uint64(16)).astype(np.uint16) + np.uint16(120)
+    f = ((h >> np.uint64(8)) & np.uint64(0x7F)).astype(np.uint16)
+    scales = (e << np.uint16(7)) | f
+    return codes, scales

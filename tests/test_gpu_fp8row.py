@@ -37,31 +37,6 @@ def head_like(N, K, seed):
     return w, codes, scales
 
 
-def special_rows(K):
-    rows = [np.zeros(K), np.where(np.arange(K) == 3, 1e-30, 0.0), np.linspace(-1, 1, K),
-            np.where(np.arange(K) == 5, np.nan, 0.5), np.where(np.arange(K) == 9, -np.inf, 0.5),
-            np.full(K, 3.0e38), np.where(np.arange(K) % 2 == 0, 1.0, -1.0),
-            synth.laplace_outlier_weights(91, 92, 1, K, 0.015, 0.05, 50.0)[0].astype(np.float64),
-            np.full(K, 1e-42), np.where(np.arange(K) == 0, 448.0, 1e-3)]
-    return np.array(rows, dtype=np.float32)
-
-
-@pytest.mark.parametrize("K", [64, 5120, 1000])
-def test_quantizer_bit_exact(env, K):
-    pn, torch, dev = env
-    w = np.concatenate([special_rows(K), head_like(40, K, 300 + K % 7)[0]])
-    N = w.shape[0]
-    codes, scales, status = oracle.fp8row_quantize_rows(w)
-    c = torch.full((N, K), 0xAA, dtype=torch.uint8, device=dev)
-    s = torch.full((N,), -0x5556, dtype=torch.int16, device=dev)  # the word 0xAAAA
-    st = torch.full((N,), -1, dtype=torch.int32, device=dev)
-    pn.fp8row_quantize_rows(up(torch, dev, w), c, s, st)
-    torch.cuda.synchronize()
-    assert np.array_equal(st.cpu().numpy(), status)
-    assert np.array_equal(s.cpu().numpy().view(np.uint16), scales)
-    assert np.array_equal(c.cpu().numpy(), codes)
-
-
 @pytest.mark.parametrize("K,aligned16", [(256, True), (100, False), (5120, True)])
 def test_validate_and_dequantize_bit_exact(env, K, aligned16):
     pn, torch, dev = env
@@ -156,30 +131,24 @@ def test_gemv_one_hot_exact(env):
 
 @pytest.mark.slow
 def test_head_shape_sampled_rows(env):
-    """The head shape, 248,320 x 5,120 (1.27 GB of codes): quantized on the GPU (bit-exact on a
-    sample of rows), GEMV at M = 1..4 against the oracle on every 97th row."""
+    """The head shape, 248,320 x 5,120 (1.27 GB of codes): seeded valid E4M3FN words and bf16
+    multipliers, GEMV at M = 1..4 against the oracle on every 97th row."""
     pn, torch, dev = env
     N, K = 248320, 5120
-    w = torch.empty((N, K), dtype=torch.float32, device=dev)
-    step = 8192
-    for r0 in range(0, N, step):
-        n = min(step, N - r0)
-        blk = synth.normal_f32(5000 + r0, n * K, 0.02).reshape(n, K)
-        blk[::7] *= 20.0
-        w[r0:r0 + n] = up(torch, dev, blk)
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     scales = torch.empty(N, dtype=torch.int16, device=dev)
-    st = torch.empty(N, dtype=torch.int32, device=dev)
-    pn.fp8row_quantize_rows(w, codes, scales, st)
-    torch.cuda.synchronize()
-    assert int(st.abs().sum()) == 0
+    step = 16384
     rows = np.arange(0, N, 97)
-    w_s = w[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    del w
-    c_s = codes[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    s_s = scales.cpu().numpy().view(np.uint16)[rows]
-    c_ref, s_ref, _ = oracle.fp8row_quantize_rows(w_s)
-    assert np.array_equal(s_s, s_ref) and np.array_equal(c_s, c_ref)
+    c_ref = np.empty((len(rows), K), np.uint8)
+    s_ref = np.empty(len(rows), np.uint16)
+    for r0 in range(0, N, step):
+        n = min(step, N - r0)
+        c, sc = synth.e4m3_row_words(5000 + r0, n, K)
+        codes[r0:r0 + n] = up(torch, dev, c)
+        scales[r0:r0 + n] = up(torch, dev, sc.view(np.int16))
+        sel = (rows >= r0) & (rows < r0 + n)
+        c_ref[sel] = c[rows[sel] - r0]
+        s_ref[sel] = sc[rows[sel] - r0]
     x = synth.activations(5001, 4, K)
     xd = up(torch, dev, x)
     y = torch.empty((4, N), dtype=torch.float32, device=dev)

@@ -24,53 +24,12 @@ def up(torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def gpu_quantize(pn, torch, dev, w):
-    N, K = w.shape
-    wd = up(torch, dev, w)
-    g = torch.zeros(1, dtype=torch.float32, device=dev)
-    pn.nvfp4_global_scale(wd, g)
-    codes = torch.zeros((N, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.zeros((N, K // 16), dtype=torch.uint8, device=dev)
-    pn.nvfp4_quantize_rows(wd, g, codes, scales)
-    torch.cuda.synchronize()
-    return float(g.item()), codes.cpu().numpy(), scales.cpu().numpy()
-
-
 def gemv(pn, torch, dev, codes, scales, g, N, K, xb):
     yd = torch.full((xb.shape[0], N), float("nan"), dtype=torch.float32, device=dev)
     pn.gemv_nvfp4(up(torch, dev, codes), up(torch, dev, scales), g, N, K,
                   up(torch, dev, xb.view(np.int16)), yd)
     torch.cuda.synchronize()
     return yd.cpu().numpy()
-
-
-def test_global_scale_and_quantizer_bit_exact(env):
-    pn, torch, dev = env
-    N, K = 64, 512
-    w = synth.gaussian_weights(501, N, K)
-    w[0, :16] = 0.0                               # an all-zero group
-    w[1, :16] = np.linspace(-1e-6, 1e-6, 16)      # scales that round to E4M3 zero/subnormal
-    w[2, 16:32] = 0.25 * np.arange(16) - 2.0      # E2M1 ties
-    w[3, 5] = 0.4                                 # the tensor's amax
-    g_ref = oracle.nvfp4_global_scale(w)
-    c_ref, s_ref = oracle.nvfp4_quantize_rows(w, g_ref)
-    g, c, s = gpu_quantize(pn, torch, dev, w)
-    assert np.float32(g).view(np.uint32) == np.float32(g_ref).view(np.uint32)
-    assert np.array_equal(s, s_ref)
-    assert np.array_equal(c, c_ref)
-
-
-def test_global_scale_special_tensors(env):
-    pn, torch, dev = env
-    for w in (np.zeros((2, 16), np.float32), np.array([[1.0] * 15 + [np.nan]], np.float32),
-              np.array([[-2688.0] + [0.0] * 15], np.float32)):
-        wd = up(torch, dev, w)
-        g = torch.zeros(1, dtype=torch.float32, device=dev)
-        pn.nvfp4_global_scale(wd, g)
-        torch.cuda.synchronize()
-        ref = oracle.nvfp4_global_scale(w)
-        got = float(g.item())
-        assert (np.isnan(got) and np.isnan(ref)) or got == ref
 
 
 def test_validate_and_dequantize_bit_exact(env):

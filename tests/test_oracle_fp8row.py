@@ -76,15 +76,11 @@ def test_fp8row_validity_clauses(desc, codes, scale, valid):
     assert int(oracle.fp8row_validate_rows(c, s, 1, len(codes))[0]) == valid, desc
 
 
-def blocked_sum(e2: np.ndarray) -> float:
-    """The quantizer's summation order: 64 partials over k = l (mod 64) in increasing k, then the
-    partials in increasing l (written out here with plain Python floats)."""
+def plain_sum(e2: np.ndarray) -> float:
+    """The quantizer's error sum: double, over k in increasing order (plain Python floats)."""
     total = 0.0
-    for l in range(64):
-        part = 0.0
-        for v in e2[l::64]:
-            part += float(v)
-        total += part
+    for v in e2:
+        total += float(v)
     return total
 
 
@@ -116,11 +112,11 @@ def test_fp8row_quantizer_invariants_and_rescan(dist):
             mag = oracle.double_to_e4m3_sat(np.abs(q))
             c = (mag | np.where(np.signbit(q), 0x80, 0)).astype(np.uint8)
             d = _decode(c[None, :], np.array([sw], np.uint16), 1, K)[0]
-            errs.append(blocked_sum((wd[n] - d) ** 2))
+            errs.append(plain_sum((wd[n] - d) ** 2))
         chosen = cands.index(int(scales[n]))
         assert errs[chosen] == min(errs)
         assert all(errs[i] > errs[chosen] for i in range(chosen))  # ties keep the earlier one
-        assert blocked_sum((wd[n] - deq[n]) ** 2) == errs[chosen]
+        assert plain_sum((wd[n] - deq[n]) ** 2) == errs[chosen]
         # every weight lands within half a code step, or is clipped at 448 * s
         sd = float(oracle.bf16_to_float(int(scales[n])))
         assert np.all(np.abs(deq[n]) <= 448 * sd)

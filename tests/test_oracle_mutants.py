@@ -28,6 +28,13 @@ MUTANTS = {
     "sigma_flipped": ("double sigma = (fabs(mn) > mx) ? 1.0 : -1.0;",
                       "double sigma = (fabs(mn) > mx) ? -1.0 : 1.0;",
                       ["test_oracle_quantizer.py"]),
+    "pn_tie_keeps_the_smaller_m": ("        if (err <= best) {",
+                                   "        if (err < best) {",
+                                   ["test_oracle_quantizer.py"]),
+    "nvfp4_tie_keeps_the_later_multiplier": (
+        "if (err < best) {\n                    best = err;\n                    best_s = sw;",
+        "if (err <= best) {\n                    best = err;\n                    best_s = sw;",
+        ["test_oracle_nvfp4.py"]),
     "multiplier_grid_shifted": ("double m = (50 + 2 * i) / 100.0;",
                                 "double m = (52 + 2 * i) / 100.0;",
                                 ["test_oracle_quantizer.py"]),

@@ -118,3 +118,36 @@ def test_quantizer_invariants_and_bruteforce(orc):
             first = int(np.argmin(errs))
             sw = int(orc.double_to_e4m3_sat([mults[first] * amax / (6.0 * g)])[0])
             assert scales[n, j] == sw
+
+
+def test_clip_search_tie_keeps_the_earlier_multiplier(orc):
+    """"The clip search": of two multipliers with exactly equal error the earlier (larger) one is
+    kept (tests/golden/nvfp4_clip_tie.txt, built by hand)."""
+    from fractions import Fraction
+    from conftest import golden_lines
+    rows = golden_lines("nvfp4_clip_tie.txt")
+    g = float(next(r for r in rows if r[0] == "g")[1])
+    w = np.zeros((1, 16), np.float32)
+    for r in rows:
+        if r[0] == "weight":
+            w[0, int(r[1])] = float(r[2])
+    scale = int(next(r for r in rows if r[0] == "scale")[1], 16)
+    other = int(next(r for r in rows if r[0] == "tie_with")[1], 16)
+    c = [int(v) for v in next(r for r in rows if r[0] == "codes")[1:]]
+    codes, scales = orc.nvfp4_quantize_rows(w, g)
+    assert int(scales[0, 0] if scales.ndim == 2 else scales[0]) == scale
+    packed = np.asarray(codes).reshape(-1)
+    assert int(packed[0]) == c[0] | (c[1] << 4) and int(packed[1]) == c[2] | (c[3] << 4)
+    assert not packed[2:].any()
+
+    # the tie is exact: decode both candidates' codes through the oracle and sum in rationals
+    def err(sw):
+        S = orc.e4m3_to_double(sw)
+        tot = Fraction(0)
+        for v in w[0].astype(np.float64):
+            code = int(orc.double_to_e2m1_sat([float(v) / (S * g)])[0])
+            dq = np.float32(np.float32(orc.e2m1_to_double(code)) * np.float32(S)) * np.float32(g)
+            tot += (Fraction(float(v)) - Fraction(float(dq))) ** 2
+        return tot
+
+    assert err(scale) == err(other) == Fraction(13, 64)

@@ -1,7 +1,8 @@
 """Pins for the oracle's PN reference quantizer ("PN weight format", "Reference quantizer").
 
 No printed vectors exist on the pages, so parity with the engine's own quantizer is unpinned.
-What is pinned: the canonical zero group, the sign rule, the candidate grid of the fixture, the
+What is pinned: the tie rule (a group built by hand whose two best candidates tie exactly), the
+canonical zero group, the sign rule, the candidate grid of the fixture, the
 code step (with the tie examples of NInfer "tensor formats" section 7), the [0, 2z-1] clamp,
 and that the kept scale is a brute-force minimum of the error over all 36 candidates (checked
 in exact rational arithmetic, so no rounding order is assumed).
@@ -157,3 +158,42 @@ def test_quantizer_handles_both_signs_of_amax(orc):
         # code; it is code 0 only when the kept m is at most 8/7, so that is not asserted
         k = int(np.argmin(w[0])) if sgn > 0 else int(np.argmax(w[0]))
         assert codes[k] == codes.min()
+
+
+def tie_fixture():
+    """The hand-built tie of tests/golden/pn_quantizer_tie.txt: (w[1, 80], d, codes, tied d)."""
+    rows = golden_lines("pn_quantizer_tie.txt")
+    w = np.zeros((1, 80), np.float32)
+    for r in rows:
+        if r[0] == "weight":
+            w[0, int(r[1])] = float(r[2])
+    d = int(next(r for r in rows if r[0] == "d")[1], 16)
+    other = int(next(r for r in rows if r[0] == "tie_with")[1], 16)
+    c0, c1, rest = (int(v) for v in next(r for r in rows if r[0] == "codes")[1:])
+    codes = np.full(80, rest, np.uint8)
+    codes[0], codes[1] = c0, c1
+    return w, d, codes, other
+
+
+def test_tie_goes_to_the_larger_m(orc):
+    """"Reference quantizer": a tie between candidate scales keeps the larger m."""
+    w, d_exp, codes_exp, other = tie_fixture()
+    W, st = orc.quantize_rows(PN3T, w)
+    d16, codes = orc.unpack_block(PN3T, W[0])
+    assert st[0] == 0
+    assert d16 == d_exp and np.array_equal(codes, codes_exp)
+
+    # the fixture really is a tie, and the minimum: exact rational errors of every candidate
+    def err(s16):
+        s = Fraction(float(orc.f16_to_double([s16])[0]))
+        tot = Fraction(0)
+        for v in w[0].astype(np.float64):
+            n = orc.pn_code(float(v), float(s), 4)
+            tot += (Fraction(float(v)) - s * (n - 4)) ** 2
+        return tot
+
+    assert err(d_exp) == err(other) and other != d_exp
+    ms = multipliers()
+    cands = [int(c) for c in (-np.array(ms) * 1.25 / 4).astype(np.float16).view(np.uint16)]
+    assert cands.index(other) + 1 == cands.index(d_exp)  # 0xB4B3 is m = 0.94, 0xB4CD is m = 0.96
+    assert min(err(c) for c in cands) == err(d_exp)
