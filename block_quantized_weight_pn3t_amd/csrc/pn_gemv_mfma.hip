@@ -996,157 +996,12 @@ bool mfma_stages_weights(int type, const void *W, int64_t N, int64_t K)
            !getenv("PN_GEMV_MFMA_DIRECT");
 }
 
-// ---- several GEMVs that share x, 3-4 tokens, in one launch ---------------------------------
-// Part i owns the workgroups [start_i, start_{i+1}) and runs the LDS-staged kernel's body there
-// with its own phases and row split, as its own launch of that many workgroups would. Tiles go in
-// groups of up to 9 (the largest group a launch uses): a workgroup of at most 9 tiles takes them in
-// one group, the same order as its own launch.
-struct MfmaGroupPart {
-    const uint8_t *W;
-    float *y;
-    int64_t N, rq;
-    int nb, type, start, rr, Pb, nph;
-};
-
-struct MfmaGroupArgs {
-    MfmaGroupPart p[4];
-    const float *x;
-    int64_t K;
-    int count, M, xvec4;
-};
-
-__global__ void __launch_bounds__(kMfmaThreads) pn_gemv_mfma_group_kernel(MfmaGroupArgs ga)
-{
-    int i = 0;
-#pragma unroll
-    for (int j = 1; j < 4; j++)
-        if (j < ga.count && (int)blockIdx.x >= ga.p[j].start)
-            i = j;
-    const MfmaGroupPart &p = ga.p[i];
-    const int blk = (int)blockIdx.x - p.start;
-    if (p.type == PN_TYPE_PN3T)
-        mfma_lds_body<PN_TYPE_PN3T, kMfmaMaxTG, 4, false>(
-            p.W, p.N, p.nb, (int64_t)p.nb * kBlockBytes, ga.x, ga.K, ga.M, p.y, p.rq, p.rr, p.Pb,
-            p.nph, ga.xvec4, 0, 1.0f, blk);
-    else
-        mfma_lds_body<PN_TYPE_PN4T, kMfmaMaxTG, 4, false>(
-            p.W, p.N, p.nb, (int64_t)p.nb * kBlockBytes, ga.x, ga.K, ga.M, p.y, p.rq, p.rr, p.Pb,
-            p.nph, ga.xvec4, 0, 1.0f, blk);
-}
-
-// Launches the group at M = 3, 4 (parts with N = 0 skipped); returns 1 where a part's weights
-// are not staged through LDS (the caller then launches the parts one by one).
-int launch_mfma_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int M,
-                      int cus, hipStream_t s)
-{
-    if (M < 3 || M > 4 || count > 4)
-        return 1;
-    MfmaGroupArgs ga{};
-    double bytes[4], total = 0.0;
-    int cap[4], n = 0;
-    size_t lds = 0;
-    const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
-    for (int i = 0; i < count; i++) {
-        const pn_gemv_part &q = parts[i];
-        if (q.N == 0)
-            continue;
-        if (!mfma_stages_weights(q.type, q.W, q.N, K))
-            return 1;
-        MfmaGroupPart &g = ga.p[n];
-        g.W = (const uint8_t *)q.W;
-        g.y = q.y;
-        g.N = q.N;
-        g.type = q.type;
-        g.nb = (int)(K / (q.type == PN_TYPE_PN3T ? 80 : 64));
-        const int per_block = q.type == PN_TYPE_PN3T ? mfma_block_bytes<PN_TYPE_PN3T>(4)
-                                                      : mfma_block_bytes<PN_TYPE_PN4T>(4);
-        const int pb_max = ((kMfmaLds - ring) / per_block) & ~(kChunkBlocks - 1);
-        g.nph = (g.nb + pb_max - 1) / pb_max;
-        g.Pb = ((g.nb + g.nph - 1) / g.nph + kChunkBlocks - 1) & ~(kChunkBlocks - 1);
-        lds = std::max(lds, std::max<size_t>((size_t)g.Pb * per_block + ring,
-                                             (size_t)kMfmaMaxTG * 8192));
-        bytes[n] = (double)q.N * g.nb * kBlockBytes;
-        total += bytes[n];
-        cap[n] = (int)std::min<int64_t>(cus, (q.N + 15) / 16);
-        n++;
-    }
-    if (n == 0)
-        return PN_OK;
-    int grid[4], used = 0;
-    for (int j = 0; j < n; j++) {
-        grid[j] = std::max(1, std::min(cap[j], (int)(cus * bytes[j] / total)));
-        used += grid[j];
-    }
-    while (used < cus) {
-        int best = -1;
-        double load = 0.0;
-        for (int j = 0; j < n; j++)
-            if (grid[j] < cap[j] && bytes[j] / grid[j] > load) {
-                load = bytes[j] / grid[j];
-                best = j;
-            }
-        if (best < 0)
-            break;
-        grid[best]++;
-        used++;
-    }
-    int start = 0;
-    for (int j = 0; j < n; j++) {
-        MfmaGroupPart &g = ga.p[j];
-        g.start = start;
-        start += grid[j];
-        g.rq = g.N / grid[j];
-        g.rr = (int)(g.N % grid[j]);
-    }
-    ga.count = n;
-    ga.x = x;
-    ga.K = K;
-    ga.M = M;
-    ga.xvec4 = aligned(x, 16) ? 1 : 0;
-    constexpr auto kern = pn_gemv_mfma_group_kernel;
-    if (!lds_limit_once<kern>(kMfmaLds))
-        return PN_ERR_HIP;
-    hipLaunchKernelGGL(kern, dim3((unsigned)start), dim3(kMfmaThreads), lds, s, ga);
-    return launch_status();
-}
-
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
                 int cus, hipStream_t s)
 {
     if (type == PN_TYPE_PN3T)
         return launch_mfma_t<PN_TYPE_PN3T>(W, N, K, x, M, y, cus, s);
     return launch_mfma_t<PN_TYPE_PN4T>(W, N, K, x, M, y, cus, s);
-}
-
-// The GEMV over Hadamard-rotated x at 3-4 tokens in one launch of the weight-staging kernel:
-// W as mfma_stages_weights takes it, slices of at most 1024 elements, and the x of the call
-// staged in one phase and one pass of units (at most 512 blocks over the tokens; every shape
-// within this fits the fp32 x in the x area: M G floats per block <= the block's operands).
-// Same grid and tiles as launch_mfma, so the result has the bits of the rotation followed by
-// pn_gemv. Returns 1 where the shape is not taken (PN_GEMV_HADAMARD_PAIRS: never, for timing).
-template <int TYPE>
-static int launch_mfma_hadamard_t(const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
-                                  float *y, int cus, int hL, float hscale, hipStream_t s)
-{
-    using T = MTile<TYPE>;
-    const int64_t nb = K / T::G;
-    const int ring = kMfmaWaves * kLdsRing * kChunkBytes;
-    const int pb_max = ((kMfmaLds - ring) / mfma_block_bytes<TYPE>(4)) & ~(kChunkBlocks - 1);
-    if (M < 3 || M > 4 || hL > 10 || !mfma_stages_weights(TYPE, W, N, K) || nb > pb_max ||
-        nb * M * 4 > kMfmaThreads * 4 || M * K > 24576 || getenv("PN_GEMV_HADAMARD_PAIRS"))
-        return 1;
-    const int grid = (int)std::min<int64_t>(cus, (N + 15) / 16);
-    const int64_t rq = N / grid;
-    const int rr = (int)(N % grid);
-    return launch_mfma_lds_t<TYPE, 4, true>(W, N, (int)nb, x, K, M, y, grid, rq, rr, s, hL, hscale);
-}
-
-int launch_mfma_hadamard(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M,
-                         float *y, int cus, int hL, float hscale, hipStream_t s)
-{
-    if (type == PN_TYPE_PN3T)
-        return launch_mfma_hadamard_t<PN_TYPE_PN3T>(W, N, K, x, M, y, cus, hL, hscale, s);
-    return launch_mfma_hadamard_t<PN_TYPE_PN4T>(W, N, K, x, M, y, cus, hL, hscale, s);
 }
 
 }  // namespace pn

@@ -87,43 +87,29 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
 /* ---- PN GEMV -------------------------------------------------------------------------------
  * y[m*N + n] = sum_k w[n, k] * x[m*K + k] for m < M (1 <= M <= 16 tokens), with w the decode above,
  * accumulated in fp32. x is fp32[M, K] row-major, y fp32[M, N] row-major (overwritten).
- * Accuracy: |y - y_exact| <= 1e-5 * sum_k |w x| for finite inputs with |x| < 2^100 and
- * sum_k |w x| >= 2^-126 (below that an fp32 y cannot resolve 1e-5 of the sum), under the
- * conditions below, which activations of ordinary dynamic range meet by a wide margin:
- *  - On the vector units the zero point is folded per block, d * (sum n x - z * sum x), with the
- *    unsigned codes n, in fp32 chains of at most 16 terms, so the rounding error scales with a
- *    block's sum n|x| rather than its sum |n - z||x|. It stays inside the bound unless, in the blocks that dominate a
- *    row, sum n|x| exceeds about 8 * sum |n - z||x| (a large x meeting a code next to z).
- *  - pn3t rows of at most 64 blocks at M <= 2 carry each x as an fp16 (hi, lo) pair, exact to
- *    2^-21 relative or to 2^-38 of the largest |x| in its 80-element block, whichever is larger:
- *    every x that meets a nonzero weight must be within 2^20 of the largest |x| of its block.
- *  - On the matrix cores (every shape from 5 tokens; at 3 and 4 tokens when W is 4-byte aligned
- *    and rows hold a multiple of 4 blocks; at 2 tokens when, in addition, rows hold 65 to 128
- *    blocks): the zero point is taken off each code exactly (no fold), and each x is carried as
- *    an fp16 (hi, lo) pair with one exponent per token and group of blocks (4 consecutive
- *    blocks where W is staged through LDS, one block where it is read directly): exact to
- *    2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the largest |x| in its group, whichever
- *    is larger -- every x that meets a nonzero weight must be within about 2^14 of the largest
- *    |x| of its group, or the group's other terms must dominate.
- *    Every other path uses x exactly (scaled by powers of two). Rows are not
+ * Accuracy ("PN weight format", "Value"): |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output, y_ref
+ * the exact sum, for every finite input whose products and partial sums stay in fp32's normal
+ * range. At 1-4 tokens each weight is decoded exactly to the integer n - z, each product with x is
+ * exact inside an fp32 fma, and the only roundings are the fp32 sums: chains of at most 20 terms
+ * per lane and block piece, one multiply by d, a 64-lane tree and the in-order sum of at most 17
+ * chunks per row (about 40 * 2^-24 of sum_k |w x| in the worst case).
+ * At 5-16 tokens (the matrix cores) the zero point is taken off each code exactly as well, but
+ * each x is carried as an fp16 (hi, lo) pair with one exponent per token and group of blocks (4
+ * consecutive blocks where W is staged through LDS, one block where it is read directly): exact to
+ * 2^-22 relative or to 2^-32 (pn3t; 2^-34 pn4t) of the largest |x| in its group, whichever is
+ * larger, so the bound above holds where every x that meets a nonzero weight is within about 2^14
+ * of the largest |x| of its group, or the group's other terms dominate. Rows are not
  * validated here (validate at load); an invalid row gives an unspecified value but no
  * out-of-bounds access. Deterministic: the same inputs and launch give the same bits on every
  * call. */
 int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
             void *stream);
 
-/* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up), as pn_gemv of each
- * part: parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], same accuracy contract and
- * determinism as pn_gemv. 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part
- * has its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument
- * errors as pn_gemv, for the first part that has one; parts with N = 0 are skipped. One launch
- * serves all parts where every part qualifies -- at 1-2 tokens, rows of at most 64 blocks, or
- * longer rows whose x fits the long-row kernel with 8 float4 of x per thread; at 3-4 tokens,
- * weights the matrix cores stage through LDS (4-byte aligned W, rows of a multiple of 4
- * blocks) -- with the workgroups shared among the parts in proportion to their bytes, so that
- * their fixed costs (x staging, the first weight latency, drain) overlap. Otherwise (or with
- * PN_GEMV_NO_GROUP set) each part is its own pn_gemv launch. Results may differ from separate pn_gemv calls in the last bits (rows are
- * summed in a different partition), never beyond the accuracy contract. The parts' y must not
+/* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up): one pn_gemv per part,
+ * in order on the stream, parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], with the bits of
+ * those separate calls. 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part has
+ * its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument errors
+ * as pn_gemv, for the first part that has one; parts with N = 0 are skipped. The parts' y must not
  * overlap each other or x. */
 typedef struct pn_gemv_part {
     int type;       /* PN_TYPE_PN3T or PN_TYPE_PN4T */
@@ -149,35 +135,18 @@ int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, const float *
  * (PN_ERR_SHAPE). out may equal x (in place); otherwise they must not overlap. */
 int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out, void *stream);
 
-/* y = W x' for M = 1..4 tokens: the PN GEMV (pn_gemv) over the rotated x, the rotation fused into
- * the kernels' x staging (each workgroup rotates x in its registers and LDS while its first
- * weight loads are in flight; x itself is not modified). Arguments as pn_gemv, plus B as in
- * pn_hadamard_rows. M outside 0..4 gives PN_ERR_TOKENS.
- * At 3-4 tokens one launch of the matrix-core kernel serves the call where W is 4-byte aligned,
- * rows hold a multiple of 4 blocks (at most 64 for pn3t, 80 for pn4t), B <= 1024 and the
- * offsets fit 31 bits; it gives the same bits, and the same accuracy, as pn_hadamard_rows
- * followed by pn_gemv on the same shape. Otherwise tokens are served two at a
- * time, one launch per pair (W read twice at 3-4 tokens), with the one- and two-token fused
- * staging: rows of at most 64 blocks, and longer rows whose x (2 * K floats for a pair) fits the
- * long-row kernel's LDS area (K up to about 34,000 at one token, 17,000 at two); other shapes
- * give PN_ERR_SHAPE: rotate with pn_hadamard_rows, then call pn_gemv. At 1-2 tokens it gives the
- * same bits as pn_hadamard_rows followed by pn_gemv on the same shape (the same transform, then
- * the same kernel), and pairs the accuracy of the one- and two-token pn_gemv on the rotated x;
- * the rotation's own error above adds to either. Every workgroup rotates the whole x of the
- * call, so where one x feeds several calls (gate and up), rotating it once with pn_hadamard_rows
- * and calling pn_gemv is cheaper. */
+/* y = W x' for M = 1..4 tokens: the rotation of pn_hadamard_rows into a stream-ordered temporary
+ * (hipMallocAsync on the stream, released with hipFreeAsync after the GEMV's launches; x itself is
+ * not modified), then pn_gemv on it: the same bits as those two calls made by hand, the rotation's
+ * error above adding to the GEMV's. Arguments as pn_gemv, plus B as in pn_hadamard_rows; M outside
+ * 0..4 gives PN_ERR_TOKENS, a failed allocation PN_ERR_HIP. */
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 
-/* Several GEMVs that share x, over the rotated x: parts[i].y = W_i x' for each part, x' the
- * rotation above (B as in pn_hadamard_rows), 0 <= M <= 4 (else PN_ERR_TOKENS), parts and errors
- * as pn_gemv_group. At 1-2 tokens, where every part takes the one- and two-token fused staging
- * with at most 8 float4 of x per thread (rows of at most 64 blocks; longer rows of up to 4096
- * float4 of x over the tokens), one launch serves all parts: every workgroup rotates x once for
- * its part, as the fused call does, and the parts share the grid in proportion to their bytes.
- * Otherwise (or with PN_GEMV_NO_GROUP set) each part is its own pn_gemv_hadamard call, with that
- * call's shapes and errors. Accuracy as pn_gemv_hadamard; results may differ from separate calls
- * in the last bits, never beyond it. */
+/* Several GEMVs that share x, over the rotated x: x rotated once into a stream-ordered temporary
+ * (as pn_gemv_hadamard), then pn_gemv_group on it -- parts[i].y = W_i x' with the bits of
+ * pn_hadamard_rows followed by one pn_gemv per part. B as in pn_hadamard_rows, 0 <= M <= 4 (else
+ * PN_ERR_TOKENS), parts and errors as pn_gemv_group. */
 int pn_gemv_group_hadamard(const pn_gemv_part *parts, int count, int64_t K, const float *x,
                            int64_t M, int64_t B, void *stream);
 

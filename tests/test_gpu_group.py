@@ -1,17 +1,15 @@
-"""Several PN GEMVs that share x in one launch (pn_gemv_group) through the C ABI against the CPU
-oracle ("PN weight format", "Value"; each part's sum y = W x itself): every part within
-1e-5 * sum_k |w x| per output, the same bits on every call, the parts' outputs independent of one
-another. The cases reach each body of the group kernels (at 1-2 tokens the register kernel's for
-rows of at most 64 blocks and the long-row kernel's for longer rows, at 3-4 tokens the
-LDS-staged matrix-core kernel's, both types), tiny and empty parts, x off 16-byte alignment, and
-the fallback to one launch per part (rows the matrix cores cannot stage, at 3-4 tokens)."""
+"""Several PN GEMVs that share x (pn_gemv_group) through the C ABI against the CPU oracle ("PN
+weight format", "Value"; each part's sum y = W x itself): every part within 1e-5 * sum_k |w x| per
+output, the same bits on every call and as one pn_gemv call per part, the parts' outputs
+independent of one another. Cases: both types, rows short and long, tiny and empty parts, x off
+16-byte alignment."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from gpu_cases import LAYER_SET, PN3T, PN4T, quantized
-from test_gpu_pn import assert_within, dev_bytes
+from test_gpu_pn import assert_within, dev_bytes, run_gemv
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +78,9 @@ def test_group_matches_oracle(env, case, M):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3])
-def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
-    """x one float off 16-byte alignment gives the bits of aligned x; with the group switched
-    off (one launch per part) every part is still within the bound."""
+def test_group_x_unaligned_and_separate_calls(env, M):
+    """x one float off 16-byte alignment gives the bits of aligned x, and the group gives the bits
+    of one pn_gemv call per part."""
     pn, torch, dev = env
     K, spec = CASES[0]
     parts = parts_for(K, spec, 13000)
@@ -91,19 +89,19 @@ def test_group_x_unaligned_and_ungrouped(env, monkeypatch, M):
     b = run_group(pn, torch, dev, K, parts, x, x_offset=1)
     for ya, yb in zip(a, b):
         assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
-    monkeypatch.setenv("PN_GEMV_NO_GROUP", "1")
-    c = run_group(pn, torch, dev, K, parts, x)
-    for (typ, W, N), y in zip(parts, c):
+    for (typ, W, N), ya in zip(parts, a):
+        y1 = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
+        assert np.array_equal(ya.view(np.uint32), y1.view(np.uint32))
         y_ref, bound = oracle.gemv(typ, W, N, K, x)
-        assert_within(y, y_ref, bound)
+        assert_within(ya, y_ref, bound)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("rows", [(6144, 1024), (17408,)])
 def test_group_layer_q_k_v(env, M, rows):
-    """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one launch, and its gate and
-    up (pn3t 17408x5120 each) in one launch, every row."""
+    """The model's q (pn3t 6144x5120), k and v (pn4t 1024x5120) in one call, and its gate and up
+    (pn3t 17408x5120 each) in one call, every row."""
     pn, torch, dev = env
     K = 5120
     spec = [(typ, N, seed) for N, KK, typ, seed in LAYER_SET if KK == K and N in rows]
@@ -136,7 +134,7 @@ ROT_CASES = [
     (5120, 256, [(PN3T, 300), (PN3T, 77)]),                  # two register parts
     (3200, 64, [(PN3T, 333), (PN4T, 65), (PN4T, 7)]),        # register bodies of both types
     (6400, 256, [(PN3T, 140), (PN4T, 301)]),                 # long-row bodies of both types
-    (17408, 1024, [(PN4T, 37), (PN4T, 20)]),                 # too long for the group: one call each
+    (17408, 1024, [(PN4T, 37), (PN4T, 20)]),                 # long rows, 17 chunks
 ]
 
 

@@ -119,8 +119,8 @@ def gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B, x_offset=0):
     return yd.cpu().numpy()
 
 
-# (type, N, nb, B): rows of at most 64 blocks take the register kernel, longer rows the long-row
-# kernel; B below 256 rotates in registers only, above it through LDS.
+# (type, N, nb, B): slices B below 256 rotate in registers only, larger ones through LDS; rows from
+# 8 to 272 blocks, some not a multiple of 8 (a lane-kernel remainder).
 FUSED = [(PN3T, 300, 64, 1024), (PN3T, 77, 8, 128), (PN3T, 33, 16, 256), (PN4T, 45, 64, 4096),
          (PN4T, 260, 272, 1024), (PN4T, 70, 96, 2048), (PN3T, 41, 80, 256), (PN4T, 19, 130, 64),
          (PN4T, 9, 256, 16384), (PN3T, 25, 8, 4), (PN4T, 31, 130, 8), (PN3T, 13, 64, 512),
@@ -145,40 +145,21 @@ def test_gemv_hadamard_matches_oracle(env, typ, N, nb, B, M):
         assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
 
 
-@pytest.mark.parametrize("typ,N,nb,B", [FUSED[0], FUSED[4], FUSED[3], FUSED[1]])
-@pytest.mark.parametrize("M", [1, 2])
-def test_gemv_hadamard_equals_rotate_then_gemv(env, typ, N, nb, B, M):
-    """The fused staging runs the same transform as the rotation kernel and then the same GEMV
-    kernel: the bits agree with pn_hadamard_rows followed by pn_gemv."""
-    pn, torch, dev = env
-    G = oracle.PARAMS[typ][1]
-    K = nb * G
-    _, W = quantized(typ, N, K, 5600 + nb)
-    Wd = dev_bytes(torch, dev, W)
-    x = synth.activations(5700 + nb + M, M, K)
-    fused = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, B)
-    xr = rotate(pn, torch, dev, x, B)
-    two = run_gemv(pn, torch, dev, typ, Wd, N, K, xr)
-    assert np.array_equal(fused.view(np.uint32), two.view(np.uint32))
+# Shapes for the bit comparison with the two calls: (type, N, nb, B, M). 40000 rows give every CU
+# several rows; pn4t 260 x 272 blocks has 17 chunks of 16 blocks (tail items); 80 blocks a short
+# last chunk; 76 and 130 blocks a remainder past the last multiple of 8 blocks.
+ROT_BITS = [(PN3T, 300, 64, 1024, 1), (PN3T, 300, 64, 1024, 4), (PN4T, 260, 272, 1024, 2),
+            (PN4T, 50, 76, 256, 3), (PN4T, 33, 80, 1024, 4), (PN3T, 25, 8, 4, 3),
+            (PN3T, 40000, 8, 64, 1), (PN4T, 70, 64, 512, 2), (PN3T, 16, 4, 2, 4),
+            (PN4T, 19, 130, 64, 1), (PN3T, 77, 8, 128, 2)]
 
 
-# Three and four tokens in one launch of the matrix-core kernel (W 4-byte aligned, rows of a
-# multiple of 4 blocks, slices of at most 1024, the x of the call staged in one pass): (type, N,
-# nb, B, M). 40000 rows give workgroups two groups of tiles; pn4t with 80 blocks is the longest
-# row it takes (FUSED has longer rows and larger slices, which go by pairs).
-MFMA_ROT = [(PN3T, 300, 64, 1024, 3), (PN3T, 300, 64, 1024, 4), (PN4T, 50, 76, 256, 3),
-            (PN4T, 50, 76, 256, 4), (PN4T, 33, 80, 1024, 4),
-            (PN3T, 25, 8, 4, 3), (PN3T, 25, 8, 4, 4), (PN3T, 40000, 8, 64, 3),
-            (PN3T, 40000, 8, 64, 4), (PN4T, 70, 64, 512, 3), (PN4T, 70, 64, 512, 4),
-            (PN3T, 16, 4, 2, 4)]
-
-
-@pytest.mark.parametrize("typ,N,nb,B,M", MFMA_ROT)
+@pytest.mark.parametrize("typ,N,nb,B,M", ROT_BITS)
 @pytest.mark.parametrize("x_offset", [0, 1])
-def test_gemv_hadamard_mfma_equals_rotate_then_gemv(env, typ, N, nb, B, M, x_offset):
-    """At three and four tokens the single launch stages the rotated x exactly as the matrix-core
-    GEMV stages a given x: its bits equal pn_hadamard_rows followed by pn_gemv, and both are
-    within the oracle's tolerance. x 16-byte aligned or not (offset by one float)."""
+def test_gemv_hadamard_equals_rotate_then_gemv(env, typ, N, nb, B, M, x_offset):
+    """The call rotates x with the rotation kernel and runs the GEMV kernels on the result: its
+    bits equal pn_hadamard_rows followed by pn_gemv, both within the oracle's tolerance. x 16-byte
+    aligned or not (offset by one float)."""
     pn, torch, dev = env
     G = oracle.PARAMS[typ][1]
     K = nb * G
@@ -211,20 +192,17 @@ def test_gemv_hadamard_one_hot_column(env):
         assert np.array_equal(y[0], deq[:, j]), j
 
 
-def test_gemv_hadamard_rejects_rows_it_cannot_stage(env):
+def test_gemv_hadamard_long_rows(env):
+    """Rows of 640 blocks (K = 40960, two slices of K for the GEMV) with x rotated in slices of 1024:
+    the call equals the two calls, bit for bit."""
     pn, torch, dev = env
-    typ, N, K = PN4T, 4, 64 * 640
-    Wd = torch.zeros(N * pn.row_bytes(typ, K), dtype=torch.uint8, device=dev)
-    x = torch.zeros((1, K), dtype=torch.float32, device=dev)
-    y = torch.zeros((1, N), dtype=torch.float32, device=dev)
-    with pytest.raises(pn.PNError):
-        pn.gemv_hadamard(typ, Wd, N, K, x, 1024, y)
-    # the two-call route covers it
-    xr = torch.empty_like(x)
-    pn.hadamard_rows(x, 1024, xr)
-    pn.gemv(typ, Wd, N, K, xr, y)
-    torch.cuda.synchronize()
-    assert torch.all(y == 0)
+    typ, N, K = PN4T, 40, 64 * 640
+    _, W = quantized(typ, N, K, 5990)
+    Wd = dev_bytes(torch, dev, W)
+    x = synth.activations(5991, 2, K)
+    fused = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, x, 1024)
+    two = run_gemv(pn, torch, dev, typ, Wd, N, K, rotate(pn, torch, dev, x, 1024))
+    assert np.array_equal(fused.view(np.uint32), two.view(np.uint32))
 
 
 @pytest.mark.slow

@@ -87,8 +87,6 @@ def test_config5_full_size(env):
     pn, torch, dev = env
     N, K = 17408, 5120
     w, g, codes, scales = nvfp4_quantized(N, K, 501)
-    g2, c2, s2 = gpu_quantize(pn, torch, dev, w)
-    assert g2 == g and np.array_equal(s2, scales) and np.array_equal(c2, codes)
     out = torch.empty((N, K), dtype=torch.float32, device=dev)
     pn.nvfp4_dequantize_rows(up(torch, dev, codes), up(torch, dev, scales), g, N, K, out)
     torch.cuda.synchronize()
