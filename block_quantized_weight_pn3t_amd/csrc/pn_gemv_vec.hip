@@ -50,6 +50,10 @@ constexpr int kThreads = 64 * kWaves;
 // ever holds two of these persistent workgroups while another holds none.
 constexpr int kLdsFloor = 82 * 1024;
 constexpr int kLdsMax = 160 * 1024;
+// Two workgroups per CU (8 waves per SIMD, at most 64 registers): each takes more than a third of
+// the LDS and at most half.
+constexpr int kLdsFloor2 = 54 * 1024;
+constexpr int kLdsMax2 = 80 * 1024;
 
 template <int TYPE> struct Dec;
 template <> struct Dec<PN_TYPE_PN3T> {
@@ -636,13 +640,17 @@ typedef uint32_t u32x5a4 __attribute__((ext_vector_type(5), aligned(4)));
 template <int P>
 __device__ __forceinline__ void read_piece(const uint8_t *sb, const LaneMap &lm, Slot<P> &sl)
 {
-    if constexpr (P == 2) {
+    if constexpr (P == 1) {
+        const u32x2a4 v = *reinterpret_cast<const u32x2a4 *>(sb + lm.main);
+        sl.dw[0] = v[0];
+        sl.ext = (uint16_t)v[1];
+    } else if constexpr (P == 2) {
         const u32x3a4 v = *reinterpret_cast<const u32x3a4 *>(sb + lm.main);
         sl.dw[0] = v[0];
         sl.dw[1] = v[1];
         sl.ext = (uint16_t)v[2];
     } else {
-        static_assert(P == 4, "streaming pieces of 2 or 4 words");
+        static_assert(P == 4, "pieces of 1, 2 or 4 words");
         const u32x4a4 v = *reinterpret_cast<const u32x4a4 *>(sb + lm.main);
         const uint32_t e = *reinterpret_cast<const uint32_t *>(sb + lm.main + 16);
         sl.dw[0] = v[0];
@@ -675,15 +683,18 @@ __device__ __forceinline__ void wait_newer(int newer)
 
 // LDS: partials [Rc_max][NC][M] and 64 dummy slots, the staged x (as above), then per wave a ring
 // of R slots of 272P bytes, then (17-chunk rows) per wave kTailMax tail slots.
-template <int TYPE, int M, int P, int R, int B, bool XLDS>
-__global__ void __launch_bounds__(kThreads) pn_gemv_stream_kernel(Args a)
+// WPE: waves per SIMD the kernel is built for (8: two workgroups per CU, 64 registers).
+template <int TYPE, int M, int P, int R, int B, bool XLDS, int WPE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+pn_gemv_stream_kernel(Args a)
 {
     using D = Dec<TYPE>;
     constexpr int XN = D::CPW * P;
     constexpr int V = B * M;
     constexpr uint32_t L = 272u * P;
     constexpr int I = copy_instrs<P>();
-    constexpr int Q = M <= 2 && R % 2 == 0 && B % 4 == 0 ? 2 : 1;  // items decoded per step
+    // items decoded per step (two in lockstep where the registers allow)
+    constexpr int Q = WPE <= 4 && M <= 2 && R % 2 == 0 && B % 4 == 0 ? 2 : 1;
     static_assert(B % R == 0 && B % (2 * Q) == 0 && R % Q == 0 && V % 4 == 0, "");
     static_assert((R - 1) * I <= 63, "vmcnt range");
     extern __shared__ float lds[];
@@ -967,10 +978,10 @@ int launch_x(const vec::Args &a, bool xlds, int grid, int waves, size_t lds, hip
                 : launch_one<TYPE, M, P, R, false>(a, grid, waves, lds, s);
 }
 
-template <int TYPE, int M, int P, int R, int B, bool XLDS>
+template <int TYPE, int M, int P, int R, int B, bool XLDS, int WPE>
 int launch_stream_one(const vec::Args &a, int grid, int waves, size_t lds, hipStream_t s)
 {
-    constexpr auto kern = vec::pn_gemv_stream_kernel<TYPE, M, P, R, B, XLDS>;
+    constexpr auto kern = vec::pn_gemv_stream_kernel<TYPE, M, P, R, B, XLDS, WPE>;
     if (!lds_limit_once<kern>(vec::kLdsMax))
         return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), lds, s, a);
@@ -980,15 +991,28 @@ int launch_stream_one(const vec::Args &a, int grid, int waves, size_t lds, hipSt
 // Items in flight per wave (a batch of R items times M tokens must be a multiple of 4).
 template <int M> constexpr int ring_items() { return M == 1 ? 8 : M == 2 ? 4 : M == 3 ? 4 : 2; }
 // Streaming kernel: LDS ring slots per wave, and items per reduction batch.
+// Streaming kernel: LDS ring slots per wave, and items per reduction batch. One token on a tall
+// matrix runs two workgroups per CU (8 waves per SIMD, 64 registers, batches of 4 items);
+// otherwise one workgroup of up to 16 waves per CU.
 template <int M> constexpr int stream_ring() { return M == 4 ? 2 : 4; }
-template <int M> constexpr int stream_batch() { return M == 1 ? 8 : M == 4 ? 2 : 4; }
+template <int M, int WPE> constexpr int stream_batch() { return WPE == 8 ? 4 : M == 1 ? 8 : M == 4 ? 2 : 4; }
+
+template <int TYPE, int M, int P, int WPE>
+int launch_stream_w(const vec::Args &a, bool xlds, int grid, int waves, size_t lds, hipStream_t s)
+{
+    constexpr int R = stream_ring<M>(), B = stream_batch<M, WPE>();
+    return xlds ? launch_stream_one<TYPE, M, P, R, B, true, WPE>(a, grid, waves, lds, s)
+                : launch_stream_one<TYPE, M, P, R, B, false, WPE>(a, grid, waves, lds, s);
+}
 
 template <int TYPE, int M, int P>
-int launch_stream_x(const vec::Args &a, bool xlds, int grid, int waves, size_t lds, hipStream_t s)
+int launch_stream_x(const vec::Args &a, bool xlds, bool two, int grid, int waves, size_t lds,
+                    hipStream_t s)
 {
-    constexpr int R = stream_ring<M>(), B = stream_batch<M>();
-    return xlds ? launch_stream_one<TYPE, M, P, R, B, true>(a, grid, waves, lds, s)
-                : launch_stream_one<TYPE, M, P, R, B, false>(a, grid, waves, lds, s);
+    if constexpr (M == 1)
+        if (two)
+            return launch_stream_w<TYPE, M, P, 8>(a, xlds, grid, waves, lds, s);
+    return launch_stream_w<TYPE, M, P, 4>(a, xlds, grid, waves, lds, s);
 }
 
 // One launch group over a slice of K of nb blocks starting at block b0 (rows of rb bytes).
@@ -1003,7 +1027,15 @@ int launch_slice(const uint8_t *W, int64_t N, int64_t rb, int64_t b0, int64_t nb
     // CU (cu, cu + G, ...) at one alignment
     const bool odd_rows = (rb & 2) != 0;
     const int cus = device_cus();
-    const int P = (nb * 8 / 2 + 63) / 64 > vec::kWaves + 1 ? 4 : 2;
+    // workgroups per CU and the LDS each may take
+    const int per_cu = stream && M == 1 && N >= 16 * (int64_t)cus ? 2 : 1;
+    const int64_t lds_max = per_cu == 2 ? vec::kLdsMax2 : vec::kLdsMax;
+    const size_t lds_floor = per_cu == 2 ? vec::kLdsFloor2 : vec::kLdsFloor;
+    // words per lane piece: 1 at 3-4 tokens (their x fills the registers), else 2; 4 where a row
+    // would need more than 17 chunks of 2-word pieces
+    const int P = M >= 3 && (nb + 7) / 8 <= vec::kWaves + 1           ? 1
+                  : (nb * 8 / 2 + 63) / 64 > vec::kWaves + 1 ? 4
+                                                             : 2;
     const int64_t NP = nb * 8 / P, NC = (NP + 63) / 64;
     if (NC > vec::kWaves + 1)
         return PN_ERR_SHAPE;  // the caller slices K so that this does not happen
@@ -1019,23 +1051,23 @@ int launch_slice(const uint8_t *W, int64_t N, int64_t rb, int64_t b0, int64_t nb
     // is staged)
     const size_t xall_bytes = (size_t)M * NC * 64 * XN * sizeof(float);
     // the streaming kernel stages x whenever the partials of its rows still fit beside it
-    const int64_t rows_hint = std::min<int64_t>((N + cus - 1) / cus, 64);
+    const int64_t rows_hint = std::min<int64_t>((N + per_cu * cus - 1) / (per_cu * cus), 64);
     const bool xlds =
         stream ? xall_bytes + ring_bytes + 64 * sizeof(float) +
                          (size_t)(rows_hint * NC * M) * sizeof(float) <=
-                     (size_t)vec::kLdsMax
+                     (size_t)lds_max
                : xall_bytes <= 128 * 1024;
     const size_t x_bytes = xlds ? xall_bytes : tail ? (size_t)M * 64 * XN * sizeof(float) : 0;
     // rows per launch: the partials must fit the LDS beside the staged x, and a wave takes at most
     // kTailMax tail items
-    int64_t rows_per_cu = ((int64_t)vec::kLdsMax - (int64_t)(x_bytes + ring_bytes) -
+    int64_t rows_per_cu = (lds_max - (int64_t)(x_bytes + ring_bytes) -
                            64 * (int64_t)sizeof(float)) /
                           (NC * M * (int64_t)sizeof(float));
     if (tail)
         rows_per_cu = std::min<int64_t>(rows_per_cu, (int64_t)vec::kTailMax * vec::kWaves);
     if (rows_per_cu < 1)
         return PN_ERR_SHAPE;
-    const int grid_cap = odd_rows && cus > 1 && (cus & 1) ? cus - 1 : cus;
+    const int grid_cap = odd_rows && cus > 1 && (cus & 1) ? cus - 1 : per_cu * cus;
     int64_t done = 0;
     while (done < N) {
         // a launch's rows stay under 2 GiB: the kernel addresses them with 32-bit byte offsets
@@ -1060,14 +1092,24 @@ int launch_slice(const uint8_t *W, int64_t N, int64_t rb, int64_t b0, int64_t nb
         a.NC = (int)NC;
         a.Rc_max = (int)((n + grid - 1) / grid);
         const size_t lds =
-            std::max<size_t>((size_t)vec::kLdsFloor,
+            std::max<size_t>(lds_floor,
                              ((size_t)a.Rc_max * NC * M + 64) * sizeof(float) + x_bytes + ring_bytes);
         int st;
+        constexpr int R = ring_items<M>();
+        if constexpr (M >= 3) {
+            if (P == 1) {
+                st = stream ? launch_stream_x<TYPE, M, 1>(a, xlds, false, grid, waves, lds, s)
+                            : launch_x<TYPE, M, 1, R>(a, xlds, grid, waves, lds, s);
+                if (st != PN_OK)
+                    return st;
+                done += n;
+                continue;
+            }
+        }
         if (stream) {
-            st = P == 2 ? launch_stream_x<TYPE, M, 2>(a, xlds, grid, waves, lds, s)
-                        : launch_stream_x<TYPE, M, 4>(a, xlds, grid, waves, lds, s);
+            st = P == 2 ? launch_stream_x<TYPE, M, 2>(a, xlds, per_cu == 2, grid, waves, lds, s)
+                        : launch_stream_x<TYPE, M, 4>(a, xlds, per_cu == 2, grid, waves, lds, s);
         } else {
-            constexpr int R = ring_items<M>();
             st = P == 2 ? launch_x<TYPE, M, 2, R>(a, xlds, grid, waves, lds, s)
                         : launch_x<TYPE, M, 4, R>(a, xlds, grid, waves, lds, s);
         }
@@ -1096,16 +1138,18 @@ int launch_range(const uint8_t *W, int64_t N, int64_t rb, int64_t b0, int64_t nb
 }
 
 // K is cut into slices of at most 17 chunks of 2-word pieces (272 blocks; 544 with 4-word pieces
-// once a row needs them); each slice after the first adds its sums to y, in slice order.
+// once a row needs them; 136 blocks of 1-word pieces at 3-4 tokens); each slice after the first
+// adds its sums to y, in slice order.
 template <int TYPE, int M>
 int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
 {
     using D = vec::Dec<TYPE>;
     const int64_t nb = K / D::G;
     const int64_t rb = nb * kBlockBytes;
-    constexpr int64_t kSliceBlocks = 512;  // 16 chunks of 4-word pieces; a multiple of 8 keeps
-                                           // every slice's alignment that of the row
-    if (nb <= 544)
+    // 16 chunks of 4-word pieces (17 chunks of 1-word pieces at 3-4 tokens); a multiple of 8
+    // keeps every slice's alignment that of the row
+    constexpr int64_t kSliceBlocks = M >= 3 ? 136 : 512;
+    if (nb <= (M >= 3 ? 136 : 544))
         return launch_range<TYPE, M>(W, N, rb, 0, nb, x, K, y, false, s);
     for (int64_t b0 = 0; b0 < nb; b0 += kSliceBlocks) {
         const int st = launch_range<TYPE, M>(W, N, rb, b0, std::min(kSliceBlocks, nb - b0), x, K,
