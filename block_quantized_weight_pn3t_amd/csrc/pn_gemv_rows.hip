@@ -1,0 +1,651 @@
+// pn_gemv_rows.hip -- PN decode-step GEMV y = W.x at 1-4 tokens on the vector units of gfx950.
+//
+// Format: "PN weight format" (PNX-FORMAT-v0): "Block layout" (34-byte blocks: fp16 d, then eight
+// little-endian u32 words; code t of a word at bit BITS*(t>>1) + 16*(t&1), so no code crosses a
+// 16-bit half), "Value" (w = d * (n - z), exact in fp32).
+//
+// Arithmetic (exact decode, x as given in fp32):
+//  * Every 16-bit half of a word holds PAIRS codes at bits BITS*r (r < PAIRS). One and-or keeps
+//    the codes at bit p = BITS*r of both halves of a dword and writes the fp16 exponent of
+//    2^(10-p) over them: each half becomes the fp16 number 2^(10-p) + n, exactly. One packed fp16
+//    add of -(2^(10-p) + z) leaves the integer n - z in each half, exactly (code z gives +0): no
+//    zero-point fold and no cancellation. Positions past the fp16 mantissa are reached after one
+//    shift of the dword (by 9 for pn3t, 8 for pn4t).
+//  * Each weight then takes one v_fma_mix_f32: the fp16 n - z widens exactly and its product with
+//    the fp32 x is exact inside the fma, so the only roundings are fp32 sums: four chains per lane
+//    and item, one multiply by the block's d, a 64-lane tree and the in-order sum over a row's
+//    chunks (and K slices).
+//
+// Reading blocks whose words are not 4-byte aligned. Take a block that starts at a 4-byte aligned
+// address p (its words straddle dwords): the aligned dwords D_i = bytes [p + 4i, p + 4i + 4) hold
+// (d | w0.lo), (w0.hi | w1.lo), ..., (w6.hi | w7.lo), (w7.hi | next block's d). Every half of
+// these still has its codes at bits BITS*r, so each of D_1..D_7 decodes as it stands (low half:
+// the odd codes of word i-1, high half: the even codes of word i), and one v_bfi joins D_0's high
+// half and D_8's low half into a ninth. A block at 2 mod 4 is read from p - 2: D_0 = (previous
+// block's last half | d), D_1..D_8 = its eight aligned words. Either way a lane reads P + 1 aligned
+// dwords and decodes P of them; only the x each half meets differs, and that is fixed per lane.
+//
+// Work split: a lane owns a "piece" of P consecutive words of one block (P = 8, 4 or 2); a wave
+// covers a chunk of 64 pieces (8P blocks) of a row per item and keeps that chunk's x in registers
+// (read from the workgroup's copy of x in LDS when its chunk changes). A workgroup (one per CU,
+// 8 waves) owns a contiguous range of rows; its items (chunk, row) are shared out over its waves
+// in chunk-major order, so a wave's x changes at most a few times. Each lane's words come straight
+// from HBM into registers through buffer loads, D items ahead of the decode. Per item the 64 lane
+// sums are added by DPP and permlane swaps; one lane writes the item's partial to LDS, and at the
+// end the workgroup adds each row's chunk partials in chunk order and writes y. No atomics: the
+// same inputs and launch shape give the same bits.
+#include <algorithm>
+
+#include "pn_common.h"
+
+namespace pn {
+namespace rows {
+
+// Dynamic LDS every launch requests at least: more than half of the CU's 160 KB, so that no CU
+// ever holds two of these workgroups while another holds none.
+constexpr int kLdsFloor = 82 * 1024;
+constexpr int kLdsMax = 160 * 1024;
+// x staged per workgroup at most (the host cuts K into slices beyond this).
+constexpr int kXLdsMax = 128 * 1024;
+
+template <int TYPE> struct Dec;
+template <> struct Dec<PN_TYPE_PN3T> {
+    // NPOS code positions per half are decoded in place (bit BITS*r, r < NPOS), the rest after a
+    // shift of the dword by SHIFT bits
+    static constexpr int BITS = 3, CPW = 10, PAIRS = 5, Z = 4, G = 80, NPOS = 3, SHIFT = 9;
+    // floats a block of x takes in LDS: 20 mod 32 words, so that the 16-byte reads of 8
+    // consecutive lanes (blocks 84 words apart) fall on 8 disjoint groups of 4 banks
+    static constexpr int GS = 84;
+};
+template <> struct Dec<PN_TYPE_PN4T> {
+    static constexpr int BITS = 4, CPW = 8, PAIRS = 4, Z = 8, G = 64, NPOS = 2, SHIFT = 8;
+    static constexpr int GS = 68;  // 4 mod 32 words
+};
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+struct Args {
+    const uint8_t *base;  // 4-byte aligned start of the bytes this launch reads
+    uint32_t nbytes;      // bytes from base the launch may read (a multiple of 4)
+    uint32_t par;         // the first block of row 0 starts at base + par (0 or 2)
+    uint32_t row_stride;  // bytes from one row of the launch to the next (a multiple of 4)
+    int N;                // rows of the launch
+    int nb;               // blocks per row in this slice of K
+    int NC;               // chunks of 8P blocks per row (the last may be partial)
+    int rows_max;         // rows of the workgroup with the most rows
+    const float *x;       // x of this slice: x[m * xstride + k], k < nb * G
+    int64_t xstride;
+    float *y;             // y[m * ystride + n * yinc] for launch row n
+    int64_t ystride;
+    int64_t yinc;
+    int accumulate;       // add to y (later slices of K) instead of overwriting it
+};
+
+// One item's registers: the P + 1 aligned dwords of the lane's piece and (P < 8) the dword that
+// holds the block's d.
+template <int P> struct Slot {
+    uint32_t s[P + 1];
+    uint32_t dw;
+};
+
+template <int P>
+__device__ __forceinline__ void load_slot(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t dvoff,
+                                          uint32_t soff, Slot<P> &sl)
+{
+    if constexpr (P == 8) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u, soff, 0);
+        sl.s[8] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 32u, soff, 0);
+        sl.s[0] = a[0]; sl.s[1] = a[1]; sl.s[2] = a[2]; sl.s[3] = a[3];
+        sl.s[4] = b[0]; sl.s[5] = b[1]; sl.s[6] = b[2]; sl.s[7] = b[3];
+        sl.dw = 0;
+    } else if constexpr (P == 4) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        sl.s[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 16u, soff, 0);
+        sl.dw = __builtin_amdgcn_raw_buffer_load_b32(rs, dvoff, soff, 0);
+        sl.s[0] = a[0]; sl.s[1] = a[1]; sl.s[2] = a[2]; sl.s[3] = a[3];
+    } else {
+        static_assert(P == 2, "pieces of 2, 4 or 8 words");
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+        sl.s[2] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 8u, soff, 0);
+        sl.dw = __builtin_amdgcn_raw_buffer_load_b32(rs, dvoff, soff, 0);
+        sl.s[0] = a[0]; sl.s[1] = a[1];
+    }
+}
+
+// Decode constants kept in registers (the and-or is a VOP3 instruction: no literal operands).
+// Position u (bit p = BITS * u of each half): the code mask in both halves, the fp16 exponent field
+// 25 - p in both halves (the code n becomes the fp16 number 2^(10 - p) + n), and
+// -(2^(10 - p) + z) in both halves.
+template <int TYPE> struct Consts {
+    uint32_t mask[Dec<TYPE>::NPOS];
+    uint32_t magic[Dec<TYPE>::NPOS];
+    h2 bias[Dec<TYPE>::NPOS];
+};
+
+template <int TYPE>
+__device__ __forceinline__ Consts<TYPE> make_consts()
+{
+    using D = Dec<TYPE>;
+    Consts<TYPE> c;
+#pragma unroll
+    for (int u = 0; u < D::NPOS; u++) {
+        const int p = D::BITS * u;
+        uint32_t mk = (((1u << D::BITS) - 1u) << p) * 0x00010001u;
+        uint32_t mg = ((uint32_t)(25 - p) << 10) * 0x00010001u;
+        const _Float16 bz = (_Float16)(-(float)((1 << (10 - p)) + D::Z));
+        uint32_t bb = __builtin_bit_cast(uint32_t, h2{bz, bz});
+        asm volatile("" : "+v"(mk));
+        asm volatile("" : "+v"(mg));
+        asm volatile("" : "+v"(bb));
+        c.mask[u] = mk;
+        c.magic[u] = mg;
+        c.bias[u] = __builtin_bit_cast(h2, bb);
+    }
+    return c;
+}
+
+// Per-lane constants of the piece: offsets of its dwords from a row chunk's start, and how its
+// halves pair with x.
+struct Lane {
+    uint32_t voff;   // the first of the P + 1 dwords
+    uint32_t dvoff;  // the dword holding d (D_0 of the block)
+    uint32_t voffl;  // voff in the last chunk of a row: past every buffer for a lane past the
+    uint32_t dvoffl; // row's end, so that its loads read nothing (dvoff likewise)
+    uint32_t bmask;  // v_bfi mask joining dword 0 and dword P into the last decoded dword
+    uint32_t dsh;    // bit of d in its dword (0 or 16)
+    bool straddle;   // the block starts at 0 mod 4 (its words straddle dwords)
+    int bl;          // block of the piece within a chunk
+    int xoff;        // LDS offset (floats) of the piece's x within a chunk
+};
+
+// x of the piece for one token, in decode order: xs[j][h][r] multiplies the code at pair r of half
+// h of decoded dword j. Words 4-byte aligned (block at 2 mod 4): dword j is word j of the piece,
+// low half = even codes, high half = odd codes. Words at 2 mod 4 (block at 0 mod 4): dword j
+// (j < P-1) holds the odd codes of word j (low half) and the even codes of word j+1 (high half);
+// the joined last dword holds the odd codes of word P-1 and the even codes of word 0. xp: the
+// piece's CPW * P consecutive x values in LDS (16-byte aligned).
+template <int TYPE, int P>
+__device__ __forceinline__ void read_x(const float *xp, bool straddle,
+                                       float (&xs)[P][2][Dec<TYPE>::PAIRS])
+{
+    using D = Dec<TYPE>;
+    constexpr int XN = D::CPW * P;
+    // the aligned order first, read straight into place: x[CPW j + 2r + h] -> xs[j][h][r]
+#pragma unroll
+    for (int i = 0; i < XN; i += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(xp + i);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int e = i + u, j = e / D::CPW, c = e - j * D::CPW;
+            xs[j][c & 1][c >> 1] = f[u];
+        }
+    }
+    // then, where the words straddle dwords, the cyclic shift in place: (e_j, o_j) -> (o_j, e_j+1)
+    float e0[D::PAIRS];
+#pragma unroll
+    for (int r = 0; r < D::PAIRS; r++)
+        e0[r] = xs[0][0][r];
+#pragma unroll
+    for (int j = 0; j < P; j++)
+#pragma unroll
+        for (int r = 0; r < D::PAIRS; r++) {
+            const float o = xs[j][1][r];
+            const float en = j < P - 1 ? xs[j + 1][0][r] : e0[r];
+            xs[j][0][r] = straddle ? o : xs[j][0][r];
+            xs[j][1][r] = straddle ? en : o;
+        }
+}
+
+// One item: out[m] = d * sum over the piece of (n - z) * x[m, k]. Software-pipelined: the codes of
+// dword j + 1 are decoded while dword j's products accumulate, into eight chains per token, so
+// that no instruction waits on the one just before it.
+template <int TYPE, int P>
+__device__ __forceinline__ void decode_dword(uint32_t v, const Consts<TYPE> &c,
+                                             h2 (&n)[Dec<TYPE>::PAIRS])
+{
+    using D = Dec<TYPE>;
+    const uint32_t vs = v >> D::SHIFT;
+#pragma unroll
+    for (int r = 0; r < D::PAIRS; r++) {
+        const int u = r < D::NPOS ? r : r - D::NPOS;
+        const uint32_t src = r < D::NPOS ? v : vs;
+        n[r] = __builtin_bit_cast(h2, (src & c.mask[u]) | c.magic[u]) + c.bias[u];
+    }
+}
+
+template <int TYPE, int M, int P>
+__device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint32_t dwid,
+                                         const float (&xs)[M][P][2][Dec<TYPE>::PAIRS],
+                                         const Consts<TYPE> &c, float (&out)[M])
+{
+    using D = Dec<TYPE>;
+    constexpr int CH = 4;  // chains per token and half
+    float acc[M][CH][2];
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int k = 0; k < CH; k++)
+            acc[m][k][0] = acc[m][k][1] = 0.0f;
+    const uint32_t last = (ln.bmask & sl.s[0]) | (~ln.bmask & sl.s[P]);
+    h2 n[2][D::PAIRS];
+    decode_dword<TYPE, P>(P > 1 ? sl.s[1] : last, c, n[0]);
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        if (j + 1 < P)
+            decode_dword<TYPE, P>(j + 1 < P - 1 ? sl.s[j + 2] : last, c, n[(j + 1) & 1]);
+#pragma unroll
+        for (int r = 0; r < D::PAIRS; r++) {
+            const h2 nn = n[j & 1][r];
+            const float wlo = (float)nn.x, whi = (float)nn.y;
+            const int k = (j * D::PAIRS + r) % CH;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                acc[m][k][0] = __builtin_fmaf(wlo, xs[m][j][0][r], acc[m][k][0]);
+                acc[m][k][1] = __builtin_fmaf(whi, xs[m][j][1][r], acc[m][k][1]);
+            }
+        }
+    }
+    // d of the block; zero width for lanes past the end of the row (their x is zero too)
+    const uint32_t dbits = __builtin_amdgcn_ubfe(P == 8 ? sl.s[0] : sl.dw, ln.dsh, dwid);
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        float t[CH];
+#pragma unroll
+        for (int k = 0; k < CH; k++)
+            t[k] = acc[m][k][0] + acc[m][k][1];
+        out[m] = d * ((t[0] + t[1]) + (t[2] + t[3]));
+    }
+}
+
+typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int TYPE, int M, int P, int DEPTH, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+pn_gemv_rows_kernel(Args a)
+{
+    using D = Dec<TYPE>;
+    constexpr int PPB = 8 / P;   // pieces per block
+    constexpr int CB = 8 * P;    // blocks per chunk
+    constexpr uint32_t CBYTES = 34u * CB;
+    constexpr int LOADS = 3;     // load instructions per item
+    static_assert(DEPTH * LOADS <= 63, "vmcnt range");
+    extern __shared__ float lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = gridDim.x, g = blockIdx.x;
+    const int r0 = (int)((int64_t)a.N * g / G), r1 = (int)((int64_t)a.N * (g + 1) / G);
+    const int nr = r1 - r0;
+    const int NC = a.NC;
+    const int I = NC * nr;  // items of the workgroup, chunk-major
+    const int it0 = (int)((int64_t)I * w / NW), it1 = (int)((int64_t)I * (w + 1) / NW);
+    // x staged per token: whole chunks, each block of x in GS floats (zero past the slice)
+    const int XT = NC * CB * D::GS;
+    float *xl = lds;
+    float *part = lds + M * XT;                    // [rows_max][NC][M]
+    const int dummy = a.rows_max * NC * M;         // then 64 dummy slots
+
+    // ---- lane constants
+    Lane ln;
+    {
+        ln.bl = lane / PPB;
+        const int q = lane - ln.bl * PPB;
+        const uint32_t bstart = a.par + 34u * (uint32_t)ln.bl;
+        const bool straddle = (bstart & 2u) == 0;  // block at 0 mod 4: words straddle dwords
+        const uint32_t s0 = straddle ? bstart : bstart - 2u;
+        ln.voff = s0 + 4u * P * (uint32_t)q;
+        ln.dvoff = s0;
+        ln.bmask = straddle ? 0xFFFF0000u : 0u;
+        ln.dsh = straddle ? 0u : 16u;
+        ln.straddle = straddle;
+        ln.xoff = D::GS * ln.bl + D::CPW * P * q;
+        const bool act_last = (NC - 1) * CB + ln.bl < a.nb;
+        ln.voffl = act_last ? ln.voff : 0x80000000u;
+        ln.dvoffl = act_last ? ln.dvoff : 0x80000000u;
+    }
+    const Consts<TYPE> cst = make_consts<TYPE>();
+    const uint32_t rstride = a.row_stride;
+
+    // ---- the wave's item sequence: its items (chunk-major) cut into one segment per chunk, each
+    // segment padded with empty items to a whole number of groups of DEPTH, so that a group never
+    // spans two chunks and x changes only between groups. Two cursors walk it: one for the loads,
+    // DEPTH items ahead, and one for the decode.
+    struct Cur {
+        int c, r;    // chunk and row (within the workgroup) of the next item
+        int rem;     // items left in the current segment
+        int pad;     // empty items left after it
+        int left;    // items left in the wave's range
+        int pos;     // items taken from the current segment
+    };
+    auto cur_init = [&](Cur &k) {
+        k.left = it1 - it0;
+        k.c = nr > 0 ? it0 / nr : 0;
+        k.r = it0 - k.c * nr;
+        k.rem = min(nr - k.r, k.left);
+        k.pad = 0;
+        k.pos = 0;
+    };
+    // the next segment, once the current one and its padding are used up
+    auto cur_seg = [&](Cur &k) {
+        if (k.rem == 0 && k.pad == 0 && k.left > 0) {
+            k.c++;
+            k.r = 0;
+            k.rem = min(nr, k.left);
+            k.pos = 0;
+        }
+    };
+    // takes one item of the sequence: true (with its chunk and row) for a real one
+    auto cur_step = [&](Cur &k, int &c, int &r) -> bool {
+        cur_seg(k);
+        if (k.rem > 0) {
+            c = k.c;
+            r = k.r;
+            k.r++;
+            k.left--;
+            k.pos++;
+            if (--k.rem == 0)
+                k.pad = (DEPTH - k.pos % DEPTH) % DEPTH;
+            return true;
+        }
+        if (k.pad > 0)
+            k.pad--;
+        return false;
+    };
+
+    // ---- weight loads. Every slot is refilled unconditionally right after its item (a refill
+    // that may or may not happen would make the compiler copy the slot, and the copy would wait
+    // for the load in flight); an empty item's load goes through a buffer of size 0, which reads
+    // no memory.
+    Cur lcur;
+    cur_init(lcur);
+    auto load_next = [&](Slot<P> &sl) {
+        int c = 0, r = 0;
+        const bool real = cur_step(lcur, c, r);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(a.base), (short)0, real ? (int)a.nbytes : 0, 0x00020000);
+        const bool lastc = c == NC - 1;
+        load_slot<P>(rs, lastc ? ln.voffl : ln.voff, lastc ? ln.dvoffl : ln.dvoff,
+                     (uint32_t)(r0 + r) * rstride + CBYTES * (uint32_t)c, sl);
+    };
+    // ---- x staging: the first pass of x loads goes out before the weight loads, so that waiting
+    // for it waits for no weights; further passes (large M * K) wait for everything in flight
+    constexpr int G4 = D::G / 4;       // 16-byte pieces of x per block
+    constexpr int XPT = 8;             // pieces per thread and pass
+    const int nvalid = a.nb * G4;      // pieces per token inside the slice
+    const int ntot = NC * CB * G4;     // pieces per token, whole chunks
+    const int npieces = M * ntot;
+    auto stage_load = [&](int pass, float4 (&v)[XPT]) {
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int f = (pass * XPT + i) * 64 * NW + (int)threadIdx.x;
+            const int m = f / ntot, e = f - m * ntot;
+            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (f < npieces && e < nvalid) {
+                const f32x4a4 t = *reinterpret_cast<const f32x4a4 *>(a.x + (int64_t)m * a.xstride + 4 * e);
+                v[i] = make_float4(t.x, t.y, t.z, t.w);
+            }
+        }
+    };
+    auto stage_store = [&](int pass, const float4 (&v)[XPT]) {
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int f = (pass * XPT + i) * 64 * NW + (int)threadIdx.x;
+            const int m = f / ntot, e = f - m * ntot;
+            const int b = e / G4, c4 = e - b * G4;
+            if (f < npieces)
+                *reinterpret_cast<float4 *>(xl + m * XT + b * D::GS + 4 * c4) = v[i];
+        }
+    };
+    const int npass = (npieces + XPT * 64 * NW - 1) / (XPT * 64 * NW);
+    float4 xv0[XPT];
+    stage_load(0, xv0);
+
+    Slot<P> ring[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; s++)
+        load_next(ring[s]);
+
+    stage_store(0, xv0);
+    for (int pass = 1; pass < npass; pass++) {
+        float4 v[XPT];
+        stage_load(pass, v);
+        stage_store(pass, v);
+    }
+    // a plain barrier: __syncthreads() would also wait for the weight loads in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // ---- items: x of the current chunk in registers, DEPTH items in flight. The partials of a
+    // group of DEPTH items are summed over the wave together (one transposed reduction), and the
+    // first lane of each DPP row stores its share of them.
+    static_assert(DEPTH % 4 == 0, "groups of 4k items");
+    constexpr int V = DEPTH * M;
+    float xs[M][P][2][D::PAIRS];
+    int xc = -1;             // chunk whose x is in xs
+    uint32_t dwid = 16;      // d field width: 0 for lanes past the end of the row
+    const int q = lane >> 4;
+    Cur ccur;
+    cur_init(ccur);
+    for (;;) {
+        cur_seg(ccur);
+        if (ccur.rem == 0)
+            break;
+        if (ccur.c != xc) {
+            xc = ccur.c;
+            dwid = xc * CB + ln.bl < a.nb ? 16u : 0u;
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                read_x<TYPE, P>(xl + m * XT + xc * CB * D::GS + ln.xoff, ln.straddle, xs[m]);
+        }
+        float pv[V];
+        int idx[DEPTH];  // LDS index of each item's first partial, -1 for an empty item
+#pragma unroll
+        for (int s = 0; s < DEPTH; s++) {
+            int c = 0, r = 0;
+            const bool real = cur_step(ccur, c, r);
+            idx[s] = real ? (r * NC + c) * M : -1;
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                pv[s * M + m] = 0.0f;
+            if (real) {  // uniform
+                float o[M];
+                item_mac<TYPE, M, P>(ring[s], ln, dwid, xs, cst, o);
+#pragma unroll
+                for (int m = 0; m < M; m++)
+                    pv[s * M + m] = o[m];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_next(ring[s]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // tot[i] in DPP row q = the wave total of value i + q * V/4: item i/M + q * DEPTH/4,
+        // token i % M. Every lane stores (the row's first lane to the partial, the others to
+        // their dummy slots): a divergent branch would make the compiler wait for the loads.
+        float tot[V / 4];
+        transpose_reduce<V>(pv, tot);
+#pragma unroll
+        for (int i = 0; i < V / 4; i++) {
+            const int s0 = i / M;
+            constexpr int ST = DEPTH / 4;
+            const int id = q == 0 ? idx[s0] : q == 1 ? idx[s0 + ST] : q == 2 ? idx[s0 + 2 * ST]
+                                                                            : idx[s0 + 3 * ST];
+            part[(lane & 15) == 0 && id >= 0 ? id + i % M : dummy + lane] = tot[i];
+        }
+    }
+
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * M; i += 64 * NW) {
+        const int k = i / M, m = i - k * M;
+        float acc = 0.0f;
+        for (int c = 0; c < NC; c++)
+            acc += part[(k * NC + c) * M + m];
+        float *yp = a.y + (int64_t)m * a.ystride + (int64_t)(r0 + k) * a.yinc;
+        *yp = a.accumulate ? *yp + acc : acc;
+    }
+}
+
+}  // namespace rows
+
+// ---- host -----------------------------------------------------------------------------------------
+
+namespace {
+
+// Launch shape per piece size: items in flight per wave (DEPTH) and waves per workgroup (NW, one
+// workgroup per CU; the register budget is 512 / (NW / 4) per lane).
+template <int TYPE, int M, int P> struct Cfg {
+    static constexpr int DEPTH = P == 2 && M <= 2 ? 8 : 4;
+    static constexpr int NW = M >= 3 ? 8 : 12;
+};
+
+template <int TYPE, int M, int P>
+int launch_one(const rows::Args &a, int grid, size_t lds, hipStream_t s)
+{
+    using C = Cfg<TYPE, M, P>;
+    constexpr auto kern = rows::pn_gemv_rows_kernel<TYPE, M, P, C::DEPTH, C::NW>;
+    if (!lds_limit_once<kern>(rows::kLdsMax))
+        return PN_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * C::NW), lds, s, a);
+    return launch_status();
+}
+
+template <int TYPE, int M>
+int launch_p(int P, const rows::Args &a, int grid, size_t lds, hipStream_t s)
+{
+    if constexpr (M == 1) {
+        if (P == 8)
+            return launch_one<TYPE, M, 8>(a, grid, lds, s);
+    }
+    if constexpr (M <= 2) {
+        if (P == 4)
+            return launch_one<TYPE, M, 4>(a, grid, lds, s);
+    }
+    return launch_one<TYPE, M, 2>(a, grid, lds, s);
+}
+
+// Piece size for a row of nb blocks at M tokens: the largest x that fits the registers (at most 80
+// floats per lane), then the fewest VALU operations per weight, counting the lanes of a partial
+// last chunk as spent.
+template <int TYPE, int M>
+int choose_p(int64_t nb)
+{
+    using D = rows::Dec<TYPE>;
+    int best = 2;
+    double best_cost = 1e30;
+    for (int P : {8, 4, 2}) {
+        if (M * D::CPW * P > 80 || (M > 1 && P == 8) || (M > 2 && P == 4))
+            continue;
+        const int64_t cb = 8 * P, nc = (nb + cb - 1) / cb;
+        const double eff = (double)nb / (double)(nc * cb);
+        const double ops = P * (1 + D::PAIRS * (2 + 2 * M)) + 18.0;  // per item and lane
+        const double cost = ops / (eff * D::CPW * P);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = P;
+        }
+    }
+    return best;
+}
+
+// rows [0, N) of one parity class (row_stride a multiple of 4), blocks [b0, b0 + nb) of each
+template <int TYPE, int M>
+int launch_rows(const uint8_t *row0, int64_t N, int64_t row_stride, int64_t nb, int64_t b0,
+                const float *x, int64_t K, float *y, int64_t ystride, int64_t yinc,
+                bool accumulate, int P, hipStream_t s)
+{
+    using D = rows::Dec<TYPE>;
+    const int64_t cb = 8 * P, NC = (nb + cb - 1) / cb;
+    const size_t x_bytes = (size_t)M * NC * cb * D::GS * sizeof(float);
+    const int cus = device_cus();
+    // partials of a workgroup beside the staged x
+    const int64_t part_cap = ((int64_t)rows::kLdsMax - (int64_t)x_bytes) / (int64_t)sizeof(float) - 64;
+    const int64_t rows_cap = part_cap / (NC * M);
+    if (rows_cap < 1)
+        return PN_ERR_SHAPE;
+    const int64_t slice_bytes = nb * kBlockBytes;
+    int64_t done = 0;
+    while (done < N) {
+        // byte offsets of a launch fit 32 bits
+        int64_t n = std::min<int64_t>(N - done, rows_cap * cus);
+        n = std::min<int64_t>(n, ((int64_t)0x7FFF0000 - slice_bytes) / row_stride + 1);
+        const int grid = (int)std::min<int64_t>(cus, n);
+        const uint8_t *first = row0 + done * row_stride + b0 * kBlockBytes;
+        const uintptr_t fa = reinterpret_cast<uintptr_t>(first);
+        rows::Args a;
+        a.par = (uint32_t)(fa & 3u);
+        a.base = first - a.par;
+        const int64_t end = (int64_t)a.par + (n - 1) * row_stride + slice_bytes;
+        a.nbytes = (uint32_t)((end + 3) & ~(int64_t)3);
+        a.row_stride = (uint32_t)row_stride;
+        a.N = (int)n;
+        a.nb = (int)nb;
+        a.NC = (int)NC;
+        a.rows_max = (int)((n + grid - 1) / grid);
+        a.x = x + b0 * D::G;
+        a.xstride = K;
+        a.y = y + done * yinc;
+        a.ystride = ystride;
+        a.yinc = yinc;
+        a.accumulate = accumulate ? 1 : 0;
+        const size_t lds = std::max<size_t>(
+            rows::kLdsFloor, x_bytes + ((size_t)a.rows_max * NC * M + 64) * sizeof(float));
+        const int st = launch_p<TYPE, M>(P, a, grid, lds, s);
+        if (st != PN_OK)
+            return st;
+        done += n;
+    }
+    return PN_OK;
+}
+
+template <int TYPE, int M>
+int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
+{
+    using D = rows::Dec<TYPE>;
+    const int64_t nb = K / D::G;
+    const int64_t rb = nb * kBlockBytes;
+    const int P = choose_p<TYPE, M>(nb);
+    const int64_t cb = 8 * P;
+    // K slices of whole chunks whose x fits the LDS; each slice after the first adds to y
+    const int64_t chunks_fit = rows::kXLdsMax / ((int64_t)M * cb * D::GS * (int64_t)sizeof(float));
+    const int64_t slice_nb = std::max<int64_t>(1, chunks_fit) * cb;
+    // rows of an odd block count alternate between two alignments: each class is its own launch
+    const bool two = (rb & 2) != 0;
+    for (int64_t b0 = 0; b0 < nb; b0 += slice_nb) {
+        const int64_t n = std::min(slice_nb, nb - b0);
+        for (int cls = 0; cls < (two ? 2 : 1); cls++) {
+            const int64_t Nc = two ? (N - cls + 1) / 2 : N;
+            if (Nc == 0)
+                continue;
+            const int st = launch_rows<TYPE, M>(W + cls * rb, Nc, two ? 2 * rb : rb, n, b0, x, K,
+                                                y + cls, N, two ? 2 : 1, b0 > 0, P, s);
+            if (st != PN_OK)
+                return st;
+        }
+    }
+    return PN_OK;
+}
+
+template <int TYPE>
+int launch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
+             hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_typed<TYPE, 1>(W, N, K, x, y, s);
+    case 2: return launch_typed<TYPE, 2>(W, N, K, x, y, s);
+    case 3: return launch_typed<TYPE, 3>(W, N, K, x, y, s);
+    default: return launch_typed<TYPE, 4>(W, N, K, x, y, s);
+    }
+}
+
+}  // namespace
+
+// The vector-unit PN GEMV for 1 <= M <= 4 (arguments already checked by the entry point).
+int launch_vec(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M,
+               float *y, hipStream_t s)
+{
+    return type == PN_TYPE_PN3T ? launch_m<PN_TYPE_PN3T>(W, N, K, x, M, y, s)
+                                : launch_m<PN_TYPE_PN4T>(W, N, K, x, M, y, s);
+}
+
+}  // namespace pn

@@ -90,9 +90,9 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
  * Accuracy ("PN weight format", "Value"): |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output, y_ref
  * the exact sum, for every finite input whose products and partial sums stay in fp32's normal
  * range. At 1-4 tokens each weight is decoded exactly to the integer n - z, each product with x is
- * exact inside an fp32 fma, and the only roundings are the fp32 sums: chains of at most 20 terms
- * per lane and block piece, one multiply by d, a 64-lane tree and the in-order sum of at most 17
- * chunks per row (about 40 * 2^-24 of sum_k |w x| in the worst case).
+ * exact inside an fp32 fma, and the only roundings are the fp32 sums: eight chains of at most 10
+ * terms per lane and block piece, one multiply by d, a 64-lane tree and the in-order sum of at most
+ * a few dozen chunk partials per row (under 30 * 2^-24 of sum_k |w x| in the worst case).
  * At 5-16 tokens (the matrix cores) the zero point is taken off each code exactly as well, but
  * each x is carried as an fp16 (hi, lo) pair with one exponent per token and group of blocks (4
  * consecutive blocks where W is staged through LDS, one block where it is read directly): exact to
