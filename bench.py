@@ -5,9 +5,11 @@ Workload (one step): one Qwen3.8-27B-shaped MLP at M = 1 token -- gate and up as
 down as pn4t 5120 x 17408. Gate and up read the same x, so they are stored stacked by rows as one
 pn3t 34816 x 5120 matrix and run as one pn_gemv call (the usual fused gate/up projection); down is a
 second call: two launches per step. Weights: seeded N(0, 0.02) fp32 quantized on the GPU by the
-reference quantizer (pn_quantize_rows); x ~ N(0, 1) fp32. Five distinct device copies of the weight
-set (615.5 MB, above the 256 MB Infinity Cache) are used round-robin, so every step reads its
-weights from HBM. value = weight bytes per step / time per step.
+reference quantizer (pn_quantize_rows), checked against the CPU oracle's quantizer byte for byte on
+every 97th row of each matrix before timing; one step's y is checked against the oracle on the same
+rows after timing. x ~ N(0, 1) fp32. Five distinct device copies of the weight set (615.5 MB, above
+the 256 MB Infinity Cache) are used round-robin, so every step reads its weights from HBM.
+value = weight bytes per step / time per step.
 
 Prints one JSON line (rank 0). See --help for the knobs.
 """
@@ -28,7 +30,7 @@ HBM_PEAK_GBS = 8000.0
 # the same counters read for a plain copy of known size; valid only for the kernel sources they
 # were taken on (their hash is recorded with them).
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pn_gemv_mlp_m1_hbm_counters.txt")
-KERNEL_SOURCES = ["block_quantized_weight_pn3t_amd/csrc/pn_gemv.hip",
+KERNEL_SOURCES = ["block_quantized_weight_pn3t_amd/csrc/pn_gemv_rows.hip",
                   "block_quantized_weight_pn3t_amd/csrc/pn_common.h"]
 METRIC = "PN GEMV weight GB/s at M=1 (% of MI355X HBM peak), K=5120/17408"
 
@@ -71,6 +73,7 @@ def build_weights(pn, torch, dev, copies):
         torch.cuda.synchronize()
         if int(st.abs().sum()) != 0 or int(ver.sum()) != N:
             raise RuntimeError(f"{name}: quantizer status / validation failed")
+        oracle_check_bytes(name, typ, parts, K, W0)
         Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
         x = torch.from_numpy(np.ascontiguousarray(synth.activations(xseed, 1, K))).to(dev)
         y = torch.empty((1, N), dtype=torch.float32, device=dev)
@@ -78,6 +81,47 @@ def build_weights(pn, torch, dev, copies):
         log(f"[bench] {name}: {N}x{K} type {typ}, {N * rb / 1e6:.2f} MB x {copies} copies "
             f"({time.time() - t0:.1f} s)")
     return mats
+
+
+SAMPLE_STRIDE = 97  # every 97th row of each matrix is checked against the oracle
+
+
+def oracle_check_bytes(name, typ, parts, K, W0):
+    """The GPU-quantized rows 0, 97, 194, ... of each stacked part must equal the CPU oracle's
+    quantization of the same fp32 rows, byte for byte."""
+    import numpy as np
+    import oracle
+    import synth
+    r0 = 0
+    for n, wseed in parts:
+        rows = np.arange(0, n, SAMPLE_STRIDE)
+        w = synth.gaussian_weights(wseed, n, K, 0.02)[rows]
+        ref, st = oracle.quantize_rows(typ, np.ascontiguousarray(w), threads=host_threads())
+        got = W0[r0 + rows].cpu().numpy()
+        if st.any() or not np.array_equal(got, ref):
+            raise RuntimeError(f"{name}: GPU quantizer differs from the oracle (seed {wseed})")
+        r0 += n
+    log(f"[bench] {name}: {sum(len(range(0, n, SAMPLE_STRIDE)) for n, _ in parts)} sampled rows "
+        f"byte-identical to the oracle quantizer")
+
+
+def oracle_check_step(mats):
+    """One step's y on the sampled rows against the oracle: |y - y_ref| <= 1e-5 sum |w x|."""
+    import numpy as np
+    import oracle
+    worst = 0.0
+    for m in mats:
+        rows = np.arange(0, m["N"], SAMPLE_STRIDE)
+        W = m["Ws"][0][rows].cpu().numpy()
+        x = m["x"].cpu().numpy()
+        y = m["y"].cpu().numpy()[0, rows].astype(np.float64)
+        y_ref, bound = oracle.gemv(m["typ"], np.ascontiguousarray(W), len(rows), m["K"], x,
+                                   threads=host_threads())
+        err = np.abs(y - y_ref[0])
+        if not np.all(err <= 1e-5 * bound[0]):
+            raise RuntimeError(f"{m['name']}: y outside the oracle bound")
+        worst = max(worst, float(np.max(err / np.maximum(bound[0], 1e-300))))
+    return worst
 
 
 def kernel_source_hash() -> str:
@@ -463,6 +507,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    one_step(0)  # copy 0, outside the timed region
+    torch.cuda.synchronize()
+    check_worst = oracle_check_step(mats)
+    log(f"[bench] one step's y on the sampled rows within the oracle bound (worst err/bound "
+        f"{check_worst:.2e})")
 
     # per-kernel durations, live, on the launch stream: each kernel launched K times back to back
     # over the rotated copies between two events (avg = elapsed / K, launch gaps included), and

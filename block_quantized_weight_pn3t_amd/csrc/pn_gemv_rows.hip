@@ -34,6 +34,8 @@
 // sums are added by DPP and permlane swaps; one lane writes the item's partial to LDS, and at the
 // end the workgroup adds each row's chunk partials in chunk order and writes y. No atomics: the
 // same inputs and launch shape give the same bits.
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "pn_common.h"
@@ -604,7 +606,14 @@ int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *
     using D = rows::Dec<TYPE>;
     const int64_t nb = K / D::G;
     const int64_t rb = nb * kBlockBytes;
-    const int P = choose_p<TYPE, M>(nb);
+    int P = choose_p<TYPE, M>(nb);
+    // PN_GEMV_PIECE=8|4|2 forces the piece size where the registers allow it (tests reach every
+    // variant with it; the results stay within the same bound)
+    if (const char *e = getenv("PN_GEMV_PIECE")) {
+        const int f = atoi(e);
+        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
+            P = f;
+    }
     const int64_t cb = 8 * P;
     // K slices of whole chunks whose x fits the LDS; each slice after the first adds to y
     const int64_t chunks_fit = rows::kXLdsMax / ((int64_t)M * cb * D::GS * (int64_t)sizeof(float));

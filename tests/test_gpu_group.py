@@ -42,11 +42,11 @@ def run_group(pn, torch, dev, K, parts, x, x_offset=0):
 
 # (K, [(type, N)]): the body each part takes is fixed by K
 CASES = [
-    (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # register pn3t + long-row pn4t (q, k, v)
+    (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # 64-block pn3t + 80-block pn4t (q, k, v)
     (5120, [(PN3T, 1000), (PN3T, 777)]),                        # two register pn3t parts (gate, up)
     (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # register bodies of both types, tiny
                                                                 # parts; 50 pn4t blocks: separate at 3-4
-    (6400, [(PN3T, 140), (PN4T, 301)]),                         # long-row bodies of both types
+    (6400, [(PN3T, 140), (PN4T, 301)]),                         # long rows of both types
     (5120, [(PN3T, 0), (PN4T, 50), (PN3T, 9)]),                 # an empty part
     (5120, [(PN3T, 200), (PN4T, 64), (PN3T, 17), (PN4T, 300)]),  # four parts, all on the matrix
                                                                 # cores at 3-4 tokens
@@ -130,10 +130,10 @@ def run_group_hadamard(pn, torch, dev, K, parts, x, B):
 
 # (K, B, [(type, N)]): x rotated in slices of B ("Files that use PN"; the reading of pn_hadamard.h)
 ROT_CASES = [
-    (5120, 1024, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),   # register pn3t + long-row pn4t
+    (5120, 1024, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),   # 64-block pn3t + 80-block pn4t
     (5120, 256, [(PN3T, 300), (PN3T, 77)]),                  # two register parts
     (3200, 64, [(PN3T, 333), (PN4T, 65), (PN4T, 7)]),        # register bodies of both types
-    (6400, 256, [(PN3T, 140), (PN4T, 301)]),                 # long-row bodies of both types
+    (6400, 256, [(PN3T, 140), (PN4T, 301)]),                 # long rows of both types
     (17408, 1024, [(PN4T, 37), (PN4T, 20)]),                 # long rows, 17 chunks
 ]
 

@@ -186,50 +186,75 @@ def test_gemv_long_rows(env, typ, N, nb, M):
         assert_within(y, y_ref, bound)
 
 
+# piece sizes (words per lane) each token count may run: the x of a piece must fit the registers
+PIECES = {1: (8, 4, 2), 2: (4, 2), 3: (2,), 4: (2,)}
+
+
 @pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 19, 40), (PN4T, 45, 128), (PN3T, 9, 72),
-                                      (PN4T, 300, 272)])
+                                      (PN4T, 300, 272), (PN3T, 21, 33), (PN4T, 40, 17)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-def test_gemv_lane_kernel_gives_the_streaming_bits(env, monkeypatch, typ, N, nb, M):
-    """Rows of a multiple of 8 blocks at a 4-byte aligned W take the streaming kernel; the lane
-    kernel (which serves any alignment) decodes each item with the same instructions and reduces
-    the same batches, so switching it on gives the same bits."""
+def test_gemv_every_piece_size(env, monkeypatch, typ, N, nb, M):
+    """Each piece size the registers allow at M tokens, forced in turn (PN_GEMV_PIECE), at both
+    alignments of W: whole and partial last chunks, and odd block counts (rows of two
+    alignments, run as two launches)."""
     pn, torch, dev = env
     G = oracle.PARAMS[typ][1]
     K = nb * G
     _, W = quantized(typ, N, K, 8000 + nb)
     x = synth.activations(8100 + nb, M, K)
-    Wd = dev_bytes(torch, dev, W)
-    y_stream = run_gemv(pn, torch, dev, typ, Wd, N, K, x)
-    monkeypatch.setenv("PN_GEMV_LANE", "1")
-    y_lane = run_gemv(pn, torch, dev, typ, Wd, N, K, x)
-    assert np.array_equal(y_stream.view(np.uint32), y_lane.view(np.uint32))
     y_ref, bound = oracle.gemv(typ, W, N, K, x)
-    assert_within(y_lane, y_ref, bound)
+    for P in PIECES[M]:
+        monkeypatch.setenv("PN_GEMV_PIECE", str(P))
+        for offset in (0, 2):
+            y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
+            assert_within(y, y_ref, bound)
 
 
-@pytest.mark.parametrize("M", [1, 2])
-def test_gemv_x_dynamic_range(env, M):
-    """pn3t rows of <= 64 blocks carry x as fp16 (hi, lo) pairs with one exponent per block: within
-    the documented range (every x within 2^20 of its block's largest |x|) the tolerance holds.
-    Here |x| is in [1, 2) with one element per block at 2^19. That element meets code 0 (weight
-    -4d), so the block's sum of n|x| stays comparable to its sum of |n - z||x|: the condition under
-    which the folded zero point keeps the bound (a dominant x meeting a code next to z is the
-    documented exception)."""
+def set_codes(W, typ, N, nb, elems, codes):
+    """Rewrites, in every row, the code of element elems[b] of block b to codes[b]: code t of word i
+    sits at bit BITS*(t>>1) + 16*(t&1) of the little-endian word at block byte 2 + 4i ("PN weight
+    format", "Block layout")."""
+    bits, G, cpw, _ = oracle.PARAMS[typ]
+    blk = W.reshape(N, nb, 34)
+    for b in range(nb):
+        i, t = divmod(int(elems[b]), cpw)
+        shift = bits * (t >> 1) + 16 * (t & 1)
+        o = 2 + 4 * i
+        word = sum(blk[:, b, o + q].astype(np.uint32) << np.uint32(8 * q) for q in range(4))
+        mask = np.uint32(((1 << bits) - 1) << shift)
+        word = (word & ~mask) | np.uint32(int(codes[b]) << shift)
+        for q in range(4):
+            blk[:, b, o + q] = ((word >> np.uint32(8 * q)) & np.uint32(0xFF)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("typ,nb", [(PN3T, 64), (PN4T, 80), (PN3T, 27), (PN4T, 272)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("mag", [2.0 ** 12, 2.0 ** 16, 2.0 ** 19])
+def test_gemv_dominant_x_on_code_near_z(env, monkeypatch, typ, nb, M, mag):
+    """One x per block far larger than the rest (|x| in [1, 2) elsewhere), meeting a weight whose
+    code is z (w = 0), z + 1 or z - 1: the bound 1e-5 * sum |w x| must hold however small the
+    other products are against the large x ("PN weight format", "Value": each weight is exact, so
+    code z contributes exactly nothing). Every piece size the token count allows, forced in turn;
+    the element and the code offset vary from block to block, and over the tokens."""
     pn, torch, dev = env
-    N, K = 300, 5120
-    _, W = quantized(PN3T, N, K, 8200)
+    bits, G, cpw, z = oracle.PARAMS[typ]
+    N, K = 48, nb * G
+    _, W = quantized(typ, N, K, 8300 + nb)
     W = W.copy()
-    # element 37 of each block is code t = 7 of word 3: bits 25..27 of the word, i.e. bits 1..3 of
-    # block byte 2 + 4*3 + 3 = 17 ("PN weight format", "Block layout"); set it to 0
-    blocks = W.reshape(N, K // 80, 34)
-    blocks[:, :, 17] &= np.uint8(0xF1)
-    u = synth.uniform(8201, M * K).reshape(M, K)
-    x = ((1.0 + u) * np.where(synth.uniform(8202, M * K).reshape(M, K) < 0.5, -1.0, 1.0))
-    x[:, 37::80] = 2.0 ** 19
+    elems = (np.arange(nb) * 37 + 11) % G
+    offs = np.array([0, 1, -1])[np.arange(nb) % 3]
+    set_codes(W, typ, N, nb, elems, z + offs)
+    u = synth.uniform(8301 + nb, M * K).reshape(M, K)
+    sgn = np.where(synth.uniform(8302 + nb, M * K).reshape(M, K) < 0.5, -1.0, 1.0)
+    x = (1.0 + u) * sgn
+    for m in range(M):
+        x[m, np.arange(nb) * G + elems] = mag * (-1.0) ** m
     x = x.astype(np.float32)
-    y_ref, bound = oracle.gemv(PN3T, W, N, K, x)
-    y = run_gemv(pn, torch, dev, PN3T, dev_bytes(torch, dev, W), N, K, x)
-    assert_within(y, y_ref, bound)
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    for P in PIECES[M]:
+        monkeypatch.setenv("PN_GEMV_PIECE", str(P))
+        y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
+        assert_within(y, y_ref, bound)
 
 
 @pytest.mark.parametrize("typ,nb", [(PN3T, 1), (PN3T, 3), (PN4T, 129)])
@@ -320,6 +345,22 @@ def test_config3_mlp_gemv(env, name, typ, N, K, seed, xseed):
     y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
     y_ref, bound = oracle.gemv(typ, W, N, K, x)
     print(name, "worst err/bound", assert_within(y, y_ref, bound))
+
+
+@pytest.mark.slow
+def test_config3_stacked_gate_up_every_row(env):
+    """The launch the bench times: gate (seed 301) and up (seed 302) stacked by rows into one pn3t
+    34816 x 5120 matrix at M = 1, every row against the oracle."""
+    pn, torch, dev = env
+    K = 5120
+    _, Wg = quantized(PN3T, 17408, K, 301)
+    _, Wu = quantized(PN3T, 17408, K, 302)
+    W = np.concatenate([Wg, Wu])
+    N = W.shape[0]
+    x = synth.activations(304, 1, K)
+    y = run_gemv(pn, torch, dev, PN3T, dev_bytes(torch, dev, W), N, K, x)
+    y_ref, bound = oracle.gemv(PN3T, W, N, K, x)
+    print("stacked gate+up worst err/bound", assert_within(y, y_ref, bound))
 
 
 # ---- config 4: the decoder-layer set at M = 1..4 -------------------------------------------------

@@ -1,6 +1,6 @@
 """GPU parity of the PN GEMV at several tokens through the C ABI against the CPU oracle ("PN weight
 format", "Block layout" and "Value"; the sum y = W x itself): the matrix-core path (5-16 tokens) and
-the vector-unit kernels at 2-4 tokens.
+the vector-unit kernel at 2-4 tokens.
 
 Tolerance as for every PN GEMV: |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per output. The cases cover
 ragged row counts (a last tile of 16 rows partly empty), both alignment parities of the weights,
@@ -161,9 +161,8 @@ def test_gemv_direct_weight_loads_forced(env, monkeypatch, typ, N, nb, M):
 @pytest.mark.parametrize("typ,N,nb", [(PN4T, 300, 80), (PN4T, 1024, 80), (PN4T, 77, 96),
                                       (PN3T, 37, 68), (PN3T, 515, 128), (PN4T, 9, 100)])
 def test_gemv_two_tokens_medium_rows(env, typ, N, nb):
-    """Two tokens on rows of 65-130 blocks, W 4-byte aligned (the streaming kernel, with a
-    lane-kernel remainder where the row is not a multiple of 8 blocks) and at +2 bytes (the lane
-    kernel)."""
+    """Two tokens on rows of 65-130 blocks (partial last chunks, odd block counts), W 4-byte
+    aligned and at +2 bytes."""
     pn, torch, dev = env
     K, W = case(typ, N, nb, 9400 + nb)
     x = synth.activations(9500 + nb, 2, K)

@@ -35,19 +35,18 @@ def gemv_x_at(pn, torch, dev, typ, Wd, N, K, x, offset_floats):
     return yd.cpu().numpy()
 
 
-# (type, N, blocks per row, M, environment switch or None): the kernel each case reaches
+# (type, N, blocks per row, M, forced piece size or None): the variant each case reaches
 CASES = [
-    (PN3T, 300, 64, 1, None),                  # register kernel, one token
-    (PN4T, 100, 40, 2, None),                  # register kernel, two tokens
-    (PN4T, 70, 272, 1, None),                  # long-row kernel, one token
-    (PN3T, 50, 70, 2, None),                   # long-row kernel, two tokens
-    (PN4T, 19, 130, 1, "PN_GEMV_NO_FLAT"),     # general kernel, forced
-    (PN4T, 77, 96, 2, None),                   # matrix cores, W through LDS, two tokens
-    (PN3T, 37, 64, 3, None),                   # matrix cores, W through LDS, three tokens
-    (PN4T, 45, 128, 4, None),                  # matrix cores, W through LDS, four tokens
+    (PN3T, 300, 64, 1, None),                  # vector units, 8-word pieces, one token
+    (PN4T, 100, 40, 2, None),                  # vector units, 4-word pieces, two tokens
+    (PN4T, 70, 272, 1, None),                  # vector units, long rows, one token
+    (PN3T, 50, 70, 2, None),                   # vector units, two tokens
+    (PN4T, 19, 130, 1, ("PN_GEMV_PIECE", "2")),  # vector units, 2-word pieces, forced
+    (PN3T, 37, 64, 3, None),                   # vector units, 2-word pieces, three tokens
+    (PN4T, 45, 128, 4, None),                  # vector units, four tokens
+    (PN4T, 77, 96, 5, None),                   # matrix cores, W through LDS
     (PN3T, 33, 10, 5, None),                   # matrix cores, direct weight loads
     (PN4T, 20, 32, 9, None),                   # matrix cores, K-split layout
-    (PN3T, 37, 64, 3, "PN_GEMV_NO_MFMA"),      # vector kernel at three tokens, forced
 ]
 
 
@@ -55,7 +54,7 @@ CASES = [
 def test_gemv_x_unaligned_same_bits(env, monkeypatch, typ, N, nb, M, force):
     pn, torch, dev = env
     if force:
-        monkeypatch.setenv(force, "1")
+        monkeypatch.setenv(*force)
     G = oracle.PARAMS[typ][1]
     K = nb * G
     _, W = quantized(typ, N, K, 11000 + nb + M)
