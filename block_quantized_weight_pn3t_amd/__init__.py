@@ -12,7 +12,7 @@ import os
 
 __all__ = ["PN3T", "PN4T", "PNError", "row_bytes", "validate_rows", "validate_row",
            "dequantize_rows", "dequantize_row", "gemv", "gemv_group", "quantize_rows", "hadamard_rows",
-           "gemv_hadamard", "gemv_group_hadamard", "nvfp4_validate_rows",
+           "gemv_hadamard", "gemv_hadamard_noalloc", "gemv_group_hadamard", "nvfp4_validate_rows",
            "nvfp4_dequantize_rows", "gemv_nvfp4", "fp8row_validate_rows", "fp8row_dequantize_rows", "gemv_fp8row",
            "library_path", "status_string", "lib"]
 
@@ -23,6 +23,7 @@ MAX_TOKENS = 4         # NVFP4 and row-scaled E4M3 GEMV
 GEMV_MAX_TOKENS = 16   # PN GEMV
 GEMV_HADAMARD_MAX_TOKENS = 4  # PN GEMV with the rotation fused
 GEMV_GROUP_MAX_PARTS = 4  # matrices per pn_gemv_group call
+NOALLOC_MAX_FLOATS = 262144  # M * K limit of pn_gemv_hadamard_noalloc
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpn.so")
@@ -52,6 +53,7 @@ _SIGS = {
     "pn_quantize_rows": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
     "pn_hadamard_rows": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "pn_gemv_hadamard": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
+    "pn_gemv_hadamard_noalloc": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
     "pn_nvfp4_validate_rows": (_I32, [_P, _F, _I64, _I64, _P, _P]),
     "pn_nvfp4_dequantize_rows": (_I32, [_P, _P, _F, _I64, _I64, _P, _P]),
     "pn_gemv_nvfp4": (_I32, [_P, _P, _F, _I64, _I64, _P, _I64, _P, _P]),
@@ -210,7 +212,8 @@ def hadamard_rows(x, B, out, M=None, K=None, stream=None):
 
 
 def gemv_hadamard(type_, W, N, K, x, B, y, M=None, stream=None):
-    """y[M, N] <- W[N, K] . (H x)[M, K]^T, the rotation fused into the GEMV (M <= 4)."""
+    """y[M, N] <- W[N, K] . (H x)[M, K]^T: x rotated into a stream-ordered temporary, then the GEMV
+    (M <= 4)."""
     import torch
     _dev(x, "x", torch.float32)
     _dev(y, "y", torch.float32)
@@ -218,6 +221,18 @@ def gemv_hadamard(type_, W, N, K, x, B, y, M=None, stream=None):
         M = 1 if x.dim() == 1 else x.shape[0]
     _check(_lib.pn_gemv_hadamard(type_, _ptr(W), N, K, _ptr(x), M, B, _ptr(y), _stream(stream)),
            "pn_gemv_hadamard")
+
+
+def gemv_hadamard_noalloc(type_, W, N, K, x, B, y, M=None, stream=None):
+    """As gemv_hadamard, with the rotated x in the library's own device array (no allocation;
+    M * K <= PN_NOALLOC_MAX_FLOATS; calls that overlap on one GPU race on that array)."""
+    import torch
+    _dev(x, "x", torch.float32)
+    _dev(y, "y", torch.float32)
+    if M is None:
+        M = 1 if x.dim() == 1 else x.shape[0]
+    _check(_lib.pn_gemv_hadamard_noalloc(type_, _ptr(W), N, K, _ptr(x), M, B, _ptr(y),
+                                         _stream(stream)), "pn_gemv_hadamard_noalloc")
 
 
 def gemv_hadamard_ptr(type_, W_ptr, N, K, x_ptr, M, B, y_ptr, stream_handle):

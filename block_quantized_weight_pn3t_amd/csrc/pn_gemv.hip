@@ -9,6 +9,8 @@
 //    stream-ordered temporary, then the GEMV above on it -- the same bits as the two calls made by
 //    hand. The group variants rotate x once for all their matrices.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "pn_common.h"
 
@@ -99,6 +101,40 @@ static int with_rotated(const float *x, int64_t M, int64_t K, int64_t B, hipStre
     return st;
 }
 
+// ---- the rotated x of pn_gemv_hadamard_noalloc: a file-scope device array --------------------
+// Each GPU the library runs on holds its own copy for the life of the process. In host code the
+// array's name is a host-side stand-in, not a device address: the address is looked up once per
+// device (with that device current) and only that address is handed to kernels.
+__device__ __align__(256) float scratch[PN_NOALLOC_MAX_FLOATS];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<float *> g_scratch[kMaxScratchDevices];
+static std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, or nullptr (the caller reports
+// PN_ERR_HIP).
+static float *scratch_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return nullptr;
+    float *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        p = static_cast<float *>(q);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace pn
 
 using namespace pn;
@@ -166,6 +202,39 @@ extern "C" int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, c
     return with_rotated(x, M, K, B, s, [&](const float *xr) {
         return dispatch(type, (const uint8_t *)W, N, K, xr, M, y, s);
     });
+}
+
+extern "C" int pn_gemv_hadamard_noalloc(int type, const void *W, int64_t N, int64_t K,
+                                        const float *x, int64_t M, int64_t B, float *y,
+                                        void *stream)
+{
+    if (type != PN_TYPE_PN3T && type != PN_TYPE_PN4T)
+        return PN_ERR_TYPE;
+    if (N < 0 || pn_row_bytes(type, K) == 0)
+        return PN_ERR_SHAPE;
+    if (M < 0 || M > PN_GEMV_HADAMARD_MAX_TOKENS)
+        return PN_ERR_TOKENS;
+    if (hadamard_log(B, K) < 0)
+        return PN_ERR_HADAMARD;
+    if (M * K > PN_NOALLOC_MAX_FLOATS)
+        return PN_ERR_SHAPE;
+    if (N == 0 || M == 0)
+        return PN_OK;
+    if (!W || !x || !y)
+        return PN_ERR_NULL;
+    if (!aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4))
+        return PN_ERR_ALIGN;
+    int st = check_device();
+    if (st != PN_OK)
+        return st;
+    float *xr = scratch_ptr();
+    if (!xr)
+        return PN_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    st = pn_hadamard_rows(x, M, K, B, xr, s);
+    if (st != PN_OK)
+        return st;
+    return dispatch(type, (const uint8_t *)W, N, K, xr, M, y, s);
 }
 
 extern "C" int pn_gemv_group_hadamard(const pn_gemv_part *parts, int count, int64_t K,

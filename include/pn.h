@@ -143,6 +143,18 @@ int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 
+/* pn_gemv_hadamard without any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it). The rotated x goes to a
+ * file-scope device array of PN_NOALLOC_MAX_FLOATS floats (1 MiB) that each GPU holds for the life
+ * of the process; the rotation overwrites every element the GEMV then reads, so nothing is cleared
+ * between calls. Same arguments, errors and bits as pn_gemv_hadamard, plus PN_ERR_SHAPE when
+ * M * K exceeds PN_NOALLOC_MAX_FLOATS. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from several host threads) race on it, so callers
+ * order them. */
+#define PN_NOALLOC_MAX_FLOATS 262144
+int pn_gemv_hadamard_noalloc(int type, const void *W, int64_t N, int64_t K, const float *x,
+                             int64_t M, int64_t B, float *y, void *stream);
+
 /* Several GEMVs that share x, over the rotated x: x rotated once into a stream-ordered temporary
  * (as pn_gemv_hadamard), then pn_gemv_group on it -- parts[i].y = W_i x' with the bits of
  * pn_hadamard_rows followed by one pn_gemv per part. B as in pn_hadamard_rows, 0 <= M <= 4 (else

@@ -82,6 +82,15 @@ def test_argument_errors_are_reported_before_any_device_work(pn):
     assert L.pn_gemv_hadamard(124, fake, 4, 650, fake, 1, 64, fake, None) == -2
     assert L.pn_gemv_hadamard(7, fake, 4, 640, fake, 1, 64, fake, None) == -1
     assert L.pn_gemv_hadamard(124, fake, 0, 640, fake, 1, 64, fake, None) == 0
+    # the entry point that allocates nothing: the same checks, plus its array's size limit
+    na = L.pn_gemv_hadamard_noalloc
+    assert na(124, fake, 4, 640, fake, 5, 64, fake, None) == -3
+    assert na(124, fake, 4, 640, fake, 1, 256, fake, None) == -8
+    assert na(7, fake, 4, 640, fake, 1, 64, fake, None) == -1
+    assert na(125, fake, 4, 65600, fake, 4, 64, fake, None) == -2      # M * K above 262,144
+    assert na(125, fake, 4, 131136, fake, 2, 64, fake, None) == -2
+    assert na(125, fake, 0, 65536, fake, 4, 1024, fake, None) == 0     # 262,144 floats: in range
+    assert na(124, P(0x1001), 4, 640, fake, 1, 64, fake, None) == -5
     assert L.pn_gemv_hadamard(124, None, 4, 640, fake, 1, 64, fake, None) == -4
     # several GEMVs that share x
     Part = pn.GemvPart
