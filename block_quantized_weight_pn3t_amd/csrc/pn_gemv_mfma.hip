@@ -628,13 +628,19 @@ pn_gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t ro
 // other kernel touch 16-20 cache lines for 512 bytes per instruction; these, 2-3 per 256. Each
 // wave keeps 3 steps in flight in a ring of 4 slots. The offsets within a step are constant per
 // lane; the step's position is one scalar offset, and the buffer's bounds check reads rows past
-// the matrix end as zero. Past its last step a wave re-issues its last one, so that exactly 27
-// loads follow every step it waits for. The waits are explicit (the compiler does not order LDS
+// the matrix end as zero. Past its last step a wave re-issues its last one, so that exactly
+// kWaitAfter loads follow every step it waits for. The waits are explicit (the compiler does not order LDS
 // reads after these copies).
 constexpr int kChunkBlocks = 4;
 constexpr int kChunkBytes = 16 * kChunkBlocks * kBlockBytes;  // 2176
 constexpr int kLdsRing = 4;                                    // slots per wave (a power of 2)
 constexpr int kStepLoads = 9;                                  // buffer loads per step
+// Steps in flight ahead of the one being read: every slot but that one. The wait for a step's copy
+// therefore leaves exactly kWaitAfter loads (the later steps') in flight.
+constexpr int kStepsAhead = kLdsRing - 1;
+constexpr int kWaitAfter = kStepsAhead * kStepLoads;
+static_assert(kWaitAfter <= 63, "vmcnt holds at most 63 loads");
+static_assert(kStepLoads == 8 + 1, "issue(): 8 loads of 64 dwords and one of the last 64");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -754,9 +760,9 @@ mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_byte
                     }
                 }
                 asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
-                issue_next();
-                issue_next();
-                issue_next();
+#pragma unroll
+                for (int s = 0; s < kStepsAhead; s++)
+                    issue_next();
                 asm volatile("" ::: "memory");
 #pragma unroll
                 for (int g0 = 0; g0 < HQ; g0 += 4)
@@ -782,9 +788,9 @@ mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_byte
                                                                            npb, xvec4, none);
             } else {
                 mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
-                    issue_next();
-                    issue_next();
-                    issue_next();
+#pragma unroll
+                    for (int s = 0; s < kStepsAhead; s++)
+                        issue_next();
                 });
             }
 #pragma unroll
@@ -792,10 +798,11 @@ mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_byte
                 const int lo = max(i0, t * n4), hi = min(i1, (t + 1) * n4);
                 for (int it = lo; it < hi; it++) {
                     // refill the slot read one step ago, then wait for this step's copy: loads
-                    // retire in order and exactly 3 steps (27 loads) were issued after it
+                    // retire in order and exactly kStepsAhead steps (kWaitAfter loads) were
+                    // issued after it
                     asm volatile("" ::: "memory");  // that slot's reads stay before
                     issue_next();
-                    asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitAfter) : "memory");
                     const uint8_t *cr = ring + (it & (kLdsRing - 1)) * kChunkBytes + 136 * n16;
                     const uint8_t *cw = cr + 8 * g;
                     const uint8_t *xb = xa + ((it - t * n4) * kChunkBlocks) * per_block;

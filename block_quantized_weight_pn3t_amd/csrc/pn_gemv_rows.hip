@@ -312,66 +312,49 @@ pn_gemv_rows_kernel(Args a)
     const uint32_t rstride = a.row_stride;
 
     // ---- the wave's item sequence: its items (chunk-major) cut into one segment per chunk, each
-    // segment padded with empty items to a whole number of groups of DEPTH, so that a group never
-    // spans two chunks and x changes only between groups. Two cursors walk it: one for the loads,
-    // DEPTH items ahead, and one for the decode.
+    // segment taken in groups of DEPTH items (the last group of a segment may hold fewer), so that
+    // a group never spans two chunks and x changes only between groups. Two cursors walk it one
+    // group at a time: one for the loads, a group ahead, and one for the decode.
     struct Cur {
-        int c, r;    // chunk and row (within the workgroup) of the next item
-        int rem;     // items left in the current segment
-        int pad;     // empty items left after it
-        int left;    // items left in the wave's range
-        int pos;     // items taken from the current segment
+        int c, r;  // chunk and row (within the workgroup) of the next item
+        int rem;   // items left in the current segment
+        int left;  // items left in the wave's range
     };
     auto cur_init = [&](Cur &k) {
         k.left = it1 - it0;
         k.c = nr > 0 ? it0 / nr : 0;
         k.r = it0 - k.c * nr;
         k.rem = min(nr - k.r, k.left);
-        k.pad = 0;
-        k.pos = 0;
     };
-    // the next segment, once the current one and its padding are used up
-    auto cur_seg = [&](Cur &k) {
-        if (k.rem == 0 && k.pad == 0 && k.left > 0) {
+    // the next group: its chunk, first row and number of items (0 past the end)
+    auto cur_group = [&](Cur &k, int &c, int &r, int &cnt) {
+        if (k.rem == 0 && k.left > 0) {
             k.c++;
             k.r = 0;
             k.rem = min(nr, k.left);
-            k.pos = 0;
         }
-    };
-    // takes one item of the sequence: true (with its chunk and row) for a real one
-    auto cur_step = [&](Cur &k, int &c, int &r) -> bool {
-        cur_seg(k);
-        if (k.rem > 0) {
-            c = k.c;
-            r = k.r;
-            k.r++;
-            k.left--;
-            k.pos++;
-            if (--k.rem == 0)
-                k.pad = (DEPTH - k.pos % DEPTH) % DEPTH;
-            return true;
-        }
-        if (k.pad > 0)
-            k.pad--;
-        return false;
+        c = k.c;
+        r = k.r;
+        cnt = min(DEPTH, k.rem);
+        k.r += cnt;
+        k.rem -= cnt;
+        k.left -= cnt;
     };
 
     // ---- weight loads. Every slot is refilled unconditionally right after its item (a refill
     // that may or may not happen would make the compiler copy the slot, and the copy would wait
-    // for the load in flight); an empty item's load goes through a buffer of size 0, which reads
-    // no memory.
-    Cur lcur;
-    cur_init(lcur);
-    auto load_next = [&](Slot<P> &sl) {
-        int c = 0, r = 0;
-        const bool real = cur_step(lcur, c, r);
+    // for the load in flight); the load of an empty item goes through a buffer of size 0, which
+    // reads no memory. Lanes past the end of a row load nothing in the row's last chunk.
+    auto load_item = [&](Slot<P> &sl, int c, int r, bool real) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(a.base), (short)0, real ? (int)a.nbytes : 0, 0x00020000);
         const bool lastc = c == NC - 1;
         load_slot<P>(rs, lastc ? ln.voffl : ln.voff, lastc ? ln.dvoffl : ln.dvoff,
                      (uint32_t)(r0 + r) * rstride + CBYTES * (uint32_t)c, sl);
     };
+    Cur lcur;
+    cur_init(lcur);
+    int lgc = 0, lgr = 0, lgn = 0;  // the group being loaded
     // ---- x staging: the first pass of x loads goes out before the weight loads, so that waiting
     // for it waits for no weights; further passes (large M * K) wait for everything in flight
     constexpr int G4 = D::G / 4;       // 16-byte pieces of x per block
@@ -406,9 +389,10 @@ pn_gemv_rows_kernel(Args a)
     stage_load(0, xv0);
 
     Slot<P> ring[DEPTH];
+    cur_group(lcur, lgc, lgr, lgn);
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-        load_next(ring[s]);
+        load_item(ring[s], lgc, lgr + s, s < lgn);
 
     stage_store(0, xv0);
     for (int pass = 1; pass < npass; pass++) {
@@ -420,38 +404,33 @@ pn_gemv_rows_kernel(Args a)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- items: x of the current chunk in registers, DEPTH items in flight. The partials of a
-    // group of DEPTH items are summed over the wave together (one transposed reduction), and the
-    // first lane of each DPP row stores its share of them.
+    // group are summed over the wave together (one transposed reduction), and the first lane of
+    // each DPP row stores its share of them.
     static_assert(DEPTH % 4 == 0, "groups of 4k items");
     constexpr int V = DEPTH * M;
     float xs[M][P][2][D::PAIRS];
     int xc = -1;             // chunk whose x is in xs
     uint32_t dwid = 16;      // d field width: 0 for lanes past the end of the row
     const int q = lane >> 4;
-    Cur ccur;
-    cur_init(ccur);
     for (;;) {
-        cur_seg(ccur);
-        if (ccur.rem == 0)
+        const int gc = lgc, gr = lgr, gn = lgn;  // this group (already loaded)
+        if (gn == 0)
             break;
-        if (ccur.c != xc) {
-            xc = ccur.c;
+        cur_group(lcur, lgc, lgr, lgn);          // the next group, loaded as this one is decoded
+        if (gc != xc) {
+            xc = gc;
             dwid = xc * CB + ln.bl < a.nb ? 16u : 0u;
 #pragma unroll
             for (int m = 0; m < M; m++)
                 read_x<TYPE, P>(xl + m * XT + xc * CB * D::GS + ln.xoff, ln.straddle, xs[m]);
         }
         float pv[V];
-        int idx[DEPTH];  // LDS index of each item's first partial, -1 for an empty item
 #pragma unroll
         for (int s = 0; s < DEPTH; s++) {
-            int c = 0, r = 0;
-            const bool real = cur_step(ccur, c, r);
-            idx[s] = real ? (r * NC + c) * M : -1;
 #pragma unroll
             for (int m = 0; m < M; m++)
                 pv[s * M + m] = 0.0f;
-            if (real) {  // uniform
+            if (s < gn) {  // uniform
                 float o[M];
                 item_mac<TYPE, M, P>(ring[s], ln, dwid, xs, cst, o);
 #pragma unroll
@@ -459,7 +438,7 @@ pn_gemv_rows_kernel(Args a)
                     pv[s * M + m] = o[m];
             }
             __builtin_amdgcn_sched_barrier(0);
-            load_next(ring[s]);
+            load_item(ring[s], lgc, lgr + s, s < lgn);
             __builtin_amdgcn_sched_barrier(0);
         }
         // tot[i] in DPP row q = the wave total of value i + q * V/4: item i/M + q * DEPTH/4,
@@ -469,11 +448,9 @@ pn_gemv_rows_kernel(Args a)
         transpose_reduce<V>(pv, tot);
 #pragma unroll
         for (int i = 0; i < V / 4; i++) {
-            const int s0 = i / M;
-            constexpr int ST = DEPTH / 4;
-            const int id = q == 0 ? idx[s0] : q == 1 ? idx[s0 + ST] : q == 2 ? idx[s0 + 2 * ST]
-                                                                            : idx[s0 + 3 * ST];
-            part[(lane & 15) == 0 && id >= 0 ? id + i % M : dummy + lane] = tot[i];
+            const int si = i / M + q * (DEPTH / 4);
+            const bool real = si < gn && (lane & 15) == 0;
+            part[real ? ((gr + si) * NC + gc) * M + i % M : dummy + lane] = tot[i];
         }
     }
 
@@ -498,7 +475,8 @@ namespace {
 // workgroup per CU; the register budget is 512 / (NW / 4) per lane).
 template <int TYPE, int M, int P> struct Cfg {
     static constexpr int DEPTH = P == 2 && M <= 2 ? 8 : 4;
-    static constexpr int NW = M >= 3 ? 8 : 12;
+    // pn3t 8-word pieces hold 80 x per lane: two waves per SIMD keep them without spills
+    static constexpr int NW = (TYPE == PN_TYPE_PN3T && P == 8) || M >= 3 ? 8 : 12;
 };
 
 template <int TYPE, int M, int P>
