@@ -197,9 +197,12 @@ def quantize_pn(pn, torch, dev, typ, w_np):
     return W
 
 
-def extra_workloads(pn, torch, dev, reps, warmup):
+EXTRA_PARTS = ("pn4t6144", "layer", "nvfp4", "fp8row")
+
+
+def extra_workloads(pn, torch, dev, reps, warmup, parts=EXTRA_PARTS):
     """The other measured configurations: per launch µs and weight-GB/s, weights rotated over
-    enough copies to exceed the 256 MB Infinity Cache."""
+    enough copies to exceed the 256 MB Infinity Cache. parts selects which of them run."""
     import numpy as np
     import synth
     stream = torch.cuda.current_stream()
@@ -212,6 +215,20 @@ def extra_workloads(pn, torch, dev, reps, warmup):
             len(Ws), reps, warmup)
         return {"us": round(us, 3), "GBs": round(Ws[0].numel() / us / 1e3, 1)}
 
+    if "pn4t6144" in parts:
+        extra_pn4t6144(pn, torch, dev, reps, warmup, out, pn_entry)
+    if "layer" in parts:
+        extra_layer(pn, torch, dev, reps, warmup, out, pn_entry, stream, sh)
+    if "nvfp4" in parts:
+        extra_nvfp4(pn, torch, dev, reps, warmup, out, stream, sh)
+    if "fp8row" in parts:
+        extra_fp8row(pn, torch, dev, reps, warmup, out, stream, sh)
+    return out
+
+
+def extra_pn4t6144(pn, torch, dev, reps, warmup, out, pn_entry):
+    import numpy as np
+    import synth
     # pn4t 5120 x 6144, Laplace(0, 0.015) with 0.1% outliers x8, M = 1, 32 copies
     N, K = 5120, 6144
     W0 = quantize_pn(pn, torch, dev, 125, synth.laplace_outlier_weights(201, 202, N, K, 0.015, 0.001, 8.0))
@@ -221,6 +238,11 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     out["pn4t_5120x6144_laplace_M1"] = pn_entry(125, N, K, Ws, 1, x, y)
     del Ws, W0
     log("[bench] extra: pn4t 5120x6144 done")
+
+
+def extra_layer(pn, torch, dev, reps, warmup, out, pn_entry, stream, sh):
+    import numpy as np
+    import synth
 
     # decoder-layer set at M = 1..4, 4 copies (679.6 MB). Every layer figure is one layer's launches
     # issued back to back with copy c of every matrix at layer c, so consecutive layers rotate over
@@ -321,6 +343,11 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     del mats, garr, ys
     log("[bench] extra: Hadamard done")
 
+
+def extra_nvfp4(pn, torch, dev, reps, warmup, out, stream, sh):
+    import numpy as np
+    import synth
+
     # NVFP4 17408 x 5120, clip-search quantized by the oracle (host threads), x bf16, M = 1..4,
     # 11 copies
     import oracle
@@ -334,13 +361,19 @@ def extra_workloads(pn, torch, dev, reps, warmup):
     C = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(10)]
     xb = torch.from_numpy(np.ascontiguousarray(synth.activations_bf16(502, 4, K)).view(np.int16)).to(dev)
     nbytes = codes.numel() + scales.numel() + 4
+    yn = torch.empty((4, N), dtype=torch.float32, device=dev)  # y of up to 4 tokens
     for M in (1, 2, 3, 4):
         us = time_launches(torch, stream, lambda c: check(pn.gemv_nvfp4_ptr(
-            C[c][0].data_ptr(), C[c][1].data_ptr(), gv, N, K, xb.data_ptr(), M, y.data_ptr(), sh),
+            C[c][0].data_ptr(), C[c][1].data_ptr(), gv, N, K, xb.data_ptr(), M, yn.data_ptr(), sh),
             "pn_gemv_nvfp4"), len(C), reps, warmup)
         out[f"nvfp4_17408x5120_M{M}"] = {"us": round(us, 3), "GBs": round(nbytes / us / 1e3, 1)}
     log("[bench] extra: nvfp4 done")
     del C, codes, scales
+
+
+def extra_fp8row(pn, torch, dev, reps, warmup, out, stream, sh):
+    import numpy as np
+    import synth
 
     # row-scaled E4M3 head, 248,320 x 5,120 (1.27 GB of codes per copy): seeded valid E4M3FN words
     # and positive bf16 multipliers, 2 copies, M = 1..4
@@ -363,7 +396,6 @@ def extra_workloads(pn, torch, dev, reps, warmup):
             "pn_gemv_fp8row"), len(H), max(10, reps // 10), max(2, warmup // 5))
         out[f"fp8row_head_248320x5120_M{M}"] = {"us": round(us, 2), "GBs": round(hbytes / us / 1e3, 1)}
     log("[bench] extra: fp8row head done")
-    return out
 
 
 def shard_shapes(pn, torch, dev, mats, reps, warmup):
@@ -462,6 +494,9 @@ def main():
                     help="skip the other measured configurations (pn4t 5120x6144, layer set at "
                          "M=1..4, the layer set with Hadamard-rotated x at M=1..4, NVFP4 at M=1..4, "
                          "row-scaled E4M3 head at M=1..4)")
+    ap.add_argument("--extra", default=",".join(EXTRA_PARTS),
+                    help="which other configurations run (comma list of " + ", ".join(EXTRA_PARTS) +
+                         "; the one-GPU shares of the MLP run with any of them)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -577,7 +612,11 @@ def main():
         "kernels": kern,
     }
     if not args.no_extra:
-        result["extra"] = extra_workloads(pn, torch, dev, args.steps, args.warmup)
+        parts = tuple(p for p in args.extra.split(",") if p)
+        bad = [p for p in parts if p not in EXTRA_PARTS]
+        if bad:
+            raise SystemExit(f"unknown --extra part(s): {bad}")
+        result["extra"] = extra_workloads(pn, torch, dev, args.steps, args.warmup, parts)
         result["extra"]["mlp_shard_M1"] = shard_shapes(pn, torch, dev, mats, args.steps,
                                                        args.warmup)
     if args.copy_mb > 0:
