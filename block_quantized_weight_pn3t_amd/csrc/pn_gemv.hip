@@ -1,7 +1,7 @@
 // pn_gemv.hip -- the PN GEMV entry points of the C ABI: argument checks and dispatch.
 //
 // "PN weight format" (PNX-FORMAT-v0), "Value": y[m, n] = sum_k d * (n_k - z) * x[m, k].
-//  * 1-4 tokens: the vector-unit kernels of pn_gemv_vec.hip (exact decode of every weight to the
+//  * 1-4 tokens: the row-stream kernel of pn_gemv_rows.hip (exact decode of every weight to the
 //    integer n - z, one fp32 fma per weight and token; no matrix cores: a matrix-vector product is
 //    not a dense contraction).
 //  * 5-16 tokens: the matrix-core kernels of pn_gemv_mfma.hip.
