@@ -28,12 +28,15 @@
 // Work split: a lane owns a "piece" of P consecutive words of one block (P = 8, 4 or 2); a wave
 // covers a chunk of 64 pieces (8P blocks) of a row per item and keeps that chunk's x in registers
 // (read from the workgroup's copy of x in LDS when its chunk changes). A workgroup (one per CU,
-// 8 waves) owns a contiguous range of rows; its items (chunk, row) are shared out over its waves
-// in chunk-major order, so a wave's x changes at most a few times. Each lane's words come straight
-// from HBM into registers through buffer loads, D items ahead of the decode. Per item the 64 lane
-// sums are added by DPP and permlane swaps; one lane writes the item's partial to LDS, and at the
-// end the workgroup adds each row's chunk partials in chunk order and writes y. No atomics: the
-// same inputs and launch shape give the same bits.
+// 8 or 12 waves) owns a contiguous range of rows; its items (chunk, row), chunk-major, form groups
+// of up to D rows of one chunk. Where a row is one chunk its waves take the groups one at a time
+// from a counter in LDS as they free up; otherwise each wave owns a contiguous run of them. Each
+// lane's words come straight from HBM into registers through buffer loads, one group ahead of the
+// decode. Per group the 64 lane sums of its items are added by DPP and permlane
+// swaps; one lane writes each item's partial to LDS, and at the end the workgroup adds each row's
+// chunk partials in chunk order and writes y. The partial of an item does not depend on the wave
+// that computes it, and nothing is added in arrival order: the same inputs and launch shape give
+// the same bits.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -264,7 +267,7 @@ __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint
 
 typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int TYPE, int M, int P, int DEPTH, int NW>
+template <int TYPE, int M, int P, int DEPTH, int NW, int PRE, bool DYN>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 pn_gemv_rows_kernel(Args a)
 {
@@ -282,13 +285,12 @@ pn_gemv_rows_kernel(Args a)
     const int r0 = (int)((int64_t)a.N * g / G), r1 = (int)((int64_t)a.N * (g + 1) / G);
     const int nr = r1 - r0;
     const int NC = a.NC;
-    const int I = NC * nr;  // items of the workgroup, chunk-major
-    const int it0 = (int)((int64_t)I * w / NW), it1 = (int)((int64_t)I * (w + 1) / NW);
     // x staged per token: whole chunks, each block of x in GS floats (zero past the slice)
     const int XT = NC * CB * D::GS;
     float *xl = lds;
     float *part = lds + M * XT;                    // [rows_max][NC][M]
     const int dummy = a.rows_max * NC * M;         // then 64 dummy slots
+    int *tickets = reinterpret_cast<int *>(part + dummy + 64);  // then the group counter
 
     // ---- lane constants
     Lane ln;
@@ -311,34 +313,58 @@ pn_gemv_rows_kernel(Args a)
     const Consts<TYPE> cst = make_consts<TYPE>();
     const uint32_t rstride = a.row_stride;
 
-    // ---- the wave's item sequence: its items (chunk-major) cut into one segment per chunk, each
-    // segment taken in groups of DEPTH items (the last group of a segment may hold fewer), so that
-    // a group never spans two chunks and x changes only between groups. Two cursors walk it one
-    // group at a time: one for the loads, a group ahead, and one for the decode.
+    // ---- groups: the items (row, chunk) of the workgroup, chunk-major, in groups of at most DEPTH
+    // rows of one chunk, so that x changes only between groups. Two ways to share them out:
+    //  * DYN (one token, rows of one chunk, at least three groups per wave): groups of DEPTH
+    //    rows; wave w takes group w first, and every further group goes to the wave that asks
+    //    next (a ticket counter in LDS), one group ahead of its decode. The SIMD's arbiter favours its older waves, so a fixed split would leave
+    //    the younger ones finishing alone; taking groups as they free up ends the waves of a
+    //    workgroup together.
+    //  * otherwise: each wave owns a contiguous run of the items, cut into one segment per chunk
+    //    and each segment into groups of DEPTH (the last may hold fewer), so that its x changes at
+    //    most a few times; a cursor walks it one group at a time, a group ahead of the decode.
+    // Either way the result of a group does not depend on the wave that takes it.
+    const int gpc = (nr + DEPTH - 1) / DEPTH;  // groups per chunk
+    const int NG = NC * gpc;
+    auto group_of = [&](int gi, int &c, int &r, int &cnt) {
+        c = gi < NG ? gi / gpc : 0;
+        r = gi < NG ? (gi - c * gpc) * DEPTH : 0;
+        cnt = gi < NG ? min(DEPTH, nr - r) : 0;
+    };
+    if (DYN && threadIdx.x == 0)
+        *tickets = 0;  // read only after the staging barrier
     struct Cur {
         int c, r;  // chunk and row (within the workgroup) of the next item
         int rem;   // items left in the current segment
-        int left;  // items left in the wave's range
+        int left;  // items left in the wave's run
     };
-    auto cur_init = [&](Cur &k) {
-        k.left = it1 - it0;
-        k.c = nr > 0 ? it0 / nr : 0;
-        k.r = it0 - k.c * nr;
-        k.rem = min(nr - k.r, k.left);
-    };
-    // the next group: its chunk, first row and number of items (0 past the end)
-    auto cur_group = [&](Cur &k, int &c, int &r, int &cnt) {
-        if (k.rem == 0 && k.left > 0) {
-            k.c++;
-            k.r = 0;
-            k.rem = min(nr, k.left);
+    Cur lcur;
+    {
+        const int I = NC * nr;
+        const int it0 = (int)((int64_t)I * w / NW), it1 = (int)((int64_t)I * (w + 1) / NW);
+        lcur.left = it1 - it0;
+        lcur.c = nr > 0 ? it0 / nr : 0;
+        lcur.r = it0 - lcur.c * nr;
+        lcur.rem = min(nr - lcur.r, lcur.left);
+    }
+    int tk = w;  // the next ticket (DYN)
+    // the next group: chunk, first row and number of items (0 past the end)
+    auto next_group = [&](int &c, int &r, int &cnt) {
+        if constexpr (DYN) {
+            group_of(tk, c, r, cnt);
+            return;
         }
-        c = k.c;
-        r = k.r;
-        cnt = min(DEPTH, k.rem);
-        k.r += cnt;
-        k.rem -= cnt;
-        k.left -= cnt;
+        if (lcur.rem == 0 && lcur.left > 0) {
+            lcur.c++;
+            lcur.r = 0;
+            lcur.rem = min(nr, lcur.left);
+        }
+        c = lcur.c;
+        r = lcur.r;
+        cnt = min(DEPTH, lcur.rem);
+        lcur.r += cnt;
+        lcur.rem -= cnt;
+        lcur.left -= cnt;
     };
 
     // ---- weight loads. Every slot is refilled unconditionally right after its item (a refill
@@ -352,8 +378,6 @@ pn_gemv_rows_kernel(Args a)
         load_slot<P>(rs, lastc ? ln.voffl : ln.voff, lastc ? ln.dvoffl : ln.dvoff,
                      (uint32_t)(r0 + r) * rstride + CBYTES * (uint32_t)c, sl);
     };
-    Cur lcur;
-    cur_init(lcur);
     int lgc = 0, lgr = 0, lgn = 0;  // the group being loaded
     // ---- x staging: the first pass of x loads goes out before the weight loads, so that waiting
     // for it waits for no weights; further passes (large M * K) wait for everything in flight
@@ -388,10 +412,13 @@ pn_gemv_rows_kernel(Args a)
     float4 xv0[XPT];
     stage_load(0, xv0);
 
+    // The first PRE items' weights go out before x is staged, the rest after: at 1-2 tokens the
+    // x of a workgroup would otherwise queue behind every wave's first group of weights in the
+    // memory system, and the barrier waits for the slowest wave's x.
     Slot<P> ring[DEPTH];
-    cur_group(lcur, lgc, lgr, lgn);
+    next_group(lgc, lgr, lgn);
 #pragma unroll
-    for (int s = 0; s < DEPTH; s++)
+    for (int s = 0; s < PRE; s++)
         load_item(ring[s], lgc, lgr + s, s < lgn);
 
     stage_store(0, xv0);
@@ -402,6 +429,9 @@ pn_gemv_rows_kernel(Args a)
     }
     // a plain barrier: __syncthreads() would also wait for the weight loads in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int s = PRE; s < DEPTH; s++)
+        load_item(ring[s], lgc, lgr + s, s < lgn);
 
     // ---- items: x of the current chunk in registers, DEPTH items in flight. The partials of a
     // group are summed over the wave together (one transposed reduction), and the first lane of
@@ -416,7 +446,15 @@ pn_gemv_rows_kernel(Args a)
         const int gc = lgc, gr = lgr, gn = lgn;  // this group (already loaded)
         if (gn == 0)
             break;
-        cur_group(lcur, lgc, lgr, lgn);          // the next group, loaded as this one is decoded
+        // the next group, loaded as this one is decoded. A ticket: all 64 lanes add one (one
+        // wave's adds are one LDS instruction), so the counter moves by 64 per ticket and the
+        // first lane's old value over 64 is the ticket; no branch around the atomic
+        if constexpr (DYN) {
+            const int t = __hip_atomic_fetch_add(tickets, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            tk = NW + (__builtin_amdgcn_readfirstlane(t) >> 6);
+        }
+        next_group(lgc, lgr, lgn);
         if (gc != xc) {
             xc = gc;
             dwid = xc * CB + ln.bl < a.nb ? 16u : 0u;
@@ -477,13 +515,28 @@ template <int TYPE, int M, int P> struct Cfg {
     static constexpr int DEPTH = P == 2 && M <= 2 ? 8 : 4;
     // pn3t 8-word pieces hold 80 x per lane: two waves per SIMD keep them without spills
     static constexpr int NW = (TYPE == PN_TYPE_PN3T && P == 8) || M >= 3 ? 8 : 12;
+    // items whose weights are requested before x is staged
+    static constexpr int PRE = M <= 2 ? 1 : DEPTH;
 };
 
 template <int TYPE, int M, int P>
 int launch_one(const rows::Args &a, int grid, size_t lds, hipStream_t s)
 {
     using C = Cfg<TYPE, M, P>;
-    constexpr auto kern = rows::pn_gemv_rows_kernel<TYPE, M, P, C::DEPTH, C::NW>;
+    // A counter hands out the groups at one token where rows are one chunk and every wave can
+    // expect at least three groups; otherwise each wave keeps its own run of items (with several
+    // chunks, so that it re-reads x only a few times; with few groups, so that no wave stands
+    // idle).
+    if constexpr (M == 1) {
+        if (a.NC == 1 && (a.rows_max + C::DEPTH - 1) / C::DEPTH >= 3 * C::NW) {
+            constexpr auto kd = rows::pn_gemv_rows_kernel<TYPE, M, P, C::DEPTH, C::NW, C::PRE, true>;
+            if (!lds_limit_once<kd>(rows::kLdsMax))
+                return PN_ERR_HIP;
+            hipLaunchKernelGGL(kd, dim3((unsigned)grid), dim3(64 * C::NW), lds, s, a);
+            return launch_status();
+        }
+    }
+    constexpr auto kern = rows::pn_gemv_rows_kernel<TYPE, M, P, C::DEPTH, C::NW, C::PRE, false>;
     if (!lds_limit_once<kern>(rows::kLdsMax))
         return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * C::NW), lds, s, a);
@@ -539,7 +592,7 @@ int launch_rows(const uint8_t *row0, int64_t N, int64_t row_stride, int64_t nb, 
     const size_t x_bytes = (size_t)M * NC * cb * D::GS * sizeof(float);
     const int cus = device_cus();
     // partials of a workgroup beside the staged x
-    const int64_t part_cap = ((int64_t)rows::kLdsMax - (int64_t)x_bytes) / (int64_t)sizeof(float) - 64;
+    const int64_t part_cap = ((int64_t)rows::kLdsMax - (int64_t)x_bytes) / (int64_t)sizeof(float) - 65;
     const int64_t rows_cap = part_cap / (NC * M);
     if (rows_cap < 1)
         return PN_ERR_SHAPE;
@@ -569,7 +622,7 @@ int launch_rows(const uint8_t *row0, int64_t N, int64_t row_stride, int64_t nb, 
         a.yinc = yinc;
         a.accumulate = accumulate ? 1 : 0;
         const size_t lds = std::max<size_t>(
-            rows::kLdsFloor, x_bytes + ((size_t)a.rows_max * NC * M + 64) * sizeof(float));
+            rows::kLdsFloor, x_bytes + ((size_t)a.rows_max * NC * M + 65) * sizeof(float));
         const int st = launch_p<TYPE, M>(P, a, grid, lds, s);
         if (st != PN_OK)
             return st;
