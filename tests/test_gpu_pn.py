@@ -363,6 +363,25 @@ def test_config3_stacked_gate_up_every_row(env):
     print("stacked gate+up worst err/bound", assert_within(y, y_ref, bound))
 
 
+@pytest.mark.parametrize("typ,N,K,offset", [(PN3T, 24613, 5120, 0), (PN3T, 24613, 5120, 2),
+                                             (PN4T, 36100, 4096, 0), (PN4T, 36101, 4096, 2)])
+def test_gemv_one_token_ticket_groups(env, typ, N, K, offset):
+    """One token on rows of one chunk (64 blocks) with enough rows per workgroup that its waves
+    take their groups of rows from a counter as they free up (at least 3 groups per wave on 256
+    compute units): ragged row counts, both alignments of W, every row against the oracle, and
+    the same bits on a second call. The rows repeat a 2048-row oracle-quantized matrix."""
+    pn, torch, dev = env
+    _, Wb = quantized(typ, 2048, K, 950 + typ)
+    W = np.ascontiguousarray(np.tile(Wb, ((N + 2047) // 2048, 1))[:N])
+    x = synth.activations(960 + typ, 1, K)
+    Wd = dev_bytes(torch, dev, W, offset)
+    y = run_gemv(pn, torch, dev, typ, Wd, N, K, x)
+    y2 = run_gemv(pn, torch, dev, typ, Wd, N, K, x)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    y_ref, bound = oracle.gemv(typ, W, N, K, x)
+    assert_within(y, y_ref, bound)
+
+
 # ---- config 4: the decoder-layer set at M = 1..4 -------------------------------------------------
 
 @pytest.mark.slow
