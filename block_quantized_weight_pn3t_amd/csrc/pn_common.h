@@ -26,6 +26,13 @@ template <> struct Fmt<PN_TYPE_PN4T> {
 
 constexpr int kBlockBytes = 34;
 
+// One matrix of a group of PN GEMVs that read the same x (host side).
+struct GroupPart {
+    const uint8_t *W;
+    int64_t N;
+    float *y;
+};
+
 // One PN block brought into registers without assuming 4-byte alignment of its words.
 // A block at byte address p (2-byte aligned) is read as 32 bytes from the 4-byte aligned address
 // q4 plus one 16-bit piece at q2:

@@ -16,6 +16,8 @@
 
 namespace pn {
 
+int launch_vec_group(int type, const GroupPart *gp, int count, int64_t K, const float *x,
+                     int64_t M, hipStream_t s);
 int launch_vec(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M,
                float *y, hipStream_t s);
 int launch_mfma(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int M, float *y,
@@ -70,6 +72,24 @@ static int check_group(const pn_gemv_part *parts, int count, int64_t K, const fl
 static int run_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int64_t M,
                      hipStream_t s)
 {
+    // parts of one type at 1-4 tokens: one launch where the shapes allow it
+    if (M <= 4) {
+        GroupPart gp[PN_GEMV_GROUP_MAX_PARTS];
+        int n = 0, type = -1;
+        bool same = true;
+        for (int i = 0; i < count; i++) {
+            if (parts[i].N == 0)
+                continue;
+            same = same && (type < 0 || parts[i].type == type);
+            type = parts[i].type;
+            gp[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y};
+        }
+        if (same && n >= 2) {
+            const int st = launch_vec_group(type, gp, n, K, x, M, s);
+            if (st != 1)
+                return st;
+        }
+    }
     for (int i = 0; i < count; i++) {
         const pn_gemv_part &p = parts[i];
         if (p.N == 0)

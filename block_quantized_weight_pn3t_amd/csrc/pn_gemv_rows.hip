@@ -69,6 +69,19 @@ template <> struct Dec<PN_TYPE_PN4T> {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// One matrix of a grouped launch (several matrices of one type and K that read the same x): its
+// workgroups are [g0, next part's g0), and it replaces base, nbytes, par, N, y and ystride.
+struct Part {
+    const uint8_t *base;
+    uint32_t nbytes;
+    uint32_t par;
+    int N;
+    int g0;
+    float *y;
+    int64_t ystride;
+};
+constexpr int kMaxParts = 4;
+
 struct Args {
     const uint8_t *base;  // 4-byte aligned start of the bytes this launch reads
     uint32_t nbytes;      // bytes from base the launch may read (a multiple of 4)
@@ -84,6 +97,8 @@ struct Args {
     int64_t ystride;
     int64_t yinc;
     int accumulate;       // add to y (later slices of K) instead of overwriting it
+    int nparts;           // 0: one matrix (the fields above); else parts[0..nparts)
+    Part parts[kMaxParts];
 };
 
 // One item's registers: the P + 1 aligned dwords of the lane's piece and (P < 8) the dword that
@@ -269,7 +284,7 @@ typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int TYPE, int M, int P, int DEPTH, int NW, int PRE, bool DYN>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-pn_gemv_rows_kernel(Args a)
+pn_gemv_rows_kernel(const Args a0)
 {
     using D = Dec<TYPE>;
     constexpr int PPB = 8 / P;   // pieces per block
@@ -281,7 +296,31 @@ pn_gemv_rows_kernel(Args a)
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = gridDim.x, g = blockIdx.x;
+    // a grouped launch: this workgroup's matrix (uniform; no indexing of the argument array)
+    Args a = a0;
+    int G = gridDim.x, g = blockIdx.x;
+    if (a0.nparts > 0) {
+        int pi = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxParts; i++)
+            pi = i < a0.nparts && g >= a0.parts[i].g0 ? i : pi;
+        Part pt = a0.parts[0];
+        int gend = a0.nparts > 1 ? a0.parts[1].g0 : G;
+#pragma unroll
+        for (int i = 1; i < kMaxParts; i++)
+            if (i == pi) {
+                pt = a0.parts[i];
+                gend = i + 1 < a0.nparts ? a0.parts[i + 1 < kMaxParts ? i + 1 : i].g0 : G;
+            }
+        a.base = pt.base;
+        a.nbytes = pt.nbytes;
+        a.par = pt.par;
+        a.N = pt.N;
+        a.y = pt.y;
+        a.ystride = pt.ystride;
+        g -= pt.g0;
+        G = gend - pt.g0;
+    }
     const int r0 = (int)((int64_t)a.N * g / G), r1 = (int)((int64_t)a.N * (g + 1) / G);
     const int nr = r1 - r0;
     const int NC = a.NC;
@@ -621,6 +660,7 @@ int launch_rows(const uint8_t *row0, int64_t N, int64_t row_stride, int64_t nb, 
         a.ystride = ystride;
         a.yinc = yinc;
         a.accumulate = accumulate ? 1 : 0;
+        a.nparts = 0;
         const size_t lds = std::max<size_t>(
             rows::kLdsFloor, x_bytes + ((size_t)a.rows_max * NC * M + 65) * sizeof(float));
         const int st = launch_p<TYPE, M>(P, a, grid, lds, s);
@@ -678,7 +718,117 @@ int launch_m(const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, 
     }
 }
 
+// Several matrices of one type and K that read the same x, as one launch: the workgroups are dealt
+// to the parts in proportion to their rows (at least one each), each part's rows split over its
+// own workgroups as in a launch of its own. Only where every part is one launch of one alignment
+// class (whole rows of x fit the LDS, row bytes a multiple of 4, 31-bit offsets) and the rows of a
+// workgroup fit its partials; otherwise returns 1 and the caller launches the parts one by one.
+template <int TYPE, int M>
+int launch_group_typed(const GroupPart *gp, int count, int64_t K, const float *x, hipStream_t s)
+{
+    using D = rows::Dec<TYPE>;
+    const int64_t nb = K / D::G;
+    const int64_t rb = nb * kBlockBytes;
+    if (count < 2 || count > rows::kMaxParts || (rb & 2))
+        return 1;
+    int P = choose_p<TYPE, M>(nb);
+    if (const char *e = getenv("PN_GEMV_PIECE")) {
+        const int f = atoi(e);
+        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
+            P = f;
+    }
+    const int64_t cb = 8 * P, NC = (nb + cb - 1) / cb;
+    const size_t x_bytes = (size_t)M * NC * cb * D::GS * sizeof(float);
+    if (x_bytes > (size_t)rows::kXLdsMax)
+        return 1;
+    int64_t total = 0;
+    for (int i = 0; i < count; i++) {
+        if (gp[i].N <= 0 || gp[i].N * rb > (int64_t)0x7FFF0000)
+            return 1;
+        total += gp[i].N;
+    }
+    const int cus = device_cus();
+    const int grid = (int)std::min<int64_t>(cus, total);
+    if (grid < count)
+        return 1;
+    // workgroups per part: proportional to rows, at least one, at most the part's rows
+    int gcount[rows::kMaxParts];
+    int used = 0;
+    for (int i = 0; i < count; i++) {
+        gcount[i] = (int)std::max<int64_t>(1, std::min<int64_t>(gp[i].N, gp[i].N * grid / total));
+        used += gcount[i];
+    }
+    for (int i = 0; used < grid; i = (i + 1) % count)
+        if (gcount[i] < gp[i].N) {
+            gcount[i]++;
+            used++;
+        }
+    for (int i = 0; used > grid; i = (i + 1) % count)
+        if (gcount[i] > 1) {
+            gcount[i]--;
+            used--;
+        }
+    const int64_t part_cap = ((int64_t)rows::kLdsMax - (int64_t)x_bytes) / (int64_t)sizeof(float) - 65;
+    rows::Args a{};
+    int64_t rows_max = 0;
+    int g0 = 0;
+    for (int i = 0; i < count; i++) {
+        const uintptr_t fa = reinterpret_cast<uintptr_t>(gp[i].W);
+        rows::Part &pt = a.parts[i];
+        pt.par = (uint32_t)(fa & 3u);
+        pt.base = gp[i].W - pt.par;
+        pt.nbytes = (uint32_t)(((int64_t)pt.par + gp[i].N * rb + 3) & ~(int64_t)3);
+        pt.N = (int)gp[i].N;
+        pt.g0 = g0;
+        pt.y = gp[i].y;
+        pt.ystride = gp[i].N;
+        g0 += gcount[i];
+        rows_max = std::max<int64_t>(rows_max, (gp[i].N + gcount[i] - 1) / gcount[i]);
+    }
+    if (rows_max * NC * M > part_cap)
+        return 1;
+    a.nparts = count;
+    a.base = a.parts[0].base;
+    a.nbytes = a.parts[0].nbytes;
+    a.par = a.parts[0].par;
+    a.N = a.parts[0].N;
+    a.y = a.parts[0].y;
+    a.ystride = a.parts[0].ystride;
+    a.row_stride = (uint32_t)rb;
+    a.nb = (int)nb;
+    a.NC = (int)NC;
+    a.rows_max = (int)rows_max;
+    a.x = x;
+    a.xstride = K;
+    a.yinc = 1;
+    a.accumulate = 0;
+    const size_t lds = std::max<size_t>(
+        rows::kLdsFloor, x_bytes + ((size_t)rows_max * NC * M + 65) * sizeof(float));
+    return launch_p<TYPE, M>(P, a, grid, lds, s);
+}
+
+template <int TYPE>
+int launch_group_m(const GroupPart *gp, int count, int64_t K, const float *x, int64_t M,
+                   hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_group_typed<TYPE, 1>(gp, count, K, x, s);
+    case 2: return launch_group_typed<TYPE, 2>(gp, count, K, x, s);
+    case 3: return launch_group_typed<TYPE, 3>(gp, count, K, x, s);
+    default: return launch_group_typed<TYPE, 4>(gp, count, K, x, s);
+    }
+}
+
 }  // namespace
+
+// Several PN GEMVs of one type and K over the same x at 1 <= M <= 4 as one launch (arguments
+// already checked): PN_OK, an error, or 1 where the parts must run as launches of their own.
+int launch_vec_group(int type, const GroupPart *gp, int count, int64_t K, const float *x,
+                     int64_t M, hipStream_t s)
+{
+    return type == PN_TYPE_PN3T ? launch_group_m<PN_TYPE_PN3T>(gp, count, K, x, M, s)
+                                : launch_group_m<PN_TYPE_PN4T>(gp, count, K, x, M, s);
+}
 
 // The vector-unit PN GEMV for 1 <= M <= 4 (arguments already checked by the entry point).
 int launch_vec(int type, const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M,
