@@ -105,9 +105,10 @@ int pn_dequantize_row(int type, const void *row, int64_t K, float *out, void *st
 int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
             void *stream);
 
-/* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up): one pn_gemv per part,
- * in order on the stream, parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], with the bits of
- * those separate calls. 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part has
+/* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up):
+ * parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], with the bits of one pn_gemv per part. At
+ * 1-4 tokens the parts of one type run as one launch where the shapes allow it (the others as
+ * launches of their own, in order on the stream). 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part has
  * its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument errors
  * as pn_gemv, for the first part that has one; parts with N = 0 are skipped. The parts' y must not
  * overlap each other or x. */
