@@ -200,45 +200,6 @@ inline RowSplit row_split(int64_t N, int grid)
     return RowSplit{N / S, (int)(N % S)};
 }
 
-// ---- E4M3FN words (NInfer "tensor formats", section 3.3) in double ----------------------------
-
-__device__ __forceinline__ double e4m3_f64(uint32_t c)
-{
-    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-    double v;
-    if (e == 0)
-        v = (double)m * 0x1p-9;
-    else if (e == 15 && m == 7)
-        v = __builtin_nan("");
-    else
-        v = __longlong_as_double((int64_t)((uint64_t)(e - 7 + 1023) << 52 | (uint64_t)m << 49));
-    return (c & 0x80u) ? -v : v;
-}
-
-// non-negative double -> E4M3FN word, nearest even, saturating at 448 (0x7E)
-__device__ __forceinline__ uint32_t f64_to_e4m3_sat(double v)
-{
-    if (!(v > 0.0))
-        return 0;
-    if (v >= 448.0)
-        return 0x7E;
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    int e = (int)(u >> 52) - 1023;
-    if (e < -6)
-        return (uint32_t)__builtin_rint(v * 512.0);  // subnormal quantum 2^-9 (8 -> 0x08)
-    const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-    uint64_t q = sig >> 49;
-    const uint64_t rem = sig & ((1ull << 49) - 1), half = 1ull << 48;
-    if (rem > half || (rem == half && (q & 1)))
-        q++;
-    if (q == 16) {
-        q = 8;
-        e++;
-    }
-    const uint32_t code = (uint32_t)((e + 7) << 3) | (uint32_t)(q - 8);
-    return code > 0x7Eu ? 0x7Eu : code;
-}
-
 // Host side --------------------------------------------------------------------------------------
 
 // Checks that the current device is gfx950 (cached per device). Returns PN_OK, PN_ERR_HIP or
