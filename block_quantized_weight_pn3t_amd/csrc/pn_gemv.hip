@@ -72,27 +72,33 @@ static int check_group(const pn_gemv_part *parts, int count, int64_t K, const fl
 static int run_group(const pn_gemv_part *parts, int count, int64_t K, const float *x, int64_t M,
                      hipStream_t s)
 {
-    // parts of one type at 1-4 tokens: one launch where the shapes allow it
+    // at 1-4 tokens the parts of each type run as one launch where the shapes allow it (the
+    // parts' outputs are independent, so the order of the launches does not matter)
+    bool done[PN_GEMV_GROUP_MAX_PARTS] = {};
     if (M <= 4) {
-        GroupPart gp[PN_GEMV_GROUP_MAX_PARTS];
-        int n = 0, type = -1;
-        bool same = true;
-        for (int i = 0; i < count; i++) {
-            if (parts[i].N == 0)
+        for (int type : {PN_TYPE_PN3T, PN_TYPE_PN4T}) {
+            GroupPart gp[PN_GEMV_GROUP_MAX_PARTS];
+            int idx[PN_GEMV_GROUP_MAX_PARTS];
+            int n = 0;
+            for (int i = 0; i < count; i++)
+                if (parts[i].N > 0 && parts[i].type == type) {
+                    idx[n] = i;
+                    gp[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y};
+                }
+            if (n < 2)
                 continue;
-            same = same && (type < 0 || parts[i].type == type);
-            type = parts[i].type;
-            gp[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y};
-        }
-        if (same && n >= 2) {
             const int st = launch_vec_group(type, gp, n, K, x, M, s);
-            if (st != 1)
+            if (st == 1)
+                continue;  // shapes it cannot group: one launch per part below
+            if (st != PN_OK)
                 return st;
+            for (int j = 0; j < n; j++)
+                done[idx[j]] = true;
         }
     }
     for (int i = 0; i < count; i++) {
         const pn_gemv_part &p = parts[i];
-        if (p.N == 0)
+        if (p.N == 0 || done[i])
             continue;
         const int st = dispatch(p.type, (const uint8_t *)p.W, p.N, K, x, M, p.y, s);
         if (st != PN_OK)
