@@ -107,15 +107,61 @@ static int run_group(const pn_gemv_part *parts, int count, int64_t K, const floa
     return PN_OK;
 }
 
+// The stream-ordered temporaries of the rotated-x calls come from a memory pool of the library's
+// own per device that keeps what is freed (release threshold at its maximum): after the first
+// call the allocation is a reuse inside the pool, not a trip to the system, which the device's
+// default pool (threshold 0) makes on every call. Each device keeps up to its largest temporary
+// for the life of the process. Under stream capture the default pool's allocation is used, which
+// a graph records as its own allocation node.
+constexpr int kMaxPoolDevices = 64;
+static std::atomic<hipMemPool_t> g_pool[kMaxPoolDevices];
+static std::mutex g_pool_mu;
+
+static hipMemPool_t temp_pool()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxPoolDevices)
+        return nullptr;
+    hipMemPool_t p = g_pool[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    p = g_pool[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        uint64_t keep = ~0ull;
+        if (hipMemPoolCreate(&p, &props) != hipSuccess || !p ||
+            hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_pool[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 // x' = the rotation of x[M, K] in a stream-ordered temporary, then f(x'); the temporary is
 // released on the same stream after f's launches.
 template <typename F>
 static int with_rotated(const float *x, int64_t M, int64_t K, int64_t B, hipStream_t s, F f)
 {
+    const size_t bytes = (size_t)(M * K) * sizeof(float);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        return PN_ERR_HIP;
+    }
+    hipMemPool_t pool = nullptr;
+    if (cap == hipStreamCaptureStatusNone && !(pool = temp_pool()))
+        return PN_ERR_HIP;
     float *xr = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void **>(&xr), (size_t)(M * K) * sizeof(float), s) !=
-            hipSuccess ||
-        !xr) {
+    const hipError_t e = pool ? hipMallocFromPoolAsync(reinterpret_cast<void **>(&xr), bytes, pool, s)
+                              : hipMallocAsync(reinterpret_cast<void **>(&xr), bytes, s);
+    if (e != hipSuccess || !xr) {
         (void)hipGetLastError();
         return PN_ERR_HIP;
     }

@@ -137,8 +137,10 @@ int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, const float *
 int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out, void *stream);
 
 /* y = W x' for M = 1..4 tokens: the rotation of pn_hadamard_rows into a stream-ordered temporary
- * (hipMallocAsync on the stream, released with hipFreeAsync after the GEMV's launches; x itself is
- * not modified), then pn_gemv on it: the same bits as those two calls made by hand, the rotation's
+ * (allocated on the stream from a memory pool the library creates per device, which keeps what is
+ * freed, so each device holds up to its largest temporary for the life of the process; under
+ * stream capture, hipMallocAsync from the device's default pool; released with hipFreeAsync after
+ * the GEMV's launches; x itself is not modified), then pn_gemv on it: the same bits as those two calls made by hand, the rotation's
  * error above adding to the GEMV's. Arguments as pn_gemv, plus B as in pn_hadamard_rows; M outside
  * 0..4 gives PN_ERR_TOKENS, a failed allocation PN_ERR_HIP. */
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
