@@ -39,7 +39,6 @@
 // (W 4-byte aligned, rows of a multiple of 4 blocks), the other reads each lane's bytes directly
 // (any 2-byte aligned W and block count).
 #include "pn_common.h"
-#include "pn_hadamard.h"
 
 namespace pn {
 
@@ -370,10 +369,7 @@ __device__ __forceinline__ void mfma_read_a(MfmaA &a, const uint8_t *blk, int g,
 // per k-step covers both; K-split (up to 16 tokens): hi and lo are two A operands on the same
 // codes. `after_loads` runs once the first x loads are issued (a caller's weight prefetch: loads
 // retire in order, so waiting for x then leaves the prefetch in flight).
-// LX: x comes from LDS instead (fp32 [M][K] at the start of the x area, the rotated x), 4 units
-// per thread: every unit is read before the area is overwritten (one pass of at most 2048 units;
-// the caller ensures it).
-template <int TYPE, bool SLOT, int EG, class F, bool LX = false>
+template <int TYPE, bool SLOT, int EG, class F>
 __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t K, int M,
                                            int ML, int pb0, int npb, int xvec4, F after_loads)
 {
@@ -381,7 +377,7 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
     constexpr int PERG = T::PERG;
     const int tid = threadIdx.x;
     const int per_block = mfma_block_bytes<TYPE>(ML), e_off = mfma_a_bytes<TYPE>(ML);
-    constexpr int UNITS = LX ? 4 : kMfmaUnits;  // units per thread and pass
+    constexpr int UNITS = kMfmaUnits;  // units per thread and pass
     const int U = npb * M * 4;
     const int nch = (U + kMfmaThreads * UNITS - 1) / (kMfmaThreads * UNITS);
     // unit u: k-group u % 4, then the block within its group of EG, then the token, then the group
@@ -391,8 +387,7 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
         m = w % M;
         brel = EG * (w / M) + bi;
     };
-    if constexpr (!LX)
-        __syncthreads();  // earlier readers of the x area are done (LX: the caller synchronised)
+    __syncthreads();  // earlier readers of the x area are done
     // x is a restrict kernel argument, so its loads may otherwise move past the prefetch below;
     // through an opaque copy of the address they stay in program order
     uint64_t xaddr = reinterpret_cast<uint64_t>(x);
@@ -407,21 +402,7 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
             const int u = min((c * UNITS + ub) * kMfmaThreads + tid, U - 1);
             int gg, m, brel;
             unit_coords(u, gg, m, brel);
-            if constexpr (LX) {
-                typedef __attribute__((address_space(3))) const mf_f4 lds_f4_t;
-                lds_f4_t *src = reinterpret_cast<lds_f4_t *>(
-                    (const lds_f32 *)(const float *)xa +
-                    ((int64_t)m * K + (int64_t)(pb0 + brel) * T::G + PERG * gg));
-#pragma unroll
-                for (int q = 0; q < PERG / 4; q++) {
-                    const mf_f4 f = src[q];
-                    xr[ub][4 * q] = f.x; xr[ub][4 * q + 1] = f.y;
-                    xr[ub][4 * q + 2] = f.z; xr[ub][4 * q + 3] = f.w;
-                }
-            } else {
-                mfma_load_unit<TYPE>(xg, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4,
-                                     xr[ub]);
-            }
+            mfma_load_unit<TYPE>(xg, K, m, (int64_t)(pb0 + brel) * T::G + PERG * gg, xvec4, xr[ub]);
         }
     };
     auto convert = [&](int c) {
@@ -480,20 +461,13 @@ __device__ __forceinline__ void mfma_stage(uint8_t *xa, const float *x, int64_t 
             }
     };
     load(0);
-    if constexpr (LX) {
-        // every read of the fp32 x is done before any thread overwrites the area (a barrier on
-        // LDS traffic only: the weight copies in flight need not land)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        convert(0);
-    } else {
-        asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
-        after_loads();
-        asm volatile("" ::: "memory");
-        convert(0);
-        for (int c = 1; c < nch; c++) {
-            load(c);
-            convert(c);
-        }
+    asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
+    after_loads();
+    asm volatile("" ::: "memory");
+    convert(0);
+    for (int c = 1; c < nch; c++) {
+        load(c);
+        convert(c);
     }
     const int used = SLOT ? 2 * M : M;
     for (int i = tid; i < npb * 16; i += kMfmaThreads)
@@ -646,15 +620,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // MC: the token capacity of the x layout (2, 4, 8 or 16; M <= MC), so that every LDS offset of
 // the loop is a constant. Up to 8, hi and lo are token slots.
-// ROT (3-4 tokens, one phase of x, one chunk of staging units, slices of at most 1024): x is
-// first rotated, x' = H_B x / sqrt(B) on slices of B = 2^hL elements (the Hadamard rotation of
-// "Files that use PN", as read in pn_hadamard.h), in registers while the first weight copies are
-// in flight, and written as fp32 to the x area, which the staging then reads.
-template <int TYPE, int TG, int MC, bool ROT>
+template <int TYPE, int TG, int MC>
 __device__ __forceinline__ void
 mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
               const float *__restrict__ x, int64_t K, int M, float *__restrict__ y, int64_t rq,
-              int rr, int Pb, int nph, int xvec4, int hL, float hscale, int blk_id){
+              int rr, int Pb, int nph, int xvec4, int blk_id){
     constexpr bool SLOT = MC <= 8;
     constexpr int ACC = SLOT ? 2 : 4;       // tokens per lane
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -727,72 +697,11 @@ mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_byte
                 }
                 ++pf;
             };
-            if constexpr (ROT) {
-                // x of the M tokens as float4 per lane: thread (wave w, lane l) takes, for
-                // u = 4 g + j, the float4 at 256 (w + 8 g) + 64 j + l, so a wave holds whole
-                // 1024-element pieces and stages 0-9 of the rotation stay in registers
-                constexpr int HQ = 12;  // M K <= 24576 elements (checked on the host)
-                const int total4 = (int)(M * K / 4), nh = 4 * ((total4 + 2047) >> 11);
-                auto hpos = [&](int u) { return 256 * (wave + 8 * (u >> 2)) + 64 * (u & 3) + lane; };
-                // the previous group's partial sums (which alias the x area and may reach into
-                // the slots) are read; no weight copy is in flight here
-                __syncthreads();
-                // through an opaque copy of the address the x loads stay before the prefetch
-                uint64_t xaddr = reinterpret_cast<uint64_t>(x);
-                asm volatile("" : "+s"(xaddr));
-                typedef __attribute__((address_space(1))) const mf_f4 g_f4_t;
-                gfloat_t *xg = reinterpret_cast<gfloat_t *>(xaddr);
-                // every load unconditional (past the end: the last float4 again, never written
-                // back), one branch on the alignment around them all: loads in branches of their
-                // own get waited for one by one where the branches join
-                float4 hv[HQ];
-                if (xvec4) {
-#pragma unroll
-                    for (int u = 0; u < HQ; u++) {
-                        const mf_f4 f = reinterpret_cast<g_f4_t *>(xg)[min(hpos(u), total4 - 1)];
-                        hv[u] = make_float4(f.x, f.y, f.z, f.w);
-                    }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < HQ; u++) {
-                        const int q = min(hpos(u), total4 - 1);
-                        hv[u] = make_float4(xg[4 * q], xg[4 * q + 1], xg[4 * q + 2], xg[4 * q + 3]);
-                    }
-                }
-                asm volatile("" ::: "memory");  // the x loads are issued before the prefetch
+            mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
 #pragma unroll
                 for (int s = 0; s < kStepsAhead; s++)
                     issue_next();
-                asm volatile("" ::: "memory");
-#pragma unroll
-                for (int g0 = 0; g0 < HQ; g0 += 4)
-                    if (g0 < nh) {  // uniform
-                        float4(&v4)[4] = *reinterpret_cast<float4(*)[4]>(&hv[g0]);
-                        hadamard_wave_n<4>(v4, hL, hscale);
-                        hadamard_regs_8_9(v4, hL, hscale);
-                    }
-                lds_f32 *xf = (lds_f32 *)(float *)xa;
-#pragma unroll
-                for (int u = 0; u < HQ; u++) {
-                    const int q = hpos(u);
-                    if (u < nh && q < total4) {
-                        xf[4 * q + 0] = hv[u].x;
-                        xf[4 * q + 1] = hv[u].y;
-                        xf[4 * q + 2] = hv[u].z;
-                        xf[4 * q + 3] = hv[u].w;
-                    }
-                }
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                auto none = [] {};
-                mfma_stage<TYPE, SLOT, kChunkBlocks, decltype(none), true>(xa, x, K, M, MC, pb0,
-                                                                           npb, xvec4, none);
-            } else {
-                mfma_stage<TYPE, SLOT, kChunkBlocks>(xa, x, K, M, MC, pb0, npb, xvec4, [&] {
-#pragma unroll
-                    for (int s = 0; s < kStepsAhead; s++)
-                        issue_next();
-                });
-            }
+            });
 #pragma unroll
             for (int t = 0; t < TG; t++) {
                 const int lo = max(i0, t * n4), hi = min(i1, (t + 1) * n4);
@@ -887,14 +796,14 @@ mfma_lds_body(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_byte
         }
     }
 }
-template <int TYPE, int TG, int MC, bool ROT = false>
+template <int TYPE, int TG, int MC>
 __global__ void __launch_bounds__(kMfmaThreads)
 pn_gemv_mfma_lds_kernel(const uint8_t *__restrict__ W, int64_t N, int nb, int64_t row_bytes,
                         const float *__restrict__ x, int64_t K, int M, float *__restrict__ y,
-                        int64_t rq, int rr, int Pb, int nph, int xvec4, int hL, float hscale)
+                        int64_t rq, int rr, int Pb, int nph, int xvec4)
 {
-    mfma_lds_body<TYPE, TG, MC, ROT>(W, N, nb, row_bytes, x, K, M, y, rq, rr, Pb, nph, xvec4, hL,
-                                     hscale, (int)blockIdx.x);
+    mfma_lds_body<TYPE, TG, MC>(W, N, nb, row_bytes, x, K, M, y, rq, rr, Pb, nph, xvec4,
+                                (int)blockIdx.x);
 }
 
 // LDS for the x of a phase and, aliased, the 8 waves' partial sums (8 KB per tile of the group).
@@ -915,24 +824,23 @@ static int launch_mfma_tg(const uint8_t *W, int64_t N, int nb, const float *x, i
     return launch_status();
 }
 
-template <int TYPE, int TG, int MC, bool ROT = false>
+template <int TYPE, int TG, int MC>
 static int launch_mfma_lds_tg(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K,
                               int M, float *y, int64_t rq, int rr, int grid, int Pb, int nph,
-                              size_t lds, hipStream_t s, int hL = 0, float hscale = 1.0f)
+                              size_t lds, hipStream_t s)
 {
-    constexpr auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC, ROT>;
+    constexpr auto kern = pn_gemv_mfma_lds_kernel<TYPE, TG, MC>;
     if (!lds_limit_once<kern>(kMfmaLds))
         return PN_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaThreads), lds, s, W, N, nb,
                        (int64_t)nb * kBlockBytes, x, K, M, y, rq, rr, Pb, nph,
-                       aligned(x, 16) ? 1 : 0, hL, hscale);
+                       aligned(x, 16) ? 1 : 0);
     return launch_status();
 }
 
-template <int TYPE, int MC, bool ROT = false>
+template <int TYPE, int MC>
 static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x, int64_t K, int M,
-                             float *y, int grid, int64_t rq, int rr, hipStream_t s, int hL = 0,
-                             float hscale = 1.0f)
+                             float *y, int grid, int64_t rq, int rr, hipStream_t s)
 {
     // tiles of 16 rows per group
     constexpr int max_tg = kMfmaMaxTG;
@@ -950,8 +858,8 @@ static int launch_mfma_lds_t(const uint8_t *W, int64_t N, int nb, const float *x
 #define PN_MFMA_CASE(tg)                                                                           \
     case tg:                                                                                       \
         if constexpr (tg <= max_tg)                                                                \
-            return launch_mfma_lds_tg<TYPE, tg, MC, ROT>(W, N, nb, x, K, M, y, rq, rr, grid, Pb,  \
-                                                           nph, lds, s, hL, hscale);               \
+            return launch_mfma_lds_tg<TYPE, tg, MC>(W, N, nb, x, K, M, y, rq, rr, grid, Pb, nph, \
+                                                      lds, s);                                 \
         else                                                                                       \
             return PN_ERR_SHAPE;
     PN_MFMA_CASE(1) PN_MFMA_CASE(2) PN_MFMA_CASE(3) PN_MFMA_CASE(4) PN_MFMA_CASE(5)

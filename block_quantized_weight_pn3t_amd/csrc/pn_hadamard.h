@@ -1,5 +1,4 @@
-// pn_hadamard.h -- Hadamard rotation of the activations, as device code shared by the standalone
-// rotation kernel and the GEMV kernels that fuse it into their x staging.
+// pn_hadamard.h -- Hadamard rotation of the activations: the device code of the rotation kernel.
 //
 // "PN weight format", section "Files that use PN": the model rotates the activations that reach the
 // PN weights with a Hadamard transform, performed by the engine; the page gives neither the order
@@ -126,73 +125,6 @@ __device__ __forceinline__ void hadamard_wave(float4 &v, int L, float scale)
         v.y *= scale;
         v.z *= scale;
         v.w *= scale;
-    }
-}
-
-// The same stages on N float4 at once, stage by stage, with no branch between them: the
-// compiler issues every lane exchange of a stage together and waits once (a per-float4 order
-// leaves a chain of dependent exchanges on the critical path).
-template <int N>
-__device__ __forceinline__ void hadamard_wave_n(float4 (&v)[N], int L, float scale)
-{
-    const unsigned lane = __lane_id();
-    if (L >= 1) {
-#pragma unroll
-        for (int u = 0; u < N; u++) {
-            const float a = v[u].x + v[u].y, b = v[u].x - v[u].y;
-            const float c = v[u].z + v[u].w, d = v[u].z - v[u].w;
-            v[u] = make_float4(a, b, c, d);
-        }
-    }
-    if (L >= 2) {
-#pragma unroll
-        for (int u = 0; u < N; u++) {
-            const float a = v[u].x + v[u].z, c = v[u].x - v[u].z;
-            const float b = v[u].y + v[u].w, d = v[u].y - v[u].w;
-            v[u] = make_float4(a, b, c, d);
-        }
-    }
-#define PN_HX_STAGE(LMIN, MASK)                                                                    \
-    if (L >= LMIN) {                                                                               \
-        _Pragma("unroll") for (int u = 0; u < N; u++) hx_lane_stage<MASK>(v[u], lane & MASK);      \
-    }
-    PN_HX_STAGE(3, 1)
-    PN_HX_STAGE(4, 2)
-    PN_HX_STAGE(5, 4)
-    PN_HX_STAGE(6, 8)
-    PN_HX_STAGE(7, 16)
-    PN_HX_STAGE(8, 32)
-#undef PN_HX_STAGE
-    if (L <= 8) {
-#pragma unroll
-        for (int u = 0; u < N; u++)
-            v[u] = make_float4(v[u].x * scale, v[u].y * scale, v[u].z * scale, v[u].w * scale);
-    }
-}
-
-// Stages 8 and 9 (where L >= 9, 10) on four float4 of a lane that sit 256 elements apart
-// (v[j] holds elements 4 lane + 256 j .. + 3 of a 1024-element piece of x), then the scaling
-// where L is 9 or 10. Same butterflies, in the same order, as the LDS pass would run.
-__device__ __forceinline__ void hadamard_regs_8_9(float4 (&v)[4], int L, float scale)
-{
-    auto bfly = [](float4 &lo, float4 &hi) {
-        const float4 a = make_float4(lo.x + hi.x, lo.y + hi.y, lo.z + hi.z, lo.w + hi.w);
-        const float4 b = make_float4(lo.x - hi.x, lo.y - hi.y, lo.z - hi.z, lo.w - hi.w);
-        lo = a;
-        hi = b;
-    };
-    if (L >= 9) {
-        bfly(v[0], v[1]);
-        bfly(v[2], v[3]);
-    }
-    if (L >= 10) {
-        bfly(v[0], v[2]);
-        bfly(v[1], v[3]);
-    }
-    if (L == 9 || L == 10) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            v[j] = make_float4(v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale);
     }
 }
 
