@@ -23,16 +23,18 @@ def env():
     return pn, torch, torch.device("cuda:0")
 
 
-def run_group(pn, torch, dev, K, parts, x, x_offset=0):
-    """parts: [(type, W bytes, N)] -> list of y (numpy), one pn_gemv_group call."""
+def run_group(pn, torch, dev, K, parts, x, x_offset=0, w_offsets=None):
+    """parts: [(type, W bytes, N)] -> list of y (numpy), one pn_gemv_group call; w_offsets: a byte
+    offset (0 or 2) per part for where its W starts in its buffer."""
     M = x.shape[0]
     buf = torch.zeros(M * K + x_offset, dtype=torch.float32, device=dev)
     xd = buf[x_offset:x_offset + M * K].view(M, K)
     xd.copy_(torch.from_numpy(np.ascontiguousarray(x, np.float32)))
     ys, args = [], []
-    for typ, W, N in parts:
+    for j, (typ, W, N) in enumerate(parts):
         yd = torch.full((M, max(N, 1)), float("nan"), dtype=torch.float32, device=dev)
-        Wd = dev_bytes(torch, dev, W) if N else torch.zeros(1, dtype=torch.uint8, device=dev)
+        off = w_offsets[j] if w_offsets else 0
+        Wd = dev_bytes(torch, dev, W, off) if N else torch.zeros(1, dtype=torch.uint8, device=dev)
         ys.append(yd)
         args.append((typ, Wd, N, yd))
     pn.gemv_group(args, K, xd, M=M)
@@ -94,6 +96,33 @@ def test_group_x_unaligned_and_separate_calls(env, M):
         assert np.array_equal(ya.view(np.uint32), y1.view(np.uint32))
         y_ref, bound = oracle.gemv(typ, W, N, K, x)
         assert_within(ya, y_ref, bound)
+
+
+# the cases above, and one whose pn4t rows hold an odd block count (15 blocks: rows of two
+# alignments, which the parts of that type take as launches of their own)
+BITS_CASES = CASES + [(960, [(PN3T, 50), (PN3T, 31), (PN4T, 40), (PN4T, 3)])]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("case", range(len(BITS_CASES)))
+def test_group_same_bits_as_separate_calls(env, case, M):
+    """Every case at 1-4 tokens, the parts' W at alternating 4-byte alignments (+0, +2 bytes): the
+    group gives the bits of one pn_gemv call per part on the same bytes (parts of one type share
+    one launch where the shapes allow it, each part with its own share of the workgroups), and
+    every output is within the oracle's bound."""
+    pn, torch, dev = env
+    K, spec = BITS_CASES[case]
+    parts = parts_for(K, spec, 14000 + 100 * case)
+    offs = [2 * (j % 2) for j in range(len(parts))]
+    x = synth.activations(14500 + case + M, M, K)
+    ys = run_group(pn, torch, dev, K, parts, x, w_offsets=offs)
+    for (typ, W, N), y, off in zip(parts, ys, offs):
+        if not N:
+            continue
+        y1 = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, off), N, K, x)
+        assert np.array_equal(y.view(np.uint32), y1.view(np.uint32))
+        y_ref, bound = oracle.gemv(typ, W, N, K, x)
+        assert_within(y, y_ref, bound)
 
 
 @pytest.mark.slow
