@@ -58,12 +58,16 @@ template <> struct Dec<PN_TYPE_PN3T> {
     // NPOS code positions per half are decoded in place (bit BITS*r, r < NPOS), the rest after a
     // shift of the dword by SHIFT bits
     static constexpr int BITS = 3, CPW = 10, PAIRS = 5, Z = 4, G = 80, NPOS = 3, SHIFT = 9;
+    // fp32 decode (3-4 tokens): codes whose bit in the dword lies past bit 20 are read after a
+    // shift by SH32
+    static constexpr int SH32 = 8;
     // floats a block of x takes in LDS: 20 mod 32 words, so that the 16-byte reads of 8
     // consecutive lanes (blocks 84 words apart) fall on 8 disjoint groups of 4 banks
     static constexpr int GS = 84;
 };
 template <> struct Dec<PN_TYPE_PN4T> {
     static constexpr int BITS = 4, CPW = 8, PAIRS = 4, Z = 8, G = 64, NPOS = 2, SHIFT = 8;
+    static constexpr int SH32 = 12;
     static constexpr int GS = 68;  // 4 mod 32 words
 };
 
@@ -165,6 +169,42 @@ __device__ __forceinline__ Consts<TYPE> make_consts()
     return c;
 }
 
+// The fp32 decode of 3-4 tokens: code r of half h sits at bit q = BITS*r + 16*h of the dword (or of
+// the dword shifted right by SH32, where q + BITS > 23); one and-or keeps it under the fp32
+// exponent of 2^(23-q), so the float is 2^(23-q) + n exactly, and one fp32 subtraction of
+// 2^(23-q) + z leaves n - z exactly. Each weight then takes plain fp32 fmas, one per token, where
+// the fp16 decode takes a mixed-precision fma per token: the same products and sums, bit for bit.
+template <int TYPE> struct Consts32 {
+    uint32_t mask[Dec<TYPE>::PAIRS][2];
+    uint32_t magic[Dec<TYPE>::PAIRS][2];
+};
+
+template <int TYPE> __host__ __device__ constexpr int q32(int r, int h)
+{
+    using D = Dec<TYPE>;
+    const int q = D::BITS * r + 16 * h;
+    return q + D::BITS > 23 ? q - D::SH32 : q;
+}
+
+template <int TYPE>
+__device__ __forceinline__ Consts32<TYPE> make_consts32()
+{
+    using D = Dec<TYPE>;
+    Consts32<TYPE> c;
+#pragma unroll
+    for (int r = 0; r < D::PAIRS; r++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int q = q32<TYPE>(r, h);
+            uint32_t mk = ((1u << D::BITS) - 1u) << q, mg = (uint32_t)(127 + 23 - q) << 23;
+            asm volatile("" : "+v"(mk));
+            asm volatile("" : "+v"(mg));
+            c.mask[r][h] = mk;
+            c.magic[r][h] = mg;
+        }
+    return c;
+}
+
 // Per-lane constants of the piece: offsets of its dwords from a row chunk's start, and how its
 // halves pair with x.
 struct Lane {
@@ -238,7 +278,8 @@ __device__ __forceinline__ void decode_dword(uint32_t v, const Consts<TYPE> &c,
 template <int TYPE, int M, int P>
 __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint32_t dwid,
                                          const float (&xs)[M][P][2][Dec<TYPE>::PAIRS],
-                                         const Consts<TYPE> &c, float (&out)[M])
+                                         const Consts<TYPE> &c, const Consts32<TYPE> &c32,
+                                         float (&out)[M])
 {
     using D = Dec<TYPE>;
     constexpr int CH = 4;  // chains per token and half
@@ -249,6 +290,28 @@ __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint
         for (int k = 0; k < CH; k++)
             acc[m][k][0] = acc[m][k][1] = 0.0f;
     const uint32_t last = (ln.bmask & sl.s[0]) | (~ln.bmask & sl.s[P]);
+    if constexpr (M >= 3) {
+#pragma unroll
+        for (int j = 0; j < P; j++) {
+            const uint32_t v = j < P - 1 ? sl.s[j + 1] : last;
+            const uint32_t vs = v >> D::SH32;
+#pragma unroll
+            for (int r = 0; r < D::PAIRS; r++) {
+                const int k = (j * D::PAIRS + r) % CH;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int q = D::BITS * r + 16 * h;
+                    const uint32_t src = q + D::BITS > 23 ? vs : v;
+                    const float w =
+                        __builtin_bit_cast(float, (src & c32.mask[r][h]) | c32.magic[r][h]) -
+                        (float)((1u << (23 - q32<TYPE>(r, h))) + (uint32_t)D::Z);
+#pragma unroll
+                    for (int m = 0; m < M; m++)
+                        acc[m][k][h] = __builtin_fmaf(w, xs[m][j][h][r], acc[m][k][h]);
+                }
+            }
+        }
+    } else {
     h2 n[2][D::PAIRS];
     decode_dword<TYPE, P>(P > 1 ? sl.s[1] : last, c, n[0]);
 #pragma unroll
@@ -266,6 +329,7 @@ __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint
                 acc[m][k][1] = __builtin_fmaf(whi, xs[m][j][1][r], acc[m][k][1]);
             }
         }
+    }
     }
     // d of the block; zero width for lanes past the end of the row (their x is zero too)
     const uint32_t dbits = __builtin_amdgcn_ubfe(P == 8 ? sl.s[0] : sl.dw, ln.dsh, dwid);
@@ -350,6 +414,9 @@ pn_gemv_rows_kernel(const Args a0)
         ln.dvoffl = act_last ? ln.dvoff : 0x80000000u;
     }
     const Consts<TYPE> cst = make_consts<TYPE>();
+    Consts32<TYPE> cst32;
+    if constexpr (M >= 3)
+        cst32 = make_consts32<TYPE>();
     const uint32_t rstride = a.row_stride;
 
     // ---- groups: the items (row, chunk) of the workgroup, chunk-major, in groups of at most DEPTH
@@ -509,7 +576,7 @@ pn_gemv_rows_kernel(const Args a0)
                 pv[s * M + m] = 0.0f;
             if (s < gn) {  // uniform
                 float o[M];
-                item_mac<TYPE, M, P>(ring[s], ln, dwid, xs, cst, o);
+                item_mac<TYPE, M, P>(ring[s], ln, dwid, xs, cst, cst32, o);
 #pragma unroll
                 for (int m = 0; m < M; m++)
                     pv[s * M + m] = o[m];
