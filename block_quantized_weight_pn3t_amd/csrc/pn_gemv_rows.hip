@@ -11,10 +11,12 @@
 //    add of -(2^(10-p) + z) leaves the integer n - z in each half, exactly (code z gives +0): no
 //    zero-point fold and no cancellation. Positions past the fp16 mantissa are reached after one
 //    shift of the dword (by 9 for pn3t, 8 for pn4t).
-//  * Each weight then takes one v_fma_mix_f32: the fp16 n - z widens exactly and its product with
-//    the fp32 x is exact inside the fma, so the only roundings are fp32 sums: four chains per lane
-//    and item, one multiply by the block's d, a 64-lane tree and the in-order sum over a row's
-//    chunks (and K slices).
+//  * Each weight then takes one v_fma_mix_f32 per token: the fp16 n - z widens exactly and its
+//    product with the fp32 x is exact inside the fma, so the only roundings are fp32 sums: four
+//    chains per lane and item, one multiply by the block's d, a 64-lane tree and the in-order sum
+//    over a row's chunks (and K slices).
+//  * At 3-4 tokens each code goes to fp32 instead (an and-or under an fp32 exponent, one exact
+//    subtraction), and each token takes a plain v_fma_f32: the same values, products and sums.
 //
 // Reading blocks whose words are not 4-byte aligned. Take a block that starts at a 4-byte aligned
 // address p (its words straddle dwords): the aligned dwords D_i = bytes [p + 4i, p + 4i + 4) hold
