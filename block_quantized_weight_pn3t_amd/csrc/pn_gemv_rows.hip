@@ -15,7 +15,7 @@
 //    product with the fp32 x is exact inside the fma, so the only roundings are fp32 sums: four
 //    chains per lane and item, one multiply by the block's d, a 64-lane tree and the in-order sum
 //    over a row's chunks (and K slices).
-//  * At 3-4 tokens each code goes to fp32 instead (an and-or under an fp32 exponent, one exact
+//  * At 2-4 tokens each code goes to fp32 instead (an and-or under an fp32 exponent, one exact
 //    subtraction), and each token takes a plain v_fma_f32: the same values, products and sums.
 //
 // Reading blocks whose words are not 4-byte aligned. Take a block that starts at a 4-byte aligned
@@ -171,7 +171,7 @@ __device__ __forceinline__ Consts<TYPE> make_consts()
     return c;
 }
 
-// The fp32 decode of 3-4 tokens: code r of half h sits at bit q = BITS*r + 16*h of the dword (or of
+// The fp32 decode of 2-4 tokens: code r of half h sits at bit q = BITS*r + 16*h of the dword (or of
 // the dword shifted right by SH32, where q + BITS > 23); one and-or keeps it under the fp32
 // exponent of 2^(23-q), so the float is 2^(23-q) + n exactly, and one fp32 subtraction of
 // 2^(23-q) + z leaves n - z exactly. Each weight then takes plain fp32 fmas, one per token, where
@@ -292,7 +292,7 @@ __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint
         for (int k = 0; k < CH; k++)
             acc[m][k][0] = acc[m][k][1] = 0.0f;
     const uint32_t last = (ln.bmask & sl.s[0]) | (~ln.bmask & sl.s[P]);
-    if constexpr (M >= 3) {
+    if constexpr (M >= 2) {
 #pragma unroll
         for (int j = 0; j < P; j++) {
             const uint32_t v = j < P - 1 ? sl.s[j + 1] : last;
@@ -417,7 +417,7 @@ pn_gemv_rows_kernel(const Args a0)
     }
     const Consts<TYPE> cst = make_consts<TYPE>();
     Consts32<TYPE> cst32;
-    if constexpr (M >= 3)
+    if constexpr (M >= 2)
         cst32 = make_consts32<TYPE>();
     const uint32_t rstride = a.row_stride;
 
@@ -621,8 +621,9 @@ namespace {
 // workgroup per CU; the register budget is 512 / (NW / 4) per lane).
 template <int TYPE, int M, int P> struct Cfg {
     static constexpr int DEPTH = P == 2 && M <= 2 ? 8 : 4;
-    // pn3t 8-word pieces hold 80 x per lane: two waves per SIMD keep them without spills
-    static constexpr int NW = (TYPE == PN_TYPE_PN3T && P == 8) || M >= 3 ? 8 : 12;
+    // pn3t 8-word pieces hold 80 x per lane, and 2-4 tokens hold M x per code plus the fp32
+    // decode's masks: two waves per SIMD keep them without spills
+    static constexpr int NW = (TYPE == PN_TYPE_PN3T && P == 8) || M >= 2 ? 8 : 12;
     // items whose weights are requested before x is staged
     static constexpr int PRE = M <= 2 ? 1 : DEPTH;
 };
