@@ -31,6 +31,7 @@ struct GroupPart {
     const uint8_t *W;
     int64_t N;
     float *y;
+    int type;
 };
 
 // One PN block brought into registers without assuming 4-byte alignment of its words.

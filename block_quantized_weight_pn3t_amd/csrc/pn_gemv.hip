@@ -76,6 +76,22 @@ static int run_group(const pn_gemv_part *parts, int count, int64_t K, const floa
     // parts' outputs are independent, so the order of the launches does not matter)
     bool done[PN_GEMV_GROUP_MAX_PARTS] = {};
     if (M <= 4) {
+        // parts of both types: one launch over all of them where the shapes allow it
+        GroupPart all[PN_GEMV_GROUP_MAX_PARTS];
+        int n = 0;
+        bool t3 = false, t4 = false;
+        for (int i = 0; i < count; i++)
+            if (parts[i].N > 0) {
+                t3 = t3 || parts[i].type == PN_TYPE_PN3T;
+                t4 = t4 || parts[i].type == PN_TYPE_PN4T;
+                all[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y,
+                                     parts[i].type};
+            }
+        if (t3 && t4) {
+            const int st = launch_vec_group(-1, all, n, K, x, M, s);
+            if (st != 1)
+                return st;
+        }
         for (int type : {PN_TYPE_PN3T, PN_TYPE_PN4T}) {
             GroupPart gp[PN_GEMV_GROUP_MAX_PARTS];
             int idx[PN_GEMV_GROUP_MAX_PARTS];
@@ -83,7 +99,7 @@ static int run_group(const pn_gemv_part *parts, int count, int64_t K, const floa
             for (int i = 0; i < count; i++)
                 if (parts[i].N > 0 && parts[i].type == type) {
                     idx[n] = i;
-                    gp[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y};
+                    gp[n++] = GroupPart{(const uint8_t *)parts[i].W, parts[i].N, parts[i].y, type};
                 }
             if (n < 2)
                 continue;

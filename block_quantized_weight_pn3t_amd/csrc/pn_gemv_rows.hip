@@ -85,6 +85,11 @@ struct Part {
     int g0;
     float *y;
     int64_t ystride;
+    int type;             // a launch of mixed types: the part's type and its row shape
+    uint32_t row_stride;
+    int nb;
+    int NC;
+    int rows_max;
 };
 constexpr int kMaxParts = 4;
 
@@ -348,10 +353,68 @@ __device__ __forceinline__ void item_mac(const Slot<P> &sl, const Lane &ln, uint
 
 typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int TYPE, int M, int P, int DEPTH, int NW, int PRE, bool DYN>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-pn_gemv_rows_kernel(const Args a0)
+// The matrix a workgroup works on: the launch's (one matrix) or, in a grouped launch, its part's,
+// found from the part table (uniform; no indexing of the argument array), with g and G made
+// part-local. Scalars only, so that nothing of the argument goes to private memory.
+struct View {
+    const uint8_t *base;
+    uint32_t nbytes, par, row_stride;
+    int N, nb, NC, rows_max;
+    float *y;
+    int64_t ystride;
+    int g, G, type;
+};
+
+__device__ __forceinline__ View make_view(const Args &a0, int type, bool mixed)
 {
+    View v;
+    v.base = a0.base;
+    v.nbytes = a0.nbytes;
+    v.par = a0.par;
+    v.row_stride = a0.row_stride;
+    v.N = a0.N;
+    v.nb = a0.nb;
+    v.NC = a0.NC;
+    v.rows_max = a0.rows_max;
+    v.y = a0.y;
+    v.ystride = a0.ystride;
+    v.g = blockIdx.x;
+    v.G = gridDim.x;
+    v.type = type;
+    if (a0.nparts > 0) {
+        int pi = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxParts; i++)
+            pi = i < a0.nparts && v.g >= a0.parts[i].g0 ? i : pi;
+#pragma unroll
+        for (int i = 0; i < kMaxParts; i++)
+            if (i == pi) {
+                const Part &pt = a0.parts[i];
+                const int gend = i + 1 < a0.nparts ? a0.parts[i + 1 < kMaxParts ? i + 1 : i].g0 : v.G;
+                v.base = pt.base;
+                v.nbytes = pt.nbytes;
+                v.par = pt.par;
+                v.N = pt.N;
+                v.y = pt.y;
+                v.ystride = pt.ystride;
+                if (mixed) {
+                    v.type = pt.type;
+                    v.row_stride = pt.row_stride;
+                    v.nb = pt.nb;
+                    v.NC = pt.NC;
+                    v.rows_max = pt.rows_max;
+                }
+                v.g -= pt.g0;
+                v.G = gend - pt.g0;
+            }
+    }
+    return v;
+}
+
+template <int TYPE, int M, int P, int DEPTH, int NW, int PRE, bool DYN>
+__device__ __forceinline__ void rows_body(const Args &a, const View &v)
+{
+    const int g = v.g, G = v.G;
     using D = Dec<TYPE>;
     constexpr int PPB = 8 / P;   // pieces per block
     constexpr int CB = 8 * P;    // blocks per chunk
@@ -362,39 +425,14 @@ pn_gemv_rows_kernel(const Args a0)
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // a grouped launch: this workgroup's matrix (uniform; no indexing of the argument array)
-    Args a = a0;
-    int G = gridDim.x, g = blockIdx.x;
-    if (a0.nparts > 0) {
-        int pi = 0;
-#pragma unroll
-        for (int i = 1; i < kMaxParts; i++)
-            pi = i < a0.nparts && g >= a0.parts[i].g0 ? i : pi;
-        Part pt = a0.parts[0];
-        int gend = a0.nparts > 1 ? a0.parts[1].g0 : G;
-#pragma unroll
-        for (int i = 1; i < kMaxParts; i++)
-            if (i == pi) {
-                pt = a0.parts[i];
-                gend = i + 1 < a0.nparts ? a0.parts[i + 1 < kMaxParts ? i + 1 : i].g0 : G;
-            }
-        a.base = pt.base;
-        a.nbytes = pt.nbytes;
-        a.par = pt.par;
-        a.N = pt.N;
-        a.y = pt.y;
-        a.ystride = pt.ystride;
-        g -= pt.g0;
-        G = gend - pt.g0;
-    }
-    const int r0 = (int)((int64_t)a.N * g / G), r1 = (int)((int64_t)a.N * (g + 1) / G);
+    const int r0 = (int)((int64_t)v.N * g / G), r1 = (int)((int64_t)v.N * (g + 1) / G);
     const int nr = r1 - r0;
-    const int NC = a.NC;
+    const int NC = v.NC;
     // x staged per token: whole chunks, each block of x in GS floats (zero past the slice)
     const int XT = NC * CB * D::GS;
     float *xl = lds;
     float *part = lds + M * XT;                    // [rows_max][NC][M]
-    const int dummy = a.rows_max * NC * M;         // then 64 dummy slots
+    const int dummy = v.rows_max * NC * M;         // then 64 dummy slots
     int *tickets = reinterpret_cast<int *>(part + dummy + 64);  // then the group counter
 
     // ---- lane constants
@@ -402,7 +440,7 @@ pn_gemv_rows_kernel(const Args a0)
     {
         ln.bl = lane / PPB;
         const int q = lane - ln.bl * PPB;
-        const uint32_t bstart = a.par + 34u * (uint32_t)ln.bl;
+        const uint32_t bstart = v.par + 34u * (uint32_t)ln.bl;
         const bool straddle = (bstart & 2u) == 0;  // block at 0 mod 4: words straddle dwords
         const uint32_t s0 = straddle ? bstart : bstart - 2u;
         ln.voff = s0 + 4u * P * (uint32_t)q;
@@ -411,7 +449,7 @@ pn_gemv_rows_kernel(const Args a0)
         ln.dsh = straddle ? 0u : 16u;
         ln.straddle = straddle;
         ln.xoff = D::GS * ln.bl + D::CPW * P * q;
-        const bool act_last = (NC - 1) * CB + ln.bl < a.nb;
+        const bool act_last = (NC - 1) * CB + ln.bl < v.nb;
         ln.voffl = act_last ? ln.voff : 0x80000000u;
         ln.dvoffl = act_last ? ln.dvoff : 0x80000000u;
     }
@@ -419,7 +457,7 @@ pn_gemv_rows_kernel(const Args a0)
     Consts32<TYPE> cst32;
     if constexpr (M >= 2)
         cst32 = make_consts32<TYPE>();
-    const uint32_t rstride = a.row_stride;
+    const uint32_t rstride = v.row_stride;
 
     // ---- groups: the items (row, chunk) of the workgroup, chunk-major, in groups of at most DEPTH
     // rows of one chunk, so that x changes only between groups. Two ways to share them out:
@@ -481,7 +519,7 @@ pn_gemv_rows_kernel(const Args a0)
     // reads no memory. Lanes past the end of a row load nothing in the row's last chunk.
     auto load_item = [&](Slot<P> &sl, int c, int r, bool real) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(a.base), (short)0, real ? (int)a.nbytes : 0, 0x00020000);
+            const_cast<uint8_t *>(v.base), (short)0, real ? (int)v.nbytes : 0, 0x00020000);
         const bool lastc = c == NC - 1;
         load_slot<P>(rs, lastc ? ln.voffl : ln.voff, lastc ? ln.dvoffl : ln.dvoff,
                      (uint32_t)(r0 + r) * rstride + CBYTES * (uint32_t)c, sl);
@@ -491,7 +529,7 @@ pn_gemv_rows_kernel(const Args a0)
     // for it waits for no weights; further passes (large M * K) wait for everything in flight
     constexpr int G4 = D::G / 4;       // 16-byte pieces of x per block
     constexpr int XPT = 8;             // pieces per thread and pass
-    const int nvalid = a.nb * G4;      // pieces per token inside the slice
+    const int nvalid = v.nb * G4;      // pieces per token inside the slice
     const int ntot = NC * CB * G4;     // pieces per token, whole chunks
     const int npieces = M * ntot;
     auto stage_load = [&](int pass, float4 (&v)[XPT]) {
@@ -565,7 +603,7 @@ pn_gemv_rows_kernel(const Args a0)
         next_group(lgc, lgr, lgn);
         if (gc != xc) {
             xc = gc;
-            dwid = xc * CB + ln.bl < a.nb ? 16u : 0u;
+            dwid = xc * CB + ln.bl < v.nb ? 16u : 0u;
 #pragma unroll
             for (int m = 0; m < M; m++)
                 read_x<TYPE, P>(xl + m * XT + xc * CB * D::GS + ln.xoff, ln.straddle, xs[m]);
@@ -606,9 +644,31 @@ pn_gemv_rows_kernel(const Args a0)
         float acc = 0.0f;
         for (int c = 0; c < NC; c++)
             acc += part[(k * NC + c) * M + m];
-        float *yp = a.y + (int64_t)m * a.ystride + (int64_t)(r0 + k) * a.yinc;
+        float *yp = v.y + (int64_t)m * v.ystride + (int64_t)(r0 + k) * a.yinc;
         *yp = a.accumulate ? *yp + acc : acc;
     }
+}
+
+template <int TYPE, int M, int P, int DEPTH, int NW, int PRE, bool DYN>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+pn_gemv_rows_kernel(const Args a)
+{
+    const View v = make_view(a, TYPE, false);
+    rows_body<TYPE, M, P, DEPTH, NW, PRE, DYN>(a, v);
+}
+
+// Matrices of both types in one launch: each workgroup runs its part's decode, with that type's
+// own piece size, ring depth and early-weight count (those a launch of the type alone takes, so
+// that every row gets the same bits), under one launch shape.
+template <int M, int P3, int DEPTH3, int PRE3, int P4, int DEPTH4, int PRE4, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+pn_gemv_rows_mixed_kernel(const Args a)
+{
+    const View v = make_view(a, PN_TYPE_PN3T, true);
+    if (v.type == PN_TYPE_PN3T)
+        rows_body<PN_TYPE_PN3T, M, P3, DEPTH3, NW, PRE3, false>(a, v);
+    else
+        rows_body<PN_TYPE_PN4T, M, P4, DEPTH4, NW, PRE4, false>(a, v);
 }
 
 }  // namespace rows
@@ -889,13 +949,152 @@ int launch_group_m(const GroupPart *gp, int count, int64_t K, const float *x, in
     }
 }
 
+template <int M, int P3, int P4>
+int launch_mixed_one(const rows::Args &a, int grid, size_t lds, hipStream_t s)
+{
+    using C3 = Cfg<PN_TYPE_PN3T, M, P3>;
+    using C4 = Cfg<PN_TYPE_PN4T, M, P4>;
+    constexpr auto kern = rows::pn_gemv_rows_mixed_kernel<M, P3, C3::DEPTH, C3::PRE, P4, C4::DEPTH,
+                                                          C4::PRE, 8>;
+    if (!lds_limit_once<kern>(rows::kLdsMax))
+        return PN_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * 8), lds, s, a);
+    return launch_status();
+}
+
+// piece sizes a launch can take: 8, 4 and 2 at one token, 4 and 2 at two, 2 at three and four
+template <int M, int P3>
+int launch_mixed_p4(const rows::Args &a, int grid, size_t lds, int P4, hipStream_t s)
+{
+    if constexpr (M == 1) {
+        if (P4 == 8)
+            return launch_mixed_one<M, P3, 8>(a, grid, lds, s);
+    }
+    if constexpr (M <= 2) {
+        if (P4 == 4)
+            return launch_mixed_one<M, P3, 4>(a, grid, lds, s);
+    }
+    return launch_mixed_one<M, P3, 2>(a, grid, lds, s);
+}
+
+template <int M>
+int launch_mixed_p3(const rows::Args &a, int grid, size_t lds, int P3, int P4, hipStream_t s)
+{
+    if constexpr (M == 1) {
+        if (P3 == 8)
+            return launch_mixed_p4<M, 8>(a, grid, lds, P4, s);
+    }
+    if constexpr (M <= 2) {
+        if (P3 == 4)
+            return launch_mixed_p4<M, 4>(a, grid, lds, P4, s);
+    }
+    return launch_mixed_p4<M, 2>(a, grid, lds, P4, s);
+}
+
+// Matrices of both types (and one K) as one launch: each type with the piece size a launch of its
+// own would take, 8 waves per CU, each part with its own row shape, x layout and share of the
+// workgroups (in proportion to its bytes). Returns 1 where the shapes do not allow it (as
+// launch_group_typed).
+template <int M>
+int launch_group_mixed(const GroupPart *gp, int count, int64_t K, const float *x, hipStream_t s)
+{
+    using D3 = rows::Dec<PN_TYPE_PN3T>;
+    using D4 = rows::Dec<PN_TYPE_PN4T>;
+    if (count < 2 || count > rows::kMaxParts || K % D3::G || K % D4::G)
+        return 1;
+    const int64_t nb3 = K / D3::G, nb4 = K / D4::G;
+    if (((nb3 * kBlockBytes) & 2) || ((nb4 * kBlockBytes) & 2))
+        return 1;
+    const int P3 = choose_p<PN_TYPE_PN3T, M>(nb3), P4 = choose_p<PN_TYPE_PN4T, M>(nb4);
+    int64_t bytes[rows::kMaxParts], total_bytes = 0, total_rows = 0;
+    for (int i = 0; i < count; i++) {
+        const int64_t rb = (gp[i].type == PN_TYPE_PN3T ? nb3 : nb4) * kBlockBytes;
+        if (gp[i].N <= 0 || gp[i].N * rb > (int64_t)0x7FFF0000)
+            return 1;
+        bytes[i] = gp[i].N * rb;
+        total_bytes += bytes[i];
+        total_rows += gp[i].N;
+    }
+    const int grid = (int)std::min<int64_t>(device_cus(), total_rows);
+    if (grid < count)
+        return 1;
+    int gcount[rows::kMaxParts];
+    int used = 0;
+    for (int i = 0; i < count; i++) {
+        gcount[i] = (int)std::max<int64_t>(1, std::min<int64_t>(gp[i].N, bytes[i] * grid / total_bytes));
+        used += gcount[i];
+    }
+    for (int i = 0; used < grid; i = (i + 1) % count)
+        if (gcount[i] < gp[i].N) {
+            gcount[i]++;
+            used++;
+        }
+    for (int i = 0; used > grid; i = (i + 1) % count)
+        if (gcount[i] > 1) {
+            gcount[i]--;
+            used--;
+        }
+    rows::Args a{};
+    size_t lds = rows::kLdsFloor;
+    int g0 = 0;
+    for (int i = 0; i < count; i++) {
+        const bool p3 = gp[i].type == PN_TYPE_PN3T;
+        const int64_t nb = p3 ? nb3 : nb4, rb = nb * kBlockBytes, cb = 8 * (p3 ? P3 : P4);
+        const int64_t NC = (nb + cb - 1) / cb;
+        const size_t x_bytes = (size_t)M * NC * cb * (p3 ? D3::GS : D4::GS) * sizeof(float);
+        if (x_bytes > (size_t)rows::kXLdsMax)
+            return 1;
+        const int64_t rows_max = (gp[i].N + gcount[i] - 1) / gcount[i];
+        const int64_t part_cap =
+            ((int64_t)rows::kLdsMax - (int64_t)x_bytes) / (int64_t)sizeof(float) - 65;
+        if (rows_max * NC * M > part_cap)
+            return 1;
+        lds = std::max(lds, x_bytes + ((size_t)rows_max * NC * M + 65) * sizeof(float));
+        const uintptr_t fa = reinterpret_cast<uintptr_t>(gp[i].W);
+        rows::Part &pt = a.parts[i];
+        pt.par = (uint32_t)(fa & 3u);
+        pt.base = gp[i].W - pt.par;
+        pt.nbytes = (uint32_t)(((int64_t)pt.par + gp[i].N * rb + 3) & ~(int64_t)3);
+        pt.N = (int)gp[i].N;
+        pt.g0 = g0;
+        pt.y = gp[i].y;
+        pt.ystride = gp[i].N;
+        pt.type = gp[i].type;
+        pt.row_stride = (uint32_t)rb;
+        pt.nb = (int)nb;
+        pt.NC = (int)NC;
+        pt.rows_max = (int)rows_max;
+        g0 += gcount[i];
+    }
+    a.nparts = count;
+    a.x = x;
+    a.xstride = K;
+    a.yinc = 1;
+    a.accumulate = 0;
+    return launch_mixed_p3<M>(a, grid, lds, P3, P4, s);
+}
+
+int launch_group_mixed_m(const GroupPart *gp, int count, int64_t K, const float *x, int64_t M,
+                         hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_group_mixed<1>(gp, count, K, x, s);
+    case 2: return launch_group_mixed<2>(gp, count, K, x, s);
+    case 3: return launch_group_mixed<3>(gp, count, K, x, s);
+    default: return launch_group_mixed<4>(gp, count, K, x, s);
+    }
+}
+
 }  // namespace
 
-// Several PN GEMVs of one type and K over the same x at 1 <= M <= 4 as one launch (arguments
-// already checked): PN_OK, an error, or 1 where the parts must run as launches of their own.
+// Several PN GEMVs of one type (type < 0: parts of both types, each part's own type in gp) and K
+// over the same x at 1 <= M <= 4 as one launch (arguments already checked): PN_OK, an error, or 1
+// where the parts must run as launches of their own.
 int launch_vec_group(int type, const GroupPart *gp, int count, int64_t K, const float *x,
                      int64_t M, hipStream_t s)
 {
+    if (type < 0)  // both types
+        return launch_group_mixed_m(gp, count, K, x, M, s);
     return type == PN_TYPE_PN3T ? launch_group_m<PN_TYPE_PN3T>(gp, count, K, x, M, s)
                                 : launch_group_m<PN_TYPE_PN4T>(gp, count, K, x, M, s);
 }

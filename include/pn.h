@@ -107,11 +107,11 @@ int pn_gemv(int type, const void *W, int64_t N, int64_t K, const float *x, int64
 
 /* Several PN GEMVs that read the same x (a layer's q, k and v; gate and up):
  * parts[i].y[m*N_i + n] = sum_k w_i[n, k] * x[m*K + k], with the bits of one pn_gemv per part. At
- * 1-4 tokens the parts of one type run as one launch where the shapes allow it (the others as
- * launches of their own, in order on the stream). 1 <= count <= PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part has
- * its own type, W (N_i rows of K weights) and y, and all share K, x and M (0..16). Argument errors
- * as pn_gemv, for the first part that has one; parts with N = 0 are skipped. The parts' y must not
- * overlap each other or x. */
+ * 1-4 tokens all parts, of either type, run as one launch where the shapes allow it (else the
+ * parts of each type, else one launch per part, in order on the stream). 1 <= count <=
+ * PN_GEMV_GROUP_MAX_PARTS (else PN_ERR_SHAPE); every part has its own type, W (N_i rows of K
+ * weights) and y, and all share K, x and M (0..16). Argument errors as pn_gemv, for the first part
+ * that has one; parts with N = 0 are skipped. The parts' y must not overlap each other or x. */
 typedef struct pn_gemv_part {
     int type;       /* PN_TYPE_PN3T or PN_TYPE_PN4T */
     const void *W;  /* N rows of pn_row_bytes(type, K) bytes, 2-byte aligned */

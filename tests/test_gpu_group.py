@@ -42,16 +42,16 @@ def run_group(pn, torch, dev, K, parts, x, x_offset=0, w_offsets=None):
     return [y.cpu().numpy()[:, :N] for y, (_, _, N) in zip(ys, parts)]
 
 
-# (K, [(type, N)]): the body each part takes is fixed by K
+# (K, [(type, N)]): K fixes each type's piece size (8, 4 or 2 words) and its chunks per row; the
+# parts of both types run as one launch in every case here at 1-4 tokens
 CASES = [
-    (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # 64-block pn3t + 80-block pn4t (q, k, v)
-    (5120, [(PN3T, 1000), (PN3T, 777)]),                        # two register pn3t parts (gate, up)
-    (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # register bodies of both types, tiny
-                                                                # parts; 50 pn4t blocks: separate at 3-4
+    (5120, [(PN3T, 600), (PN4T, 130), (PN4T, 129)]),            # q, k, v: 64-block pn3t rows (one
+                                                                # chunk), 80-block pn4t (ragged)
+    (5120, [(PN3T, 1000), (PN3T, 777)]),                        # gate, up: one type
+    (3200, [(PN3T, 333), (PN4T, 65), (PN3T, 1), (PN4T, 7)]),    # tiny parts of both types
     (6400, [(PN3T, 140), (PN4T, 301)]),                         # long rows of both types
     (5120, [(PN3T, 0), (PN4T, 50), (PN3T, 9)]),                 # an empty part
-    (5120, [(PN3T, 200), (PN4T, 64), (PN3T, 17), (PN4T, 300)]),  # four parts, all on the matrix
-                                                                # cores at 3-4 tokens
+    (5120, [(PN3T, 200), (PN4T, 64), (PN3T, 17), (PN4T, 300)]),  # four parts
 ]
 
 
@@ -107,9 +107,9 @@ BITS_CASES = CASES + [(960, [(PN3T, 50), (PN3T, 31), (PN4T, 40), (PN4T, 3)])]
 @pytest.mark.parametrize("case", range(len(BITS_CASES)))
 def test_group_same_bits_as_separate_calls(env, case, M):
     """Every case at 1-4 tokens, the parts' W at alternating 4-byte alignments (+0, +2 bytes): the
-    group gives the bits of one pn_gemv call per part on the same bytes (parts of one type share
-    one launch where the shapes allow it, each part with its own share of the workgroups), and
-    every output is within the oracle's bound."""
+    group gives the bits of one pn_gemv call per part on the same bytes (the parts share one
+    launch where the shapes allow it, each part with its own share of the workgroups and its
+    type's own piece size), and every output is within the oracle's bound."""
     pn, torch, dev = env
     K, spec = BITS_CASES[case]
     parts = parts_for(K, spec, 14000 + 100 * case)
