@@ -212,8 +212,8 @@ def hadamard_rows(x, B, out, M=None, K=None, stream=None):
 
 
 def gemv_hadamard(type_, W, N, K, x, B, y, M=None, stream=None):
-    """y[M, N] <- W[N, K] . (H x)[M, K]^T: x rotated into a stream-ordered temporary, then the GEMV
-    (M <= 4)."""
+    """y[M, N] <- W[N, K] . (H x)[M, K]^T: x rotated into the library's per-device workspace, then
+    the GEMV (M <= 4)."""
     import torch
     _dev(x, "x", torch.float32)
     _dev(y, "y", torch.float32)

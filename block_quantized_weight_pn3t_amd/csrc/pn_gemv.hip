@@ -123,70 +123,99 @@ static int run_group(const pn_gemv_part *parts, int count, int64_t K, const floa
     return PN_OK;
 }
 
-// The stream-ordered temporaries of the rotated-x calls come from a memory pool of the library's
-// own per device that keeps what is freed (release threshold at its maximum): after the first
-// call the allocation is a reuse inside the pool, not a trip to the system, which the device's
-// default pool (threshold 0) makes on every call. Each device keeps up to its largest temporary
-// for the life of the process. Under stream capture the default pool's allocation is used, which
-// a graph records as its own allocation node.
-constexpr int kMaxPoolDevices = 64;
-static std::atomic<hipMemPool_t> g_pool[kMaxPoolDevices];
-static std::mutex g_pool_mu;
+// The rotated x of the rotated-x calls lives in a workspace per stream: each device keeps a table
+// of up to kStreamSlots streams, each with a buffer grown on that stream when a call needs more
+// and held for the life of the process. Work on one stream runs in order, so a call reuses its
+// stream's buffer with no event and no allocation (a stream-ordered allocation and free per call
+// cost about 14 us of host time, and an event recorded per call about 2-4 us of GPU time, more
+// than the rotation); different streams never share a buffer. The device's lock is held while a
+// call enqueues its launches, so that calls from several host threads on one stream do not
+// interleave. A stream's handle names its slot: a destroyed stream's handle is not handed out
+// again before the work on it has ended, so a new stream with the same handle may take the slot
+// over. When the table is full, on hipStreamPerThread (one handle for a different stream in each
+// host thread) and under stream capture (so that the graph records an allocation node of its
+// own), a call allocates a temporary on its stream (hipMallocAsync) and frees it there after its
+// launches.
+constexpr int kStreamSlots = 16;
+struct StreamSlot {
+    hipStream_t stream = nullptr;
+    float *buf = nullptr;
+    size_t cap = 0;
+    bool used = false;
+};
+struct Workspace {
+    std::mutex mu;
+    StreamSlot slot[kStreamSlots];
+};
+constexpr int kMaxWorkspaceDevices = 64;
+static Workspace g_ws[kMaxWorkspaceDevices];
 
-static hipMemPool_t temp_pool()
+template <typename F>
+static int rotate_then(float *xr, const float *x, int64_t M, int64_t K, int64_t B, hipStream_t s,
+                       F f)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxPoolDevices)
-        return nullptr;
-    hipMemPool_t p = g_pool[dev].load(std::memory_order_acquire);
-    if (p)
-        return p;
-    std::lock_guard<std::mutex> lk(g_pool_mu);
-    p = g_pool[dev].load(std::memory_order_relaxed);
-    if (!p) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        uint64_t keep = ~0ull;
-        if (hipMemPoolCreate(&p, &props) != hipSuccess || !p ||
-            hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-        g_pool[dev].store(p, std::memory_order_release);
-    }
-    return p;
+    const int st = pn_hadamard_rows(x, M, K, B, xr, s);
+    return st == PN_OK ? f(xr) : st;
 }
 
-// x' = the rotation of x[M, K] in a stream-ordered temporary, then f(x'); the temporary is
-// released on the same stream after f's launches.
+static int hip_failed()
+{
+    (void)hipGetLastError();
+    return PN_ERR_HIP;
+}
+
+// x' = the rotation of x[M, K] in the stream's workspace (else a temporary), then f(x').
 template <typename F>
 static int with_rotated(const float *x, int64_t M, int64_t K, int64_t B, hipStream_t s, F f)
 {
     const size_t bytes = (size_t)(M * K) * sizeof(float);
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
-        (void)hipGetLastError();
-        return PN_ERR_HIP;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess)
+        return hip_failed();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxWorkspaceDevices)
+        return hip_failed();
+    Workspace &w = g_ws[dev];
+    std::lock_guard<std::mutex> lk(w.mu);
+    StreamSlot *sl = nullptr;
+    if (cap == hipStreamCaptureStatusNone && s != hipStreamPerThread) {
+        for (StreamSlot &c : w.slot)
+            if (c.used && c.stream == s) {
+                sl = &c;
+                break;
+            }
+        if (!sl)
+            for (StreamSlot &c : w.slot)
+                if (!c.used) {
+                    c.used = true;
+                    c.stream = s;
+                    sl = &c;
+                    break;
+                }
     }
-    hipMemPool_t pool = nullptr;
-    if (cap == hipStreamCaptureStatusNone && !(pool = temp_pool()))
-        return PN_ERR_HIP;
-    float *xr = nullptr;
-    const hipError_t e = pool ? hipMallocFromPoolAsync(reinterpret_cast<void **>(&xr), bytes, pool, s)
-                              : hipMallocAsync(reinterpret_cast<void **>(&xr), bytes, s);
-    if (e != hipSuccess || !xr) {
-        (void)hipGetLastError();
-        return PN_ERR_HIP;
+    if (!sl) {
+        float *xr = nullptr;
+        if (hipMallocAsync(reinterpret_cast<void **>(&xr), bytes, s) != hipSuccess || !xr)
+            return hip_failed();
+        int st = rotate_then(xr, x, M, K, B, s, f);
+        if (hipFreeAsync(xr, s) != hipSuccess && st == PN_OK)
+            st = hip_failed();
+        return st;
     }
-    int st = pn_hadamard_rows(x, M, K, B, xr, s);
-    if (st == PN_OK)
-        st = f(xr);
-    if (hipFreeAsync(xr, s) != hipSuccess && st == PN_OK)
-        st = PN_ERR_HIP;
-    return st;
+    if (bytes > sl->cap) {
+        // every earlier use of the old buffer is on this stream, so it is released after them
+        if (sl->buf && hipFreeAsync(sl->buf, s) != hipSuccess)
+            return hip_failed();
+        sl->buf = nullptr;
+        sl->cap = 0;
+        const size_t want = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+        if (hipMallocAsync(reinterpret_cast<void **>(&sl->buf), want, s) != hipSuccess || !sl->buf) {
+            sl->buf = nullptr;
+            return hip_failed();
+        }
+        sl->cap = want;
+    }
+    return rotate_then(sl->buf, x, M, K, B, s, f);
 }
 
 // ---- the rotated x of pn_gemv_hadamard_noalloc: a file-scope device array --------------------

@@ -136,13 +136,16 @@ int pn_gemv_group(const pn_gemv_part *parts, int count, int64_t K, const float *
  * (PN_ERR_SHAPE). out may equal x (in place); otherwise they must not overlap. */
 int pn_hadamard_rows(const float *x, int64_t M, int64_t K, int64_t B, float *out, void *stream);
 
-/* y = W x' for M = 1..4 tokens: the rotation of pn_hadamard_rows into a stream-ordered temporary
- * (allocated on the stream from a memory pool the library creates per device, which keeps what is
- * freed, so each device holds up to its largest temporary for the life of the process; under
- * stream capture, hipMallocAsync from the device's default pool; released with hipFreeAsync after
- * the GEMV's launches; x itself is not modified), then pn_gemv on it: the same bits as those two calls made by hand, the rotation's
- * error above adding to the GEMV's. Arguments as pn_gemv, plus B as in pn_hadamard_rows; M outside
- * 0..4 gives PN_ERR_TOKENS, a failed allocation PN_ERR_HIP. */
+/* y = W x' for M = 1..4 tokens: the rotation of pn_hadamard_rows into a workspace, then pn_gemv
+ * on it: the same bits as those two calls made by hand, the rotation's error above adding to the
+ * GEMV's; x itself is not modified. The workspace is a buffer per stream (up to 16 streams per
+ * device) that the library keeps for the life of the process, grown on its stream
+ * (hipMallocAsync, the old one hipFreeAsync'd) when a call needs more than it holds: a call
+ * allocates nothing otherwise. Calls on one stream reuse its buffer in stream order; calls on
+ * different streams never share one. Past 16 streams on a device, on hipStreamPerThread and under
+ * stream capture, a call takes a temporary instead (hipMallocAsync and hipFreeAsync on its stream,
+ * which a graph records as nodes of its own). Arguments as pn_gemv, plus B as in
+ * pn_hadamard_rows; M outside 0..4 gives PN_ERR_TOKENS, a failed allocation PN_ERR_HIP. */
 int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float *x, int64_t M,
                      int64_t B, float *y, void *stream);
 
@@ -158,10 +161,10 @@ int pn_gemv_hadamard(int type, const void *W, int64_t N, int64_t K, const float 
 int pn_gemv_hadamard_noalloc(int type, const void *W, int64_t N, int64_t K, const float *x,
                              int64_t M, int64_t B, float *y, void *stream);
 
-/* Several GEMVs that share x, over the rotated x: x rotated once into a stream-ordered temporary
- * (as pn_gemv_hadamard), then pn_gemv_group on it -- parts[i].y = W_i x' with the bits of
- * pn_hadamard_rows followed by one pn_gemv per part. B as in pn_hadamard_rows, 0 <= M <= 4 (else
- * PN_ERR_TOKENS), parts and errors as pn_gemv_group. */
+/* Several GEMVs that share x, over the rotated x: x rotated once into the workspace of
+ * pn_gemv_hadamard (same streams and allocation), then pn_gemv_group on it -- parts[i].y = W_i x'
+ * with the bits of pn_hadamard_rows followed by one pn_gemv per part. B as in pn_hadamard_rows,
+ * 0 <= M <= 4 (else PN_ERR_TOKENS), parts and errors as pn_gemv_group. */
 int pn_gemv_group_hadamard(const pn_gemv_part *parts, int count, int64_t K, const float *x,
                            int64_t M, int64_t B, void *stream);
 

@@ -221,3 +221,78 @@ def test_gemv_hadamard_full_size(env, typ, N, K, seed, xseed):
         tol = 1e-5 * bound[:M] + (1 + 1e-5) * gamma(1024) * rbound[:M]
         err = np.abs(y.astype(np.float64) - y_ref[:M])
         assert np.all(err <= tol), f"M={M} max |err| / tol = {float(np.max(err / tol)):.3f}"
+
+
+def test_gemv_hadamard_two_streams_in_flight(env):
+    """Rotated-x calls on two streams with nothing synchronising them, large matrices (whose GEMV
+    reads the rotated x for some 15 us) between small ones, one call that needs a larger workspace
+    in the middle and one grouped call: every output has the bits of the same call made alone.
+    Each stream's calls reuse that stream's workspace, so this holds only if the two streams'
+    workspaces are apart and a grown one is released after the calls that read it."""
+    pn, torch, dev = env
+    B = 1024
+    mats = {
+        "down": (PN4T, 5120, 17408, 303),   # the full-size test's weights (cached)
+        "gate": (PN3T, 17408, 5120, 301),
+        "small": (PN3T, 300, 5120, 6101),
+        "kv": (PN4T, 130, 5120, 6102),
+        "long": (PN4T, 64, 81920, 6103),    # 4 x 81920 floats: past a 1 MiB workspace
+    }
+    Wd = {}
+    for name, (typ, N, K, seed) in mats.items():
+        Wd[name] = dev_bytes(torch, dev, quantized(typ, N, K, seed)[1])
+    calls = [("down", 4), ("small", 1), ("gate", 2), ("down", 1), ("long", 4), ("small", 3),
+             ("down", 2), ("long", 1), ("group", 2), ("gate", 1)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    xs, outs = [], []
+    for i, (name, M) in enumerate(calls):
+        K = 5120 if name == "group" else mats[name][2]
+        x = synth.activations(6200 + i, M, K)
+        _, xd = dev_f32(torch, dev, x)
+        xs.append((x, xd))
+        if name == "group":
+            outs.append([torch.full((M, mats[p][1]), float("nan"), dtype=torch.float32, device=dev)
+                         for p in ("small", "kv")])
+        else:
+            outs.append([torch.full((M, mats[name][1]), float("nan"), dtype=torch.float32,
+                                    device=dev)])
+    torch.cuda.synchronize()
+    for i, (name, M) in enumerate(calls):
+        s = streams[i % 2]
+        xd = xs[i][1]
+        if name == "group":
+            parts = [(mats[p][0], Wd[p], mats[p][1], y) for p, y in zip(("small", "kv"), outs[i])]
+            pn.gemv_group_hadamard(parts, 5120, xd, B, M=M, stream=s)
+        else:
+            typ, N, K, _ = mats[name]
+            pn.gemv_hadamard(typ, Wd[name], N, K, xd, B, outs[i][0], M=M, stream=s)
+    torch.cuda.synchronize()
+    for i, (name, M) in enumerate(calls):
+        x = xs[i][0]
+        for p, y in zip(("small", "kv") if name == "group" else (name,), outs[i]):
+            typ, N, K, _ = mats[p]
+            alone = gemv_hadamard(pn, torch, dev, typ, Wd[p], N, K, x, B)
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), alone.view(np.uint32)), (i, p)
+
+
+def test_gemv_hadamard_more_streams_than_slots(env):
+    """24 streams (more than the 16 workspaces a device keeps, so some calls take a temporary of
+    their own), one rotated-x call on each with nothing synchronising them: every output has the
+    bits of the same call made alone."""
+    pn, torch, dev = env
+    typ, N, K, B = PN3T, 300, 5120, 1024
+    Wd = dev_bytes(torch, dev, quantized(typ, N, K, 6101)[1])
+    streams = [torch.cuda.Stream() for _ in range(24)]
+    xs, ys = [], []
+    for i in range(len(streams)):
+        M = 1 + i % 4
+        x = synth.activations(6300 + i, M, K)
+        xs.append((x, dev_f32(torch, dev, x)[1]))
+        ys.append(torch.full((M, N), float("nan"), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    for i, s in enumerate(streams):
+        pn.gemv_hadamard(typ, Wd, N, K, xs[i][1], B, ys[i], M=xs[i][0].shape[0], stream=s)
+    torch.cuda.synchronize()
+    for i in range(len(streams)):
+        alone = gemv_hadamard(pn, torch, dev, typ, Wd, N, K, xs[i][0], B)
+        assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), alone.view(np.uint32)), i
