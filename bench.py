@@ -163,9 +163,27 @@ def copy_calibration(torch, dev, mb: int, reps: int = 4):
     log(f"[bench] copy calibration: {reps} copies of {mb} MiB")
 
 
+# Untimed sustained work before each timed region: the GPU's clocks rise over the first
+# milliseconds of back-to-back launches (the same launches run 20.5, 18.3 and 17.6 µs in three
+# consecutive 6 ms windows after an idle host phase), and a decoder serving tokens runs in the
+# settled state. Reported in the JSON line as settle_s.
+SETTLE_S = 0.2
+
+
+def settle(torch, launch, copies, seconds=SETTLE_S):
+    """Run `launch(i)` back to back (rotating copies) for about `seconds` of wall time, untimed."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            launch(i % copies)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_launches(torch, stream, launch, copies, reps, warmup):
     """Average µs of `launch(i)` over `reps` back-to-back launches (rotating copies i % copies)
-    between two events on the launch stream."""
+    between two events on the launch stream, after a settle phase and `warmup` launches."""
+    settle(torch, launch, copies, SETTLE_S / 4)
     for i in range(warmup):
         launch(i % copies)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -528,6 +546,7 @@ def main():
             if st != 0:
                 raise RuntimeError(f"pn_gemv failed: {pn.status_string(st)}")
 
+    settle(torch, one_step, args.copies)
     for s in range(args.warmup):
         one_step(s)
     torch.cuda.synchronize()
@@ -558,6 +577,7 @@ def main():
                              m["x"].data_ptr(), 1, m["y"].data_ptr(), sh)
             if st != 0:
                 raise RuntimeError(f"pn_gemv failed: {pn.status_string(st)}")
+        settle(torch, launch, args.copies)
         for s in range(args.warmup):
             launch(s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -593,6 +613,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
