@@ -728,7 +728,12 @@ int launch_p(int P, const rows::Args &a, int grid, size_t lds, hipStream_t s)
 
 // Piece size for a row of nb blocks at M tokens: the largest x that fits the registers (at most 80
 // floats per lane), then the fewest VALU operations per weight, counting the lanes of a partial
-// last chunk as spent.
+// last chunk as spent. Each item also pays a fixed cost whatever its piece size: the reduction of
+// its partial across the wave, the partial's LDS write and the item's scheduling. Its weight,
+// kItemOps, is fitted to launches timed at every piece size (rows of 40-272 blocks, 1024-17408
+// rows, 1-2 tokens): at 18 the model kept 2-word pieces where 4 or 8 words ran 0.3-2 us faster.
+constexpr double kItemOps = 70.0;
+
 template <int TYPE, int M>
 int choose_p(int64_t nb)
 {
@@ -740,7 +745,7 @@ int choose_p(int64_t nb)
             continue;
         const int64_t cb = 8 * P, nc = (nb + cb - 1) / cb;
         const double eff = (double)nb / (double)(nc * cb);
-        const double ops = P * (1 + D::PAIRS * (2 + 2 * M)) + 18.0;  // per item and lane
+        const double ops = P * (1 + D::PAIRS * (2 + 2 * M)) + kItemOps;  // per item and lane
         const double cost = ops / (eff * D::CPW * P);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
