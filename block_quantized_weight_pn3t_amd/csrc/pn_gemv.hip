@@ -6,8 +6,8 @@
 //    not a dense contraction).
 //  * 5-16 tokens: the matrix-core kernels of pn_gemv_mfma.hip.
 //  * Hadamard-rotated activations ("Files that use PN"): the rotation of pn_hadamard_rows into a
-//    stream-ordered temporary, then the GEMV above on it -- the same bits as the two calls made by
-//    hand. The group variants rotate x once for all their matrices.
+//    workspace of the call's stream, then the GEMV above on it -- the same bits as the two calls
+//    made by hand. The group variants rotate x once for all their matrices.
 #include <algorithm>
 #include <atomic>
 #include <mutex>

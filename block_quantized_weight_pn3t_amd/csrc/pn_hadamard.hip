@@ -1,7 +1,7 @@
 // pn_hadamard.hip -- the Hadamard rotation of the activations as its own launch
 // ("PN weight format", "Files that use PN"; the reading and the arithmetic are stated in
-// pn_hadamard.h). pn_gemv_hadamard and pn_gemv_group_hadamard run it into a temporary ahead of the
-// GEMV, and pn_gemv_hadamard_noalloc into a static device array.
+// pn_hadamard.h). pn_gemv_hadamard and pn_gemv_group_hadamard run it into a per-stream
+// workspace ahead of the GEMV, and pn_gemv_hadamard_noalloc into a static device array.
 #include "pn_common.h"
 #include "pn_hadamard.h"
 
