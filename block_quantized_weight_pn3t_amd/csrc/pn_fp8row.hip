@@ -356,7 +356,9 @@ template <int M, int QX, int D>
 static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                               const float *x, float *y, hipStream_t s)
 {
-    constexpr int R = 2;
+    // rows per item: x is read from LDS once per chunk for R rows (4 at 2-4 tokens: 198 / 230 /
+    // 266 us on the head at 2 / 3 / 4 tokens against 203 / 256 / 294 us with 2)
+    constexpr int R = M == 1 ? 2 : 4;
     constexpr auto kern = fp8row_gemv_kernel<M, R, D, QX>;
     if (!lds_limit_once<kern>(kFp8MaxLds))
         return PN_ERR_HIP;
