@@ -755,6 +755,21 @@ int choose_p(int64_t nb)
     return best;
 }
 
+// The piece size a launch takes: the model's, or PN_GEMV_PIECE=8|4|2 where the registers allow
+// it (tests reach every variant with it; the results stay within the same bound). Every launcher
+// takes it from here, so a group keeps the bits of separate calls under the override too.
+template <int TYPE, int M>
+int piece_for(int64_t nb)
+{
+    int P = choose_p<TYPE, M>(nb);
+    if (const char *e = getenv("PN_GEMV_PIECE")) {
+        const int f = atoi(e);
+        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
+            P = f;
+    }
+    return P;
+}
+
 // rows [0, N) of one parity class (row_stride a multiple of 4), blocks [b0, b0 + nb) of each
 template <int TYPE, int M>
 int launch_rows(const uint8_t *row0, int64_t N, int64_t row_stride, int64_t nb, int64_t b0,
@@ -812,14 +827,7 @@ int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *
     using D = rows::Dec<TYPE>;
     const int64_t nb = K / D::G;
     const int64_t rb = nb * kBlockBytes;
-    int P = choose_p<TYPE, M>(nb);
-    // PN_GEMV_PIECE=8|4|2 forces the piece size where the registers allow it (tests reach every
-    // variant with it; the results stay within the same bound)
-    if (const char *e = getenv("PN_GEMV_PIECE")) {
-        const int f = atoi(e);
-        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
-            P = f;
-    }
+    const int P = piece_for<TYPE, M>(nb);
     const int64_t cb = 8 * P;
     // K slices of whole chunks whose x fits the LDS; each slice after the first adds to y
     const int64_t chunks_fit = rows::kXLdsMax / ((int64_t)M * cb * D::GS * (int64_t)sizeof(float));
@@ -866,12 +874,7 @@ int launch_group_typed(const GroupPart *gp, int count, int64_t K, const float *x
     const int64_t rb = nb * kBlockBytes;
     if (count < 2 || count > rows::kMaxParts || (rb & 2))
         return 1;
-    int P = choose_p<TYPE, M>(nb);
-    if (const char *e = getenv("PN_GEMV_PIECE")) {
-        const int f = atoi(e);
-        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
-            P = f;
-    }
+    const int P = piece_for<TYPE, M>(nb);
     const int64_t cb = 8 * P, NC = (nb + cb - 1) / cb;
     const size_t x_bytes = (size_t)M * NC * cb * D::GS * sizeof(float);
     if (x_bytes > (size_t)rows::kXLdsMax)
@@ -1010,7 +1013,7 @@ int launch_group_mixed(const GroupPart *gp, int count, int64_t K, const float *x
     const int64_t nb3 = K / D3::G, nb4 = K / D4::G;
     if (((nb3 * kBlockBytes) & 2) || ((nb4 * kBlockBytes) & 2))
         return 1;
-    const int P3 = choose_p<PN_TYPE_PN3T, M>(nb3), P4 = choose_p<PN_TYPE_PN4T, M>(nb4);
+    const int P3 = piece_for<PN_TYPE_PN3T, M>(nb3), P4 = piece_for<PN_TYPE_PN4T, M>(nb4);
     int64_t bytes[rows::kMaxParts], total_bytes = 0, total_rows = 0;
     for (int i = 0; i < count; i++) {
         const int64_t rb = (gp[i].type == PN_TYPE_PN3T ? nb3 : nb4) * kBlockBytes;

@@ -201,3 +201,22 @@ def test_group_hadamard_layer_q_k_v(env, M):
         tol = 1e-5 * bound + (1 + 1e-5) * gamma(B) * rbound
         err = np.abs(y.astype(np.float64) - y_ref)
         assert np.all(err <= tol), f"max |err| / tol = {float(np.max(err / tol)):.3f}"
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_group_same_bits_every_piece_size(env, monkeypatch, M):
+    """Each piece size the registers allow at M tokens, forced in turn (PN_GEMV_PIECE): the group of
+    both types (q, k and v shapes) still gives the bits of one pn_gemv call per part, and every
+    output is within the oracle's bound."""
+    pn, torch, dev = env
+    K, spec = CASES[0]
+    parts = parts_for(K, spec, 13000)
+    x = synth.activations(14700 + M, M, K)
+    for P in {1: (8, 4, 2), 2: (4, 2), 3: (2,), 4: (2,)}[M]:
+        monkeypatch.setenv("PN_GEMV_PIECE", str(P))
+        ys = run_group(pn, torch, dev, K, parts, x)
+        for (typ, W, N), y in zip(parts, ys):
+            y1 = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W), N, K, x)
+            assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), P
+            y_ref, bound = oracle.gemv(typ, W, N, K, x)
+            assert_within(y, y_ref, bound)
