@@ -369,7 +369,9 @@ static int launch_fp8row_gemv(const uint8_t *codes, const uint16_t *scales, int6
     const size_t lds = (size_t)M * phase_ch * kChunkStride * sizeof(float);
     const int grid = (int)std::min<int64_t>(fp8_num_cus(), (N + 3) / 4);
     const char *e = getenv("PN_GEMV_SPLIT");
-    const int fnum = e ? std::max(4, std::min(15, atoi(e))) : 8;  // measured best here
+    // the older wave's share of a SIMD's rows, in sixteenths (measured on the head: 8 at 1-2
+    // tokens; 9 at 3-4 tokens, 227 / 265 us against 234 / 280 us with 8)
+    const int fnum = e ? std::max(4, std::min(15, atoi(e))) : (M >= 3 ? 9 : 8);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, codes, scales, N, K, x, y,
                        row_split(N, grid), fnum, phase_ch, aligned(x, 16) ? 1 : 0);
     return launch_status();
