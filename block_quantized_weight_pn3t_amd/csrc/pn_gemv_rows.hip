@@ -52,7 +52,8 @@ namespace rows {
 // ever holds two of these workgroups while another holds none.
 constexpr int kLdsFloor = 82 * 1024;
 constexpr int kLdsMax = 160 * 1024;
-// x staged per workgroup at most (the host cuts K into slices beyond this).
+// x a workgroup can always stage (more where the partials leave room; the host cuts K into
+// slices beyond that).
 constexpr int kXLdsMax = 128 * 1024;
 
 template <int TYPE> struct Dec;
@@ -829,9 +830,18 @@ int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *
     const int64_t rb = nb * kBlockBytes;
     const int P = piece_for<TYPE, M>(nb);
     const int64_t cb = 8 * P;
-    // K slices of whole chunks whose x fits the LDS; each slice after the first adds to y
-    const int64_t chunks_fit = rows::kXLdsMax / ((int64_t)M * cb * D::GS * (int64_t)sizeof(float));
-    const int64_t slice_nb = std::max<int64_t>(1, chunks_fit) * cb;
+    // K slices of whole chunks, each slice after the first adding to y: as few as fit the LDS
+    // beside the partials of ceil(N / CUs) rows per workgroup (never fewer chunks per slice than
+    // kXLdsMax of x holds; taller matrices then split their rows over launches), and of balanced
+    // length, so that no launch is a short tail
+    const int64_t nc_all = (nb + cb - 1) / cb;
+    const int64_t cbytes = (int64_t)M * cb * D::GS * (int64_t)sizeof(float);
+    const int64_t rows_wg = (N + device_cus() - 1) / device_cus();
+    const int64_t fit_rows = ((int64_t)rows::kLdsMax - 65 * (int64_t)sizeof(float)) /
+                             (cbytes + rows_wg * M * (int64_t)sizeof(float));
+    const int64_t fit = std::max<int64_t>(1, std::max<int64_t>(fit_rows, rows::kXLdsMax / cbytes));
+    const int64_t nslices = (nc_all + fit - 1) / fit;
+    const int64_t slice_nb = (nc_all + nslices - 1) / nslices * cb;
     // rows of an odd block count alternate between two alignments: each class is its own launch
     const bool two = (rb & 2) != 0;
     for (int64_t b0 = 0; b0 < nb; b0 += slice_nb) {
