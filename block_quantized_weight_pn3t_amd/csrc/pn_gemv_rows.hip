@@ -720,16 +720,17 @@ int launch_p(int P, const rows::Args &a, int grid, size_t lds, hipStream_t s)
         if (P == 8)
             return launch_one<TYPE, M, 8>(a, grid, lds, s);
     }
-    if constexpr (M <= 2) {
+    if constexpr (M <= 3) {
         if (P == 4)
             return launch_one<TYPE, M, 4>(a, grid, lds, s);
     }
     return launch_one<TYPE, M, 2>(a, grid, lds, s);
 }
 
-// Piece size for a row of nb blocks at M tokens: the largest x that fits the registers (at most 80
-// floats per lane), then the fewest VALU operations per weight, counting the lanes of a partial
-// last chunk as spent. Each item also pays a fixed cost whatever its piece size: the reduction of
+// Piece size for a row of nb blocks at M tokens: among the sizes whose x fits the registers without
+// spills (8 words at one token, 4 up to three tokens: 120 x floats and 218 VGPRs for pn3t at
+// three; 2 always), the fewest VALU operations per weight, counting the lanes of a partial last
+// chunk as spent. Each item also pays a fixed cost whatever its piece size: the reduction of
 // its partial across the wave, the partial's LDS write and the item's scheduling. Its weight,
 // kItemOps, is fitted to launches timed at every piece size (rows of 40-272 blocks, 1024-17408
 // rows, 1-2 tokens): at 18 the model kept 2-word pieces where 4 or 8 words ran 0.3-2 us faster.
@@ -742,7 +743,7 @@ int choose_p(int64_t nb)
     int best = 2;
     double best_cost = 1e30;
     for (int P : {8, 4, 2}) {
-        if (M * D::CPW * P > 80 || (M > 1 && P == 8) || (M > 2 && P == 4))
+        if ((M > 1 && P == 8) || (M > 3 && P == 4))
             continue;
         const int64_t cb = 8 * P, nc = (nb + cb - 1) / cb;
         const double eff = (double)nb / (double)(nc * cb);
@@ -765,7 +766,7 @@ int piece_for(int64_t nb)
     int P = choose_p<TYPE, M>(nb);
     if (const char *e = getenv("PN_GEMV_PIECE")) {
         const int f = atoi(e);
-        if ((f == 8 && M == 1) || (f == 4 && M <= 2) || f == 2)
+        if ((f == 8 && M == 1) || (f == 4 && M <= 3) || f == 2)
             P = f;
     }
     return P;
@@ -980,7 +981,7 @@ int launch_mixed_one(const rows::Args &a, int grid, size_t lds, hipStream_t s)
     return launch_status();
 }
 
-// piece sizes a launch can take: 8, 4 and 2 at one token, 4 and 2 at two, 2 at three and four
+// piece sizes a launch can take: 8, 4 and 2 at one token, 4 and 2 at two and three, 2 at four
 template <int M, int P3>
 int launch_mixed_p4(const rows::Args &a, int grid, size_t lds, int P4, hipStream_t s)
 {
@@ -988,7 +989,7 @@ int launch_mixed_p4(const rows::Args &a, int grid, size_t lds, int P4, hipStream
         if (P4 == 8)
             return launch_mixed_one<M, P3, 8>(a, grid, lds, s);
     }
-    if constexpr (M <= 2) {
+    if constexpr (M <= 3) {
         if (P4 == 4)
             return launch_mixed_one<M, P3, 4>(a, grid, lds, s);
     }
@@ -1002,7 +1003,7 @@ int launch_mixed_p3(const rows::Args &a, int grid, size_t lds, int P3, int P4, h
         if (P3 == 8)
             return launch_mixed_p4<M, 8>(a, grid, lds, P4, s);
     }
-    if constexpr (M <= 2) {
+    if constexpr (M <= 3) {
         if (P3 == 4)
             return launch_mixed_p4<M, 4>(a, grid, lds, P4, s);
     }

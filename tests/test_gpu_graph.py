@@ -24,7 +24,7 @@ def env():
 
 def setup(pn, torch, dev):
     """Four calls of a decode step: pn3t at one token (8-word pieces), pn4t at three tokens
-    (2-word pieces), pn3t with x rotated in slices of 256 at one token (under capture rotated
+    (4-word pieces), pn3t with x rotated in slices of 256 at one token (under capture rotated
     into a temporary), and a pn3t and a pn4t matrix that share x in one pn_gemv_group launch."""
     calls = []
     for typ, N, nb, M, seed, B in [(PN3T, 300, 64, 1, 12000, None), (PN4T, 77, 96, 3, 12001, None),

@@ -212,7 +212,7 @@ def test_group_same_bits_every_piece_size(env, monkeypatch, M):
     K, spec = CASES[0]
     parts = parts_for(K, spec, 13000)
     x = synth.activations(14700 + M, M, K)
-    for P in {1: (8, 4, 2), 2: (4, 2), 3: (2,), 4: (2,)}[M]:
+    for P in {1: (8, 4, 2), 2: (4, 2), 3: (4, 2), 4: (2,)}[M]:
         monkeypatch.setenv("PN_GEMV_PIECE", str(P))
         ys = run_group(pn, torch, dev, K, parts, x)
         for (typ, W, N), y in zip(parts, ys):

@@ -187,7 +187,7 @@ def test_gemv_long_rows(env, typ, N, nb, M):
 
 
 # piece sizes (words per lane) each token count may run: the x of a piece must fit the registers
-PIECES = {1: (8, 4, 2), 2: (4, 2), 3: (2,), 4: (2,)}
+PIECES = {1: (8, 4, 2), 2: (4, 2), 3: (4, 2), 4: (2,)}
 
 
 @pytest.mark.parametrize("typ,N,nb", [(PN3T, 37, 64), (PN4T, 19, 40), (PN4T, 45, 128), (PN3T, 9, 72),

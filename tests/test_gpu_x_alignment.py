@@ -42,8 +42,8 @@ CASES = [
     (PN4T, 70, 272, 1, None),                  # vector units, long rows, one token
     (PN3T, 50, 70, 2, None),                   # vector units, two tokens
     (PN4T, 19, 130, 1, ("PN_GEMV_PIECE", "2")),  # vector units, 2-word pieces, forced
-    (PN3T, 37, 64, 3, None),                   # vector units, 2-word pieces, three tokens
-    (PN4T, 45, 128, 4, None),                  # vector units, four tokens
+    (PN3T, 37, 64, 3, None),                   # vector units, 4-word pieces, three tokens
+    (PN4T, 45, 128, 4, None),                  # vector units, 2-word pieces, four tokens
     (PN4T, 77, 96, 5, None),                   # matrix cores, W through LDS
     (PN3T, 33, 10, 5, None),                   # matrix cores, direct weight loads
     (PN4T, 20, 32, 9, None),                   # matrix cores, K-split layout
