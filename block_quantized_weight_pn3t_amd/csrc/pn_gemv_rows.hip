@@ -757,13 +757,22 @@ int choose_p(int64_t nb)
     return best;
 }
 
-// The piece size a launch takes: the model's, or PN_GEMV_PIECE=8|4|2 where the registers allow
-// it (tests reach every variant with it; the results stay within the same bound). Every launcher
-// takes it from here, so a group keeps the bits of separate calls under the override too.
+// The piece size a launch takes for a matrix of N rows of nb blocks: the model's, or
+// PN_GEMV_PIECE=8|4|2 where the registers allow it (tests reach every variant with it; the results
+// stay within the same bound). At three tokens 4-word pieces are kept only where the ceil(N / CUs)
+// rows of a workgroup give its 8 waves at least 8 groups of 4 items: on fewer rows (k and v,
+// 1024x5120: 3 groups) the waves sit idle and 2-word pieces run 5.8 against 7.9 us. It depends on
+// the matrix alone, never on how a group deals its workgroups, so a group keeps the bits of
+// separate calls; every launcher takes the piece size from here.
 template <int TYPE, int M>
-int piece_for(int64_t nb)
+int piece_for(int64_t nb, int64_t N)
 {
     int P = choose_p<TYPE, M>(nb);
+    if (M == 3 && P == 4) {
+        const int64_t rows_wg = (N + device_cus() - 1) / device_cus();
+        if ((rows_wg + 3) / 4 * ((nb + 31) / 32) < 8)
+            P = 2;
+    }
     if (const char *e = getenv("PN_GEMV_PIECE")) {
         const int f = atoi(e);
         if ((f == 8 && M == 1) || (f == 4 && M <= 3) || f == 2)
@@ -829,7 +838,7 @@ int launch_typed(const uint8_t *W, int64_t N, int64_t K, const float *x, float *
     using D = rows::Dec<TYPE>;
     const int64_t nb = K / D::G;
     const int64_t rb = nb * kBlockBytes;
-    const int P = piece_for<TYPE, M>(nb);
+    const int P = piece_for<TYPE, M>(nb, N);
     const int64_t cb = 8 * P;
     // K slices of whole chunks, each slice after the first adding to y: as few as fit the LDS
     // beside the partials of ceil(N / CUs) rows per workgroup (never fewer chunks per slice than
@@ -885,7 +894,11 @@ int launch_group_typed(const GroupPart *gp, int count, int64_t K, const float *x
     const int64_t rb = nb * kBlockBytes;
     if (count < 2 || count > rows::kMaxParts || (rb & 2))
         return 1;
-    const int P = piece_for<TYPE, M>(nb);
+    // one piece size for all parts: the one each would take alone, else separate launches
+    const int P = piece_for<TYPE, M>(nb, gp[0].N);
+    for (int i = 1; i < count; i++)
+        if (piece_for<TYPE, M>(nb, gp[i].N) != P)
+            return 1;
     const int64_t cb = 8 * P, NC = (nb + cb - 1) / cb;
     const size_t x_bytes = (size_t)M * NC * cb * D::GS * sizeof(float);
     if (x_bytes > (size_t)rows::kXLdsMax)
@@ -1012,8 +1025,9 @@ int launch_mixed_p3(const rows::Args &a, int grid, size_t lds, int P3, int P4, h
 
 // Matrices of both types (and one K) as one launch: each type with the piece size a launch of its
 // own would take, 8 waves per CU, each part with its own row shape, x layout and share of the
-// workgroups (in proportion to its bytes). Returns 1 where the shapes do not allow it (as
-// launch_group_typed).
+// workgroups. The shares follow the cost model of choose_p (rows x chunks x operations per item),
+// not the bytes: a pn4t row of 80 blocks is two items, the second a quarter full, against one
+// for a pn3t row of 64. Returns 1 where the shapes do not allow it (as launch_group_typed).
 template <int M>
 int launch_group_mixed(const GroupPart *gp, int count, int64_t K, const float *x, hipStream_t s)
 {
@@ -1024,14 +1038,33 @@ int launch_group_mixed(const GroupPart *gp, int count, int64_t K, const float *x
     const int64_t nb3 = K / D3::G, nb4 = K / D4::G;
     if (((nb3 * kBlockBytes) & 2) || ((nb4 * kBlockBytes) & 2))
         return 1;
-    const int P3 = piece_for<PN_TYPE_PN3T, M>(nb3), P4 = piece_for<PN_TYPE_PN4T, M>(nb4);
-    int64_t bytes[rows::kMaxParts], total_bytes = 0, total_rows = 0;
+    // one piece size per type: the one each part would take alone, else no mixed launch
+    int P3 = 0, P4 = 0;
     for (int i = 0; i < count; i++) {
-        const int64_t rb = (gp[i].type == PN_TYPE_PN3T ? nb3 : nb4) * kBlockBytes;
+        const bool p3 = gp[i].type == PN_TYPE_PN3T;
+        const int Pi = p3 ? piece_for<PN_TYPE_PN3T, M>(nb3, gp[i].N)
+                          : piece_for<PN_TYPE_PN4T, M>(nb4, gp[i].N);
+        int &Pt = p3 ? P3 : P4;
+        if (Pt && Pt != Pi)
+            return 1;
+        Pt = Pi;
+    }
+    if (!P3)
+        P3 = 2;
+    if (!P4)
+        P4 = 2;
+    // per-item operations of each type (the cost model of choose_p)
+    const int64_t ops3 = (int64_t)(P3 * (1 + D3::PAIRS * (2 + 2 * M)) + kItemOps);
+    const int64_t ops4 = (int64_t)(P4 * (1 + D4::PAIRS * (2 + 2 * M)) + kItemOps);
+    const int64_t nc3 = (nb3 + 8 * P3 - 1) / (8 * P3), nc4 = (nb4 + 8 * P4 - 1) / (8 * P4);
+    int64_t cost[rows::kMaxParts], total_cost = 0, total_rows = 0;
+    for (int i = 0; i < count; i++) {
+        const bool p3 = gp[i].type == PN_TYPE_PN3T;
+        const int64_t rb = (p3 ? nb3 : nb4) * kBlockBytes;
         if (gp[i].N <= 0 || gp[i].N * rb > (int64_t)0x7FFF0000)
             return 1;
-        bytes[i] = gp[i].N * rb;
-        total_bytes += bytes[i];
+        cost[i] = gp[i].N * (p3 ? nc3 * ops3 : nc4 * ops4);
+        total_cost += cost[i];
         total_rows += gp[i].N;
     }
     const int grid = (int)std::min<int64_t>(device_cus(), total_rows);
@@ -1040,7 +1073,7 @@ int launch_group_mixed(const GroupPart *gp, int count, int64_t K, const float *x
     int gcount[rows::kMaxParts];
     int used = 0;
     for (int i = 0; i < count; i++) {
-        gcount[i] = (int)std::max<int64_t>(1, std::min<int64_t>(gp[i].N, bytes[i] * grid / total_bytes));
+        gcount[i] = (int)std::max<int64_t>(1, std::min<int64_t>(gp[i].N, cost[i] * grid / total_cost));
         used += gcount[i];
     }
     for (int i = 0; used < grid; i = (i + 1) % count)
