@@ -198,3 +198,18 @@ def test_gemv_vector_kernels_few_tokens(env, typ, N, nb, M):
     for offset in (0, 2):
         y = run_gemv(pn, torch, dev, typ, dev_bytes(torch, dev, W, offset), N, K, x)
         assert_within(y, y_ref, bound)
+
+@pytest.mark.slow
+def test_gemv_down_full_size_tokens(env):
+    """Down (pn4t 5120x17408) at 1-4 tokens, every row against the oracle. Its K slices: one launch
+    at one and two tokens (at two, 156.7 KB of x beside the partials in the 160 KB LDS), two of
+    9 + 8 chunks at three and four."""
+    pn, torch, dev = env
+    N, K = 5120, 17408
+    _, W = quantized(PN4T, N, K, 303)
+    Wd = dev_bytes(torch, dev, W)
+    x4 = synth.activations(9990, 4, K)
+    y_ref, bound = oracle.gemv(PN4T, W, N, K, x4)
+    for M in (1, 2, 3, 4):
+        y = run_gemv(pn, torch, dev, PN4T, Wd, N, K, x4[:M])
+        assert_within(y, y_ref[:M], bound[:M])
